@@ -1,0 +1,181 @@
+/*
+ * kvq.h -- C ABI of libkvq: a KV cache whose keys and values are stored at
+ * independently chosen precisions (f16, q8_0, q4_0), with a quantizing
+ * append and flash attention (decode and causal chunked prefill) that reads
+ * the quantized blocks directly.  Built for AMD Instinct MI355X (gfx950).
+ *
+ * Sources, cited by page title and section:
+ *  - llama.cpp optimization guide "llama.cpp fuer Geschwindigkeit und
+ *    Speicher optimieren" (docs.tokios.com), section "KV-Cache-Praezision":
+ *    the cache types f16 / q8_0 / q4_0 and the fact that keys and values are
+ *    set independently; section "Flash Attention": tiled attention that never
+ *    materializes the score matrix and is exactly standard attention;
+ *    section "Batch-Groessen-Abstimmung": prompts are processed in
+ *    micro-batches (chunked prefill).
+ *  - "KVSplit - 2- bis 3-mal laengerer Kontext auf Apple Silicon"
+ *    (news.hada.io): sections "Zentrale Benchmark-Ergebnisse" and
+ *    "Vergleich der Speicherersparnis" (K8V4 = 8-bit keys, 4-bit values;
+ *    cache sizes at 8K tokens), "Roadmap" (separate quantization per layer).
+ *  - llama.cpp issue "Eval bug: Metal fails mixed quantized KV on Apple
+ *    Silicon when Flash Attention is unavailable ...": the llama_kv_cache
+ *    size log lines (K q8_0 / V q4_0 byte totals) and, under "Expected
+ *    behavior", the request for a clear early rejection without partial
+ *    initialization -- which is this library's error convention.
+ *
+ * Conventions for every entry point:
+ *  - All tensors live in device memory owned by the caller; the library
+ *    allocates nothing, keeps no global state and is re-entrant.
+ *  - Per-sequence integer arrays (pos, ctx_len, q_pos0) are HOST arrays of
+ *    n_seqs entries; they are validated on the host and passed to the
+ *    kernels by value.
+ *  - Every argument is validated on the host before anything is enqueued;
+ *    on error a negative KVQ_E_* code is returned and no device work was
+ *    issued.  KVQ_E_HIP reports a failed launch; faults inside a kernel
+ *    surface at the caller's next synchronization.
+ *  - `stream` is a hipStream_t (NULL = the default stream); all work is
+ *    asynchronous on it and no host synchronization happens inside.
+ *  - Device pointers must be 16-byte aligned.
+ *  - Inputs must be finite: NaN/Inf inside K, V or Q is outside the
+ *    contract and is not checked on the hot path.
+ *
+ * Storage layout of one layer's planes (the contract the CPU oracle
+ * re-implements independently).  S = n_seqs, H = n_kv_heads,
+ * D = head_dim, nb = D/32, Tc = max_ctx rounded up to a multiple of 32,
+ * pair = s*H + h:
+ *  - A 32-element block stores: f16: 32 binary16 values (64 B);
+ *    q8_0: 32 int8 codes (32 B) + binary16 scale d, x^ = d*q;
+ *    q4_0: 16 bytes, byte i = c_i | c_(i+16) << 4 (4-bit codes) + binary16
+ *    scale d, x^ = d*(c-8).  Row code bytes R = 2D, D or D/2; block b of a
+ *    row occupies code bytes [b*R/nb, (b+1)*R/nb).
+ *  - K plane ("token-major"): code byte r of token t at
+ *        codes + (pair*Tc + t)*R + r;
+ *    scale of block b at  scales + 2*((pair*Tc + t)*nb + b).
+ *  - V plane ("8-token interleaved", so that one 8-byte or 16-byte load
+ *    returns 8 consecutive tokens of one channel, the operand shape of the
+ *    matrix-core P.V product): with unit size w = 2 bytes for f16 (one
+ *    value) and 1 byte otherwise, U = R/w units per row, unit u of token t
+ *    at  codes + w*((((pair*(Tc/8)) + t/8)*U + u)*8 + t%8);
+ *    scale of block b at  scales + 2*(((pair*(Tc/8) + t/8)*nb + b)*8 + t%8).
+ *  - Plane bytes: codes S*H*Tc*R, scales S*H*Tc*nb*2 (0 for f16).  With
+ *    max_ctx a multiple of 32 nothing is padded: q8_0 costs 34 B and q4_0
+ *    18 B per 32 elements, the sizes behind the KVSplit page's 176 / 93.5 /
+ *    71.5 / 49.5 MiB and the issue's 816 + 432 MiB.
+ *
+ * Quantization (the ggml q8_0 / q4_0 block formats of the cache types named
+ * on the llama.cpp pages), bit-exact, in binary32 unless stated:
+ *  q8_0: amax = max|x|; d = f16(amax/127); id = d ? 1/d : 0;
+ *        q = clamp(round_half_away(x*id), -127, 127).
+ *  q4_0: m = the x of largest |x| (lowest index on ties, +0 if all zero);
+ *        d = f16(m/-8); id = d ? 1/d : 0;
+ *        c = clamp(trunc((x*id) + 8.5), 0, 15), product and sum rounded
+ *        separately (no fused multiply-add).
+ *  f16 (the conversion) rounds to nearest even.
+ */
+#ifndef KVQ_H
+#define KVQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Cache element types (llama.cpp's --cache-type-k / --cache-type-v values). */
+typedef enum kvq_type { KVQ_F16 = 0, KVQ_Q8_0 = 1, KVQ_Q4_0 = 2 } kvq_type;
+
+enum {
+    KVQ_OK = 0,
+    KVQ_E_ARG = -1,       /* NULL or misaligned pointer, malformed argument   */
+    KVQ_E_TYPE = -2,      /* unknown type, or type differs from the plane's   */
+    KVQ_E_SHAPE = -3,     /* unsupported head_dim / head grouping / counts    */
+    KVQ_E_RANGE = -4,     /* layer, position or context length out of range   */
+    KVQ_E_WORKSPACE = -5, /* workspace NULL or smaller than required          */
+    KVQ_E_HIP = -6        /* a HIP call or kernel launch failed               */
+};
+
+/* Supported limits. */
+#define KVQ_MAX_SEQS 256   /* n_seqs: per-sequence arrays travel as kernel args */
+#define KVQ_MAX_GROUP 16   /* n_q_heads / n_kv_heads                            */
+#define KVQ_MAX_SPLITS 256 /* decode context splits per (sequence, kv head)     */
+/* head_dim must be 64, 128 or 256. */
+
+typedef struct kvq_shape {
+    int32_t n_layers;   /* >= 1                                  */
+    int32_t n_seqs;     /* 1 .. KVQ_MAX_SEQS                     */
+    int32_t n_q_heads;  /* multiple of n_kv_heads                */
+    int32_t n_kv_heads; /* >= 1, n_q_heads/n_kv_heads <= 16      */
+    int32_t head_dim;   /* 64, 128 or 256                        */
+    int32_t max_ctx;    /* cache capacity in tokens, >= 1        */
+} kvq_shape;
+
+/* One plane (the K or the V half of one layer). */
+typedef struct kvq_plane {
+    int32_t type;  /* kvq_type                                               */
+    void *codes;   /* device, kvq_plane_bytes() codes bytes                  */
+    void *scales;  /* device binary16 scales; NULL (and unused) for KVQ_F16  */
+} kvq_plane;
+
+/* The whole cache: k[l] and v[l] describe layer l (host arrays of
+ * shape.n_layers planes; the types may differ per layer and per K/V). */
+typedef struct kvq_cache {
+    kvq_shape shape;
+    const kvq_plane *k;
+    const kvq_plane *v;
+} kvq_cache;
+
+/* Message for a KVQ_* code (static string, never NULL). */
+const char *kvq_strerror(int code);
+
+/* Bytes of one plane of `type` for `shape` (codes and scales separately).
+ * Host only.  Errors: KVQ_E_ARG (NULL), KVQ_E_SHAPE, KVQ_E_TYPE. */
+int kvq_plane_bytes(const kvq_shape *shape, int32_t type, size_t *codes_bytes, size_t *scale_bytes);
+
+/* Validate a cache descriptor on the host (shape limits, types, non-NULL and
+ * aligned plane pointers).  No device access. */
+int kvq_cache_check(const kvq_cache *cache);
+
+/* Quantize n_new new rows per sequence into layer `layer` at positions
+ * pos[s] .. pos[s]+n_new-1 (the quantizing row copy into the cache that the
+ * llama.cpp issue names "CPY").
+ *   K, V : device binary16 [n_seqs][n_new][n_kv_heads][head_dim]
+ *   pos  : host int32 [n_seqs], 0 <= pos[s], pos[s] + n_new <= max_ctx
+ *   k_type, v_type must equal the layer's plane types (else KVQ_E_TYPE).
+ * Rows outside the written range are untouched.  One kernel launch. */
+int kvq_append(const kvq_cache *cache, int32_t layer, const void *K, const void *V, int32_t n_new,
+               const int32_t *pos, int32_t k_type, int32_t v_type, void *stream);
+
+/* Workspace bytes that kvq_attn_decode needs for any ctx_len <= max_ctx and
+ * any split count it may choose (n_seqs*n_q_heads*splits*(head_dim+2)*4). */
+int kvq_decode_workspace_bytes(const kvq_shape *shape, size_t *bytes);
+
+/* Flash-decode one query token per sequence over layer `layer`.
+ *   Q       : device binary16 [n_seqs][n_q_heads][head_dim]
+ *   ctx_len : host int32 [n_seqs], 1 <= ctx_len[s] <= max_ctx; query s
+ *             attends to cache positions 0 .. ctx_len[s]-1 (append the new
+ *             token's K/V first: ctx_len counts it)
+ *   scale   : multiplies Q.K (typically 1/sqrt(head_dim)), used as passed
+ *   out     : device float32 [n_seqs][n_q_heads][head_dim]
+ *   workspace, workspace_bytes: device scratch for split partials
+ *   n_splits: context splits per (sequence, kv head); 0 chooses one
+ * Query head hq reads kv head hq / (n_q_heads/n_kv_heads).  Two launches:
+ * a split-K pass writing (max, sum, unnormalized output) partials, then a
+ * log-sum-exp merge. */
+int kvq_attn_decode(const kvq_cache *cache, int32_t layer, const void *Q, const int32_t *ctx_len, float scale,
+                    float *out, void *workspace, size_t workspace_bytes, int32_t n_splits, void *stream);
+
+/* Causal attention for a chunk of n_tok queries per sequence whose K/V rows
+ * are already appended at positions q_pos0[s] .. q_pos0[s]+n_tok-1 (the
+ * micro-batch of the llama.cpp guide's "Batch-Groessen-Abstimmung").
+ *   Q      : device binary16 [n_seqs][n_tok][n_q_heads][head_dim]
+ *   q_pos0 : host int32 [n_seqs], 0 <= q_pos0[s], q_pos0[s]+n_tok <= max_ctx
+ *   out    : device float32 [n_seqs][n_tok][n_q_heads][head_dim]
+ * Query i of sequence s attends to positions 0 .. q_pos0[s]+i. */
+int kvq_attn_prefill_chunk(const kvq_cache *cache, int32_t layer, const void *Q, int32_t n_tok,
+                           const int32_t *q_pos0, float scale, float *out, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KVQ_H */

@@ -1,0 +1,214 @@
+"""Python binding of libkvq (argument marshalling only).
+
+Every entry point of ``include/kvq.h`` is exposed under the same name and
+forwards plain pointers and sizes through ctypes; every step of the hot path
+runs in the HIP kernels of ``libkvq.so``.  PyTorch is used for device memory
+and streams only (``KVCache`` allocates the planes with torch).
+
+The library must be built (``python -m mixed_precision_quantized_quantize_amd.build``);
+there is no fallback of any kind: a missing library raises ``KvqLibraryMissing``.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libkvq.so")
+
+F16, Q8_0, Q4_0 = 0, 1, 2
+TYPES = {"f16": F16, "q8_0": Q8_0, "q4_0": Q4_0}
+TYPE_NAMES = {v: k for k, v in TYPES.items()}
+
+KVQ_OK, KVQ_E_ARG, KVQ_E_TYPE, KVQ_E_SHAPE, KVQ_E_RANGE, KVQ_E_WORKSPACE, KVQ_E_HIP = 0, -1, -2, -3, -4, -5, -6
+KVQ_MAX_SEQS, KVQ_MAX_GROUP, KVQ_MAX_SPLITS = 256, 16, 256
+
+EXPORTS = ["kvq_strerror", "kvq_plane_bytes", "kvq_cache_check", "kvq_append", "kvq_decode_workspace_bytes",
+           "kvq_attn_decode", "kvq_attn_prefill_chunk"]
+
+
+class KvqLibraryMissing(RuntimeError):
+    pass
+
+
+class KvqError(RuntimeError):
+    def __init__(self, code: int, where: str):
+        self.code = code
+        super().__init__(f"{where}: {kvq_strerror(code)} (code {code})")
+
+
+class kvq_shape(ctypes.Structure):
+    _fields_ = [("n_layers", ctypes.c_int32), ("n_seqs", ctypes.c_int32), ("n_q_heads", ctypes.c_int32),
+                ("n_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32), ("max_ctx", ctypes.c_int32)]
+
+
+class kvq_plane(ctypes.Structure):
+    _fields_ = [("type", ctypes.c_int32), ("codes", ctypes.c_void_p), ("scales", ctypes.c_void_p)]
+
+
+class kvq_cache(ctypes.Structure):
+    _fields_ = [("shape", kvq_shape), ("k", ctypes.POINTER(kvq_plane)), ("v", ctypes.POINTER(kvq_plane))]
+
+
+_lock = threading.Lock()
+_lib = None
+
+
+def lib():
+    """The loaded libkvq.so (raises KvqLibraryMissing if it was not built)."""
+    global _lib
+    with _lock:
+        if _lib is None:
+            if not os.path.exists(LIB_PATH):
+                raise KvqLibraryMissing(f"{LIB_PATH} is not built; run "
+                                        "`python -m mixed_precision_quantized_quantize_amd.build`")
+            L = ctypes.CDLL(LIB_PATH)
+            vp, i32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
+            P = ctypes.POINTER
+            L.kvq_strerror.argtypes = [ctypes.c_int]
+            L.kvq_strerror.restype = ctypes.c_char_p
+            L.kvq_plane_bytes.argtypes = [P(kvq_shape), i32, P(sz), P(sz)]
+            L.kvq_cache_check.argtypes = [P(kvq_cache)]
+            L.kvq_append.argtypes = [P(kvq_cache), i32, vp, vp, i32, P(ctypes.c_int32), i32, i32, vp]
+            L.kvq_decode_workspace_bytes.argtypes = [P(kvq_shape), P(sz)]
+            L.kvq_attn_decode.argtypes = [P(kvq_cache), i32, vp, P(ctypes.c_int32), ctypes.c_float, vp, vp, sz,
+                                          i32, vp]
+            L.kvq_attn_prefill_chunk.argtypes = [P(kvq_cache), i32, vp, i32, P(ctypes.c_int32), ctypes.c_float,
+                                                 vp, vp]
+            for name in EXPORTS:
+                if name != "kvq_strerror":
+                    getattr(L, name).restype = ctypes.c_int
+            _lib = L
+    return _lib
+
+
+def _i32_array(vals):
+    vals = [int(v) for v in vals]
+    return (ctypes.c_int32 * len(vals))(*vals)
+
+
+def _check(rc: int, where: str):
+    if rc != KVQ_OK:
+        raise KvqError(rc, where)
+
+
+def _type(t) -> int:
+    return TYPES[t] if isinstance(t, str) else int(t)
+
+
+# ------------------------------------------------------------------ C ABI, same names
+
+def kvq_strerror(code: int) -> str:
+    return lib().kvq_strerror(int(code)).decode()
+
+
+def kvq_plane_bytes(shape: kvq_shape, type_) -> tuple[int, int]:
+    a, b = ctypes.c_size_t(), ctypes.c_size_t()
+    _check(lib().kvq_plane_bytes(ctypes.byref(shape), _type(type_), ctypes.byref(a), ctypes.byref(b)),
+           "kvq_plane_bytes")
+    return a.value, b.value
+
+
+def kvq_cache_check(cache: kvq_cache) -> int:
+    return lib().kvq_cache_check(ctypes.byref(cache))
+
+
+def kvq_decode_workspace_bytes(shape: kvq_shape) -> int:
+    b = ctypes.c_size_t()
+    _check(lib().kvq_decode_workspace_bytes(ctypes.byref(shape), ctypes.byref(b)), "kvq_decode_workspace_bytes")
+    return b.value
+
+
+def kvq_append(cache: kvq_cache, layer: int, K_ptr: int, V_ptr: int, n_new: int, pos, k_type, v_type,
+               stream: int) -> int:
+    return lib().kvq_append(ctypes.byref(cache), int(layer), K_ptr, V_ptr, int(n_new), _i32_array(pos),
+                            _type(k_type), _type(v_type), stream)
+
+
+def kvq_attn_decode(cache: kvq_cache, layer: int, Q_ptr: int, ctx_len, scale: float, out_ptr: int, ws_ptr: int,
+                    ws_bytes: int, n_splits: int, stream: int) -> int:
+    return lib().kvq_attn_decode(ctypes.byref(cache), int(layer), Q_ptr, _i32_array(ctx_len), float(scale), out_ptr,
+                                 ws_ptr, int(ws_bytes), int(n_splits), stream)
+
+
+def kvq_attn_prefill_chunk(cache: kvq_cache, layer: int, Q_ptr: int, n_tok: int, q_pos0, scale: float,
+                           out_ptr: int, stream: int) -> int:
+    return lib().kvq_attn_prefill_chunk(ctypes.byref(cache), int(layer), Q_ptr, int(n_tok), _i32_array(q_pos0),
+                                        float(scale), out_ptr, stream)
+
+
+# ------------------------------------------------------------------ torch plumbing
+
+class KVCache:
+    """Cache planes in device memory (allocated with torch) plus the kvq_cache
+    descriptor that points at them.  ``types`` is one (k_type, v_type) pair
+    for all layers, or a list with one pair per layer."""
+
+    def __init__(self, n_layers, n_seqs, n_q_heads, n_kv_heads, head_dim, max_ctx, types, device="cuda"):
+        import torch
+
+        self.torch = torch
+        self.device = torch.device(device)
+        self.shape = kvq_shape(n_layers, n_seqs, n_q_heads, n_kv_heads, head_dim, max_ctx)
+        if isinstance(types[0], (str, int)):
+            types = [tuple(types)] * n_layers
+        assert len(types) == n_layers
+        self.types = [(_type(k), _type(v)) for k, v in types]
+        self.k_planes = (kvq_plane * n_layers)()
+        self.v_planes = (kvq_plane * n_layers)()
+        self.buffers = []  # (k_codes, k_scales, v_codes, v_scales) per layer
+        for l, (kt, vt) in enumerate(self.types):
+            bufs = []
+            for t, planes in ((kt, self.k_planes), (vt, self.v_planes)):
+                cb, sb = kvq_plane_bytes(self.shape, t)
+                codes = torch.empty(cb, dtype=torch.uint8, device=self.device)
+                scales = torch.empty(max(sb // 2, 1), dtype=torch.int16, device=self.device) if sb else None
+                planes[l] = kvq_plane(t, codes.data_ptr(), scales.data_ptr() if scales is not None else None)
+                bufs += [codes, scales]
+            self.buffers.append(tuple(bufs))
+        self.desc = kvq_cache(self.shape, self.k_planes, self.v_planes)
+        _check(kvq_cache_check(self.desc), "kvq_cache_check")
+        self._ws = None
+
+    def _stream(self):
+        return self.torch.cuda.current_stream(self.device).cuda_stream
+
+    def append(self, layer, K, V, pos):
+        """K, V: binary16 device tensors [S][n_new][Hkv][D]; pos: host ints [S]."""
+        assert K.dtype == self.torch.float16 and V.dtype == self.torch.float16
+        assert K.is_contiguous() and V.is_contiguous() and K.shape == V.shape and K.dim() == 4
+        kt, vt = self.types[layer]
+        _check(kvq_append(self.desc, layer, K.data_ptr(), V.data_ptr(), K.shape[1], pos, kt, vt, self._stream()),
+               "kvq_append")
+
+    def workspace(self):
+        if self._ws is None:
+            nb = kvq_decode_workspace_bytes(self.shape)
+            self._ws = self.torch.empty(nb // 4, dtype=self.torch.float32, device=self.device)
+        return self._ws
+
+    def decode(self, layer, Q, ctx_len, scale, out=None, n_splits=0):
+        """Q: binary16 [S][Hq][D] -> float32 [S][Hq][D]."""
+        sh = self.shape
+        assert Q.dtype == self.torch.float16 and Q.is_contiguous()
+        assert tuple(Q.shape) == (sh.n_seqs, sh.n_q_heads, sh.head_dim)
+        if out is None:
+            out = self.torch.empty(tuple(Q.shape), dtype=self.torch.float32, device=self.device)
+        ws = self.workspace()
+        _check(kvq_attn_decode(self.desc, layer, Q.data_ptr(), ctx_len, scale, out.data_ptr(), ws.data_ptr(),
+                               ws.numel() * 4, n_splits, self._stream()), "kvq_attn_decode")
+        return out
+
+    def prefill(self, layer, Q, q_pos0, scale, out=None):
+        """Q: binary16 [S][n_tok][Hq][D] -> float32 [S][n_tok][Hq][D]."""
+        assert Q.dtype == self.torch.float16 and Q.is_contiguous() and Q.dim() == 4
+        if out is None:
+            out = self.torch.empty(tuple(Q.shape), dtype=self.torch.float32, device=self.device)
+        _check(kvq_attn_prefill_chunk(self.desc, layer, Q.data_ptr(), Q.shape[1], q_pos0, scale, out.data_ptr(),
+                                      self._stream()), "kvq_attn_prefill_chunk")
+        return out
+
+    def plane_tensors(self, layer):
+        """(k_codes, k_scales, v_codes, v_scales) device tensors of a layer."""
+        return self.buffers[layer]

@@ -1,0 +1,287 @@
+// kvq_api.cpp -- the C ABI of libkvq: host-side validation and dispatch.
+//
+// Every argument is checked here before anything is enqueued, so a failing
+// call returns a KVQ_E_* code with no device side effects -- the "clear early
+// rejection without partial initialization" that the llama.cpp issue asks
+// for under "Expected behavior".  The kernels themselves assume the checked
+// preconditions.
+#include <math.h>
+#include <string.h>
+
+#include <algorithm>
+
+#include "kvq_internal.h"
+
+using namespace kvq;
+
+namespace {
+
+bool valid_type(int32_t t) { return t == KVQ_F16 || t == KVQ_Q8_0 || t == KVQ_Q4_0; }
+
+bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+int check_shape(const kvq_shape *sh)
+{
+    if (!sh)
+        return KVQ_E_ARG;
+    if (sh->n_layers < 1 || sh->n_seqs < 1 || sh->n_seqs > KVQ_MAX_SEQS || sh->n_kv_heads < 1 ||
+        sh->n_q_heads < 1 || sh->max_ctx < 1)
+        return KVQ_E_SHAPE;
+    if (sh->head_dim != 64 && sh->head_dim != 128 && sh->head_dim != 256)
+        return KVQ_E_SHAPE;
+    if (sh->n_q_heads % sh->n_kv_heads != 0 || sh->n_q_heads / sh->n_kv_heads > KVQ_MAX_GROUP)
+        return KVQ_E_SHAPE;
+    // byte offsets inside one plane must fit comfortably in 63 bits, and the
+    // grid dimensions in their hardware limits
+    if ((int64_t)sh->n_seqs * sh->n_kv_heads * capacity(sh->max_ctx) > ((int64_t)1 << 40))
+        return KVQ_E_SHAPE;
+    return KVQ_OK;
+}
+
+int check_plane(const kvq_plane *p)
+{
+    if (!valid_type(p->type))
+        return KVQ_E_TYPE;
+    if (!p->codes || !aligned16(p->codes))
+        return KVQ_E_ARG;
+    if (p->type != KVQ_F16 && (!p->scales || !aligned16(p->scales)))
+        return KVQ_E_ARG;
+    return KVQ_OK;
+}
+
+int check_cache(const kvq_cache *c)
+{
+    if (!c)
+        return KVQ_E_ARG;
+    int rc = check_shape(&c->shape);
+    if (rc)
+        return rc;
+    if (!c->k || !c->v)
+        return KVQ_E_ARG;
+    for (int l = 0; l < c->shape.n_layers; l++) {
+        if ((rc = check_plane(&c->k[l])) || (rc = check_plane(&c->v[l])))
+            return rc;
+    }
+    return KVQ_OK;
+}
+
+int check_layer(const kvq_cache *c, int32_t layer)
+{
+    int rc = check_cache(c);
+    if (rc)
+        return rc;
+    if (layer < 0 || layer >= c->shape.n_layers)
+        return KVQ_E_RANGE;
+    return KVQ_OK;
+}
+
+// Split plan of a decode call: tokens per split (a multiple of the 32-token
+// tile) and the split count covering the longest context.
+void decode_plan(const kvq_shape &sh, int max_len, int32_t req, int *n_splits, int *tps)
+{
+    const int64_t units = (int64_t)sh.n_seqs * sh.n_kv_heads;
+    int want = req;
+    if (want <= 0) {
+        // enough workgroups to fill 256 CUs several times over, at least
+        // 128 tokens (one tile per wave) per split
+        const int64_t target = 2048;
+        want = (int)std::min<int64_t>(KVQ_MAX_SPLITS, (target + units - 1) / units);
+        want = std::min(want, std::max(1, (max_len + 127) / 128));
+    }
+    want = std::max(1, std::min(want, KVQ_MAX_SPLITS));
+    int t = (max_len + want - 1) / want;
+    t = (t + 31) / 32 * 32;
+    *tps = t;
+    *n_splits = (max_len + t - 1) / t;
+}
+
+size_t workspace_need(const kvq_shape &sh, int n_splits)
+{
+    return (size_t)sh.n_seqs * sh.n_q_heads * n_splits * (sh.head_dim + 2) * sizeof(float);
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *kvq_strerror(int code)
+{
+    switch (code) {
+    case KVQ_OK: return "ok";
+    case KVQ_E_ARG: return "invalid argument (NULL or misaligned pointer, malformed value)";
+    case KVQ_E_TYPE: return "unknown cache type, or type does not match the layer's plane";
+    case KVQ_E_SHAPE: return "unsupported shape (head_dim 64/128/256, n_q_heads multiple of n_kv_heads, group <= 16, n_seqs <= 256)";
+    case KVQ_E_RANGE: return "layer, position or context length out of range";
+    case KVQ_E_WORKSPACE: return "workspace missing or too small";
+    case KVQ_E_HIP: return "HIP launch failed";
+    default: return "unknown kvq error code";
+    }
+}
+
+int kvq_plane_bytes(const kvq_shape *shape, int32_t type, size_t *codes_bytes, size_t *scale_bytes)
+{
+    int rc = check_shape(shape);
+    if (rc)
+        return rc;
+    if (!codes_bytes || !scale_bytes)
+        return KVQ_E_ARG;
+    if (!valid_type(type))
+        return KVQ_E_TYPE;
+    const int64_t rows = (int64_t)shape->n_seqs * shape->n_kv_heads * capacity(shape->max_ctx);
+    *codes_bytes = (size_t)(rows * row_code_bytes(type, shape->head_dim));
+    *scale_bytes = (type == KVQ_F16) ? 0 : (size_t)(rows * (shape->head_dim / 32) * 2);
+    return KVQ_OK;
+}
+
+int kvq_cache_check(const kvq_cache *cache) { return check_cache(cache); }
+
+int kvq_append(const kvq_cache *cache, int32_t layer, const void *K, const void *V, int32_t n_new,
+               const int32_t *pos, int32_t k_type, int32_t v_type, void *stream)
+{
+    int rc = check_layer(cache, layer);
+    if (rc)
+        return rc;
+    const kvq_shape &sh = cache->shape;
+    if (!K || !V || !pos || !aligned16(K) || !aligned16(V))
+        return KVQ_E_ARG;
+    if (!valid_type(k_type) || !valid_type(v_type))
+        return KVQ_E_TYPE;
+    if (k_type != cache->k[layer].type || v_type != cache->v[layer].type)
+        return KVQ_E_TYPE;
+    if (n_new < 1)
+        return KVQ_E_RANGE;
+    for (int s = 0; s < sh.n_seqs; s++)
+        if (pos[s] < 0 || (int64_t)pos[s] + n_new > sh.max_ctx)
+            return KVQ_E_RANGE;
+    const int64_t n_quads = (int64_t)sh.n_seqs * n_new * sh.n_kv_heads * (sh.head_dim / 32);
+    if (n_quads > ((int64_t)1 << 31) - 64)
+        return KVQ_E_SHAPE;
+
+    AppendArgs a;
+    memset(&a, 0, sizeof(a));
+    a.src[0] = (const uint16_t *)K;
+    a.src[1] = (const uint16_t *)V;
+    a.codes[0] = (uint8_t *)cache->k[layer].codes;
+    a.codes[1] = (uint8_t *)cache->v[layer].codes;
+    a.scales[0] = (uint16_t *)cache->k[layer].scales;
+    a.scales[1] = (uint16_t *)cache->v[layer].scales;
+    a.H = sh.n_kv_heads;
+    a.D = sh.head_dim;
+    a.Tc = (int32_t)capacity(sh.max_ctx);
+    a.n_new = n_new;
+    a.n_seqs = sh.n_seqs;
+    memcpy(a.pos, pos, sizeof(int32_t) * sh.n_seqs);
+    hipError_t e = launch_append(k_type, v_type, a, (int)n_quads, (hipStream_t)stream);
+    return e == hipSuccess ? KVQ_OK : KVQ_E_HIP;
+}
+
+int kvq_decode_workspace_bytes(const kvq_shape *shape, size_t *bytes)
+{
+    int rc = check_shape(shape);
+    if (rc)
+        return rc;
+    if (!bytes)
+        return KVQ_E_ARG;
+    // the most splits any call can use: KVQ_MAX_SPLITS, or one per tile
+    const int most = (int)std::min<int64_t>(KVQ_MAX_SPLITS, capacity(shape->max_ctx) / 32);
+    *bytes = workspace_need(*shape, most);
+    return KVQ_OK;
+}
+
+int kvq_attn_decode(const kvq_cache *cache, int32_t layer, const void *Q, const int32_t *ctx_len, float scale,
+                    float *out, void *workspace, size_t workspace_bytes, int32_t n_splits, void *stream)
+{
+    int rc = check_layer(cache, layer);
+    if (rc)
+        return rc;
+    const kvq_shape &sh = cache->shape;
+    if (!Q || !ctx_len || !out || !aligned16(Q) || !aligned16(out))
+        return KVQ_E_ARG;
+    if (!isfinite(scale))
+        return KVQ_E_ARG;
+    if (n_splits < 0 || n_splits > KVQ_MAX_SPLITS)
+        return KVQ_E_RANGE;
+    int max_len = 0;
+    for (int s = 0; s < sh.n_seqs; s++) {
+        if (ctx_len[s] < 1 || ctx_len[s] > sh.max_ctx)
+            return KVQ_E_RANGE;
+        max_len = std::max(max_len, ctx_len[s]);
+    }
+    int nsp, tps;
+    decode_plan(sh, max_len, n_splits, &nsp, &tps);
+    if (!workspace || !aligned16(workspace) || workspace_bytes < workspace_need(sh, nsp))
+        return KVQ_E_WORKSPACE;
+
+    const kvq_plane &kp = cache->k[layer], &vp = cache->v[layer];
+    DecodeArgs a;
+    memset(&a, 0, sizeof(a));
+    a.kc = (const uint8_t *)kp.codes;
+    a.ks = (const uint16_t *)kp.scales;
+    a.vc = (const uint8_t *)vp.codes;
+    a.vs = (const uint16_t *)vp.scales;
+    a.q = (const uint16_t *)Q;
+    a.ws = (float *)workspace;
+    a.Hq = sh.n_q_heads;
+    a.Hkv = sh.n_kv_heads;
+    a.G = sh.n_q_heads / sh.n_kv_heads;
+    a.Tc = (int32_t)capacity(sh.max_ctx);
+    a.tps = tps;
+    a.n_splits = nsp;
+    a.c2 = (float)((double)scale * 1.4426950408889634);
+    memcpy(a.ctx_len, ctx_len, sizeof(int32_t) * sh.n_seqs);
+    hipStream_t st = (hipStream_t)stream;
+    hipError_t e = launch_decode(kp.type, vp.type, sh.head_dim, a, sh.n_seqs, st);
+    if (e != hipSuccess)
+        return KVQ_E_HIP;
+
+    MergeArgs m;
+    memset(&m, 0, sizeof(m));
+    m.ws = (const float *)workspace;
+    m.out = out;
+    m.Hq = sh.n_q_heads;
+    m.tps = tps;
+    m.n_splits = nsp;
+    memcpy(m.ctx_len, ctx_len, sizeof(int32_t) * sh.n_seqs);
+    e = launch_merge(sh.head_dim, m, sh.n_seqs, st);
+    return e == hipSuccess ? KVQ_OK : KVQ_E_HIP;
+}
+
+int kvq_attn_prefill_chunk(const kvq_cache *cache, int32_t layer, const void *Q, int32_t n_tok,
+                           const int32_t *q_pos0, float scale, float *out, void *stream)
+{
+    int rc = check_layer(cache, layer);
+    if (rc)
+        return rc;
+    const kvq_shape &sh = cache->shape;
+    if (!Q || !q_pos0 || !out || !aligned16(Q) || !aligned16(out))
+        return KVQ_E_ARG;
+    if (!isfinite(scale))
+        return KVQ_E_ARG;
+    if (n_tok < 1)
+        return KVQ_E_RANGE;
+    for (int s = 0; s < sh.n_seqs; s++)
+        if (q_pos0[s] < 0 || (int64_t)q_pos0[s] + n_tok > sh.max_ctx)
+            return KVQ_E_RANGE;
+
+    const kvq_plane &kp = cache->k[layer], &vp = cache->v[layer];
+    PrefillArgs a;
+    memset(&a, 0, sizeof(a));
+    a.kc = (const uint8_t *)kp.codes;
+    a.ks = (const uint16_t *)kp.scales;
+    a.vc = (const uint8_t *)vp.codes;
+    a.vs = (const uint16_t *)vp.scales;
+    a.q = (const uint16_t *)Q;
+    a.out = out;
+    a.Hq = sh.n_q_heads;
+    a.Hkv = sh.n_kv_heads;
+    a.G = sh.n_q_heads / sh.n_kv_heads;
+    a.Tc = (int32_t)capacity(sh.max_ctx);
+    a.n_tok = n_tok;
+    a.n_seqs = sh.n_seqs;
+    a.c2 = (float)((double)scale * 1.4426950408889634);
+    memcpy(a.q_pos0, q_pos0, sizeof(int32_t) * sh.n_seqs);
+    hipError_t e = launch_prefill(kp.type, vp.type, sh.head_dim, a, (hipStream_t)stream);
+    return e == hipSuccess ? KVQ_OK : KVQ_E_HIP;
+}
+
+}  // extern "C"

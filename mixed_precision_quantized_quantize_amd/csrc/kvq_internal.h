@@ -1,0 +1,67 @@
+// kvq_internal.h -- kernel argument blocks and launchers shared by the host
+// validation layer (kvq_api.cpp) and the HIP kernels (*.hip).  Not part of
+// the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "kvq.h"
+
+namespace kvq {
+
+// Plane capacity in tokens: a whole number of 32-token tiles, so that a
+// kernel reading a full tile never leaves the plane.
+__host__ __device__ inline int64_t capacity(int64_t max_ctx) { return (max_ctx + 31) / 32 * 32; }
+
+__host__ __device__ inline int64_t row_code_bytes(int type, int64_t D)
+{
+    return type == KVQ_F16 ? 2 * D : type == KVQ_Q8_0 ? D : D / 2;
+}
+
+struct AppendArgs {
+    const uint16_t *src[2];  // K, V binary16 [S][n_new][H][D]
+    uint8_t *codes[2];       // K plane, V plane
+    uint16_t *scales[2];
+    int32_t H, D, Tc, n_new, n_seqs;
+    int32_t pos[KVQ_MAX_SEQS];
+};
+
+struct DecodeArgs {
+    const uint8_t *kc;
+    const uint16_t *ks;
+    const uint8_t *vc;
+    const uint16_t *vs;
+    const uint16_t *q;  // [S][Hq][D]
+    float *ws;          // [S][Hq][n_splits][D+2]: O (unnormalized), m (log2 units), l
+    int32_t Hq, Hkv, G, Tc, tps, n_splits;
+    float c2;  // scale * log2(e)
+    int32_t ctx_len[KVQ_MAX_SEQS];
+};
+
+struct MergeArgs {
+    const float *ws;
+    float *out;  // [S][Hq][D]
+    int32_t Hq, tps, n_splits;
+    int32_t ctx_len[KVQ_MAX_SEQS];
+};
+
+struct PrefillArgs {
+    const uint8_t *kc;
+    const uint16_t *ks;
+    const uint8_t *vc;
+    const uint16_t *vs;
+    const uint16_t *q;  // [S][n_tok][Hq][D]
+    float *out;         // [S][n_tok][Hq][D]
+    int32_t Hq, Hkv, G, Tc, n_tok, n_seqs;
+    float c2;
+    int32_t q_pos0[KVQ_MAX_SEQS];
+};
+
+// Launchers return hipSuccess or the launch error.
+hipError_t launch_append(int k_type, int v_type, const AppendArgs &a, int n_quads, hipStream_t st);
+hipError_t launch_decode(int k_type, int v_type, int D, const DecodeArgs &a, int n_seqs, hipStream_t st);
+hipError_t launch_merge(int D, const MergeArgs &a, int n_seqs, hipStream_t st);
+hipError_t launch_prefill(int k_type, int v_type, int D, const PrefillArgs &a, hipStream_t st);
+
+}  // namespace kvq

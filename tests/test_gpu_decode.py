@@ -1,0 +1,126 @@
+"""GPU parity of kvq_attn_decode (split-K flash decode + log-sum-exp merge)
+against the binary64 oracle on the same inputs.
+
+Small shapes cover all nine K/V type pairs, head_dim 64/128/256, GQA group
+sizes 1..16, several tiles with a ragged tail, ragged ctx_len across the
+batch, ctx_len = 1 and several split counts.  The named workloads run at
+their full sizes on one layer, in the launch configuration the benchmark
+times (automatic split count), and are compared on sampled outputs that the
+oracle computes one sequence at a time."""
+import itertools
+import zlib
+
+import numpy as np
+import pytest
+
+import oracle
+from kvq_testutil import assert_attn_close, assert_planes_equal, bits, zero_cache
+
+pytestmark = pytest.mark.gpu
+
+PAIRS = list(itertools.product(["f16", "q8_0", "q4_0"], repeat=2))
+
+
+def small_case(kt, vt, S, Hq, Hkv, D, T, ctx, n_splits_list, seed, kscale=3.0):
+    import torch
+
+    import mixed_precision_quantized_quantize_amd as kvq
+
+    rng = np.random.default_rng(seed)
+    cache = kvq.KVCache(1, S, Hq, Hkv, D, T, (kt, vt))
+    zero_cache(cache)
+    orc = oracle.OracleLayer(kt, vt, S, Hq, Hkv, D, T)
+    K = torch.from_numpy((rng.standard_t(4, (S, T, Hkv, D)) * kscale).astype(np.float16)).cuda()
+    V = torch.from_numpy(rng.standard_normal((S, T, Hkv, D)).astype(np.float16)).cuda()
+    Q = torch.from_numpy(rng.standard_normal((S, Hq, D)).astype(np.float16)).cuda()
+    cache.append(0, K, V, [0] * S)
+    orc.append(bits(K), bits(V), np.zeros(S, np.int32))
+    scale = 1.0 / np.sqrt(D)
+    ref = orc.attn_decode(bits(Q), np.array(ctx, np.int32), scale)
+    for ns in n_splits_list:
+        out = cache.decode(0, Q, ctx, scale, n_splits=ns)
+        torch.cuda.synchronize()
+        assert_attn_close(out.cpu().numpy(), ref, f"{kt}/{vt} D={D} G={Hq // Hkv} splits={ns}")
+
+
+@pytest.mark.parametrize("kt,vt", PAIRS)
+@pytest.mark.parametrize("D", [64, 128])
+def test_decode_pairs(kt, vt, D):
+    print(f"decode parity {kt}/{vt} D={D}", flush=True)
+    small_case(kt, vt, S=3, Hq=16, Hkv=2, D=D, T=333, ctx=[333, 37, 1], n_splits_list=[0, 1, 3],
+               seed=zlib.crc32(f"{kt}{vt}{D}".encode()) % 1000)
+
+
+@pytest.mark.parametrize("kt,vt", [("q8_0", "q4_0"), ("f16", "f16"), ("q4_0", "q8_0")])
+def test_decode_head_dim_256(kt, vt):
+    print(f"decode parity {kt}/{vt} D=256", flush=True)
+    small_case(kt, vt, S=2, Hq=8, Hkv=2, D=256, T=200, ctx=[200, 64], n_splits_list=[0, 2], seed=7)
+
+
+@pytest.mark.parametrize("G", [1, 2, 5, 16])
+def test_decode_group_sizes(G):
+    print(f"decode parity G={G}", flush=True)
+    small_case("q8_0", "q4_0", S=2, Hq=2 * G, Hkv=2, D=128, T=260, ctx=[260, 129], n_splits_list=[0, 4], seed=G)
+
+
+def test_decode_many_splits_short_context():
+    print("decode parity many splits", flush=True)
+    small_case("q8_0", "q4_0", S=1, Hq=8, Hkv=1, D=128, T=2000, ctx=[1999], n_splits_list=[0, 63, 256], seed=11)
+
+
+# ---------------------------------------------------------------- named workloads
+
+def workload_layer(name, layer, seqs_check, heads_check, pair=None, chunk_tokens=2048):
+    """Fill one layer at full size on the GPU, decode it with the automatic
+    split count, and compare sampled outputs (and the sampled sequences'
+    planes, bit for bit) with the oracle."""
+    import torch
+
+    import mixed_precision_quantized_quantize_amd as kvq
+    from mixed_precision_quantized_quantize_amd import synth
+
+    w = synth.WORKLOADS[name]
+    kt, vt = pair or w.type_pairs[0]
+    print(f"decode parity {name} layer {layer} {kt}/{vt}", flush=True)
+    cache = kvq.KVCache(1, w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim, w.ctx, (kt, vt))
+    for t0 in range(0, w.ctx, chunk_tokens):
+        n = min(chunk_tokens, w.ctx - t0)
+        K, V = synth.kv_batch(w, layer, t0, n, device="cuda")
+        cache.append(0, K, V, [t0] * w.batch)
+        del K, V
+    Q = synth.queries(w, layer, device="cuda")
+    ctx = [w.ctx] * w.batch
+    out = cache.decode(0, Q, ctx, w.scale).cpu().numpy()
+    torch.cuda.synchronize()
+    Qb = bits(Q)
+    for s in seqs_check:
+        orc = oracle.OracleLayer(kt, vt, 1, w.n_q_heads, w.n_kv_heads, w.head_dim, w.ctx)
+        K, V = synth.kv_batch(w, layer, 0, w.ctx, device="cuda", seqs=[s])
+        orc.append(bits(K), bits(V), np.zeros(1, np.int32))
+        del K, V
+        assert_planes_equal(cache, 0, orc, seq=s, n_seqs=w.batch)
+        want = np.zeros((1, w.n_q_heads), np.uint8)
+        want[0, heads_check] = 1
+        ref = orc.attn_decode(Qb[s:s + 1], np.array([w.ctx], np.int32), w.scale, want=want)
+        print(assert_attn_close(out[s, heads_check], ref[0, heads_check], f"{name} seq {s}"), flush=True)
+
+
+def test_single_layer_2k_all_outputs():
+    workload_layer("single_layer_2k", 0, [0], list(range(32)))
+
+
+@pytest.mark.parametrize("pair", [("f16", "f16"), ("q8_0", "q8_0"), ("q8_0", "q4_0"), ("q4_0", "q4_0")])
+def test_tinyllama_8k(pair):
+    workload_layer("tinyllama_8k", 21, [0], list(range(32)), pair=pair)
+
+
+def test_llama3_8b_32k_full_size_sampled():
+    workload_layer("llama3_8b_32k", 0, [0, 13], [0, 7, 8, 31])
+
+
+def test_llama31_70b_32k_full_size_sampled():
+    workload_layer("llama31_70b_32k", 0, [0], [0, 9, 63])
+
+
+def test_llama3_8b_128k_decode_full_size_sampled():
+    workload_layer("llama3_8b_128k_prefill", 0, [3], [0, 17])

@@ -146,7 +146,12 @@ int kvq_append(const kvq_cache *cache, int32_t layer, const void *K, const void 
                const int32_t *pos, int32_t k_type, int32_t v_type, void *stream);
 
 /* Workspace bytes that kvq_attn_decode needs for any ctx_len <= max_ctx and
- * any split count it may choose (n_seqs*n_q_heads*splits*(head_dim+2)*4). */
+ * any split count: a counter region of n_seqs*n_kv_heads*4 bytes rounded up
+ * to 256, then n_seqs*n_q_heads*splits*(head_dim+2)*4 bytes of split
+ * partials.  The counter region must be zero-filled before the first call
+ * (e.g. allocate the workspace zeroed); every call leaves it zero again.
+ * A workspace serves one call at a time: calls that overlap in time (other
+ * streams) need workspaces of their own. */
 int kvq_decode_workspace_bytes(const kvq_shape *shape, size_t *bytes);
 
 /* Flash-decode one query token per sequence over layer `layer`.
@@ -157,10 +162,13 @@ int kvq_decode_workspace_bytes(const kvq_shape *shape, size_t *bytes);
  *   scale   : multiplies Q.K (typically 1/sqrt(head_dim)), used as passed
  *   out     : device float32 [n_seqs][n_q_heads][head_dim]
  *   workspace, workspace_bytes: device scratch for split partials
- *   n_splits: context splits per (sequence, kv head); 0 chooses one
- * Query head hq reads kv head hq / (n_q_heads/n_kv_heads).  Two launches:
- * a split-K pass writing (max, sum, unnormalized output) partials, then a
- * log-sum-exp merge. */
+ *   n_splits: context splits per (sequence, kv head); 0 chooses; the
+ *             library may use fewer than asked (never more than its merge
+ *             can combine for this type pair, head_dim and head group)
+ * Query head hq reads kv head hq / (n_q_heads/n_kv_heads).  One launch: each
+ * workgroup handles one context split of one (sequence, kv head) and writes a
+ * (max, sum, unnormalized output) partial; the last workgroup of each
+ * (sequence, kv head) merges the partials (log-sum-exp) into `out`. */
 int kvq_attn_decode(const kvq_cache *cache, int32_t layer, const void *Q, const int32_t *ctx_len, float scale,
                     float *out, void *workspace, size_t workspace_bytes, int32_t n_splits, void *stream);
 

@@ -77,7 +77,7 @@ int check_layer(const kvq_cache *c, int32_t layer)
 
 // Split plan of a decode call: tokens per split (a multiple of the 32-token
 // tile) and the split count covering the longest context.
-void decode_plan(const kvq_shape &sh, int max_len, int32_t req, int *n_splits, int *tps)
+void decode_plan(const kvq_shape &sh, int max_len, int32_t req, int cap, int *n_splits, int *tps)
 {
     const int64_t units = (int64_t)sh.n_seqs * sh.n_kv_heads;
     int want = req;
@@ -88,16 +88,20 @@ void decode_plan(const kvq_shape &sh, int max_len, int32_t req, int *n_splits, i
         want = (int)std::min<int64_t>(KVQ_MAX_SPLITS, (target + units - 1) / units);
         want = std::min(want, std::max(1, (max_len + 127) / 128));
     }
-    want = std::max(1, std::min(want, KVQ_MAX_SPLITS));
+    want = std::max(1, std::min(want, std::min(KVQ_MAX_SPLITS, cap)));
     int t = (max_len + want - 1) / want;
     t = (t + 31) / 32 * 32;
     *tps = t;
     *n_splits = (max_len + t - 1) / t;
 }
 
+// Workspace: per-(sequence, kv head) counters first (their zero state must
+// survive calls with different split counts), then the split partials.
+size_t counters_bytes(const kvq_shape &sh) { return ((size_t)sh.n_seqs * sh.n_kv_heads * 4 + 255) / 256 * 256; }
+
 size_t workspace_need(const kvq_shape &sh, int n_splits)
 {
-    return (size_t)sh.n_seqs * sh.n_q_heads * n_splits * (sh.head_dim + 2) * sizeof(float);
+    return counters_bytes(sh) + (size_t)sh.n_seqs * sh.n_q_heads * n_splits * (sh.head_dim + 2) * sizeof(float);
 }
 
 }  // namespace
@@ -207,12 +211,13 @@ int kvq_attn_decode(const kvq_cache *cache, int32_t layer, const void *Q, const 
             return KVQ_E_RANGE;
         max_len = std::max(max_len, ctx_len[s]);
     }
+    const kvq_plane &kp = cache->k[layer], &vp = cache->v[layer];
+    const int cap = decode_split_cap(kp.type, vp.type, sh.head_dim, sh.n_q_heads / sh.n_kv_heads);
     int nsp, tps;
-    decode_plan(sh, max_len, n_splits, &nsp, &tps);
+    decode_plan(sh, max_len, n_splits, cap, &nsp, &tps);
     if (!workspace || !aligned16(workspace) || workspace_bytes < workspace_need(sh, nsp))
         return KVQ_E_WORKSPACE;
 
-    const kvq_plane &kp = cache->k[layer], &vp = cache->v[layer];
     DecodeArgs a;
     memset(&a, 0, sizeof(a));
     a.kc = (const uint8_t *)kp.codes;
@@ -220,7 +225,9 @@ int kvq_attn_decode(const kvq_cache *cache, int32_t layer, const void *Q, const 
     a.vc = (const uint8_t *)vp.codes;
     a.vs = (const uint16_t *)vp.scales;
     a.q = (const uint16_t *)Q;
-    a.ws = (float *)workspace;
+    a.out = out;
+    a.counters = (uint32_t *)workspace;
+    a.ws = (float *)((char *)workspace + counters_bytes(sh));
     a.Hq = sh.n_q_heads;
     a.Hkv = sh.n_kv_heads;
     a.G = sh.n_q_heads / sh.n_kv_heads;
@@ -229,20 +236,7 @@ int kvq_attn_decode(const kvq_cache *cache, int32_t layer, const void *Q, const 
     a.n_splits = nsp;
     a.c2 = (float)((double)scale * 1.4426950408889634);
     memcpy(a.ctx_len, ctx_len, sizeof(int32_t) * sh.n_seqs);
-    hipStream_t st = (hipStream_t)stream;
-    hipError_t e = launch_decode(kp.type, vp.type, sh.head_dim, a, sh.n_seqs, st);
-    if (e != hipSuccess)
-        return KVQ_E_HIP;
-
-    MergeArgs m;
-    memset(&m, 0, sizeof(m));
-    m.ws = (const float *)workspace;
-    m.out = out;
-    m.Hq = sh.n_q_heads;
-    m.tps = tps;
-    m.n_splits = nsp;
-    memcpy(m.ctx_len, ctx_len, sizeof(int32_t) * sh.n_seqs);
-    e = launch_merge(sh.head_dim, m, sh.n_seqs, st);
+    hipError_t e = launch_decode(kp.type, vp.type, sh.head_dim, a, sh.n_seqs, (hipStream_t)stream);
     return e == hipSuccess ? KVQ_OK : KVQ_E_HIP;
 }
 

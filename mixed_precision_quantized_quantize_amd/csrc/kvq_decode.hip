@@ -1,28 +1,30 @@
-// kvq_decode.hip -- split-K flash decode over the quantized cache, then a
-// log-sum-exp merge of the split partials.
+// kvq_decode.hip -- split-K flash decode over the quantized cache with the
+// log-sum-exp merge of the split partials folded into the same launch.
 //
 // Flash attention in the sense of the llama.cpp guide's "Flash Attention"
 // section (tiled, the score matrix never materialized, exactly softmax
-// attention), reading the quantized blocks directly as the KVSplit page's
-// discussion asks ("integrated directly into FlashAttention") -- the
-// quantized-V-requires-flash-attention rule of the llama.cpp issue.
+// attention), reading the quantized blocks directly -- the KVSplit page's
+// discussion expects the gain "integrated directly into FlashAttention", and
+// the llama.cpp issue shows a quantized V cache is only usable that way.
 //
 // One workgroup = (split of the context, kv head, sequence), four waves.
-// Each wave walks 32-token tiles of the split and serves the whole GQA group
+// Each wave walks 32-token tiles of its split and serves the whole GQA group
 // (up to 16 query heads) of its kv head with two matrix-core contractions
 // per tile, both v_mfma_f32_16x16x32_f16:
-//   S^T[token][head] = K[token][c] . Q^T[c][head]   (one MFMA per 16 tokens
-//       and 32-channel block: the raw codes are exact in binary16, the
-//       block's K scale is applied to the MFMA result per token)
-//   O^T[chan][head] += V^T[chan][token] . P'[token][head]  (one MFMA per
-//       16 channels and 32 tokens; P' = p * (V scale of that token and
-//       block), rounded once to binary16)
-// The score layout of the first product is exactly the operand layout the
-// second one needs, so probabilities never leave registers.  The V plane is
-// stored 8 tokens interleaved so each lane's P.V operand (8 tokens of one
-// channel) is a single 8- or 16-byte load.  Online softmax runs in base 2
-// (scores pre-multiplied by scale*log2 e).  The four waves' (m, l, O) merge
-// in LDS and the workgroup writes one partial per (query head, split).
+//   S^T[token][head] = K[token][c] . Q^T[c][head]  -- one MFMA per 16 tokens
+//       and 32-channel block; the raw codes are exact in binary16 and the
+//       block's K scale multiplies the MFMA result per token;
+//   O^T[chan][head] += V^T[chan][token] . P'[token][head]  -- one MFMA per 16
+//       channels and 32 tokens; P' = binary16(p) * V scale of (token, block).
+// The score layout of the first product is exactly the operand layout of the
+// second, so probabilities never leave registers.  The V plane stores 8
+// tokens interleaved, so a lane's P.V operand (8 tokens of one channel) is
+// one 8- or 16-byte load.  Online softmax runs in base 2 (scores times
+// scale*log2 e).  The next tile's codes and scales are loaded while the
+// current one is computed.  The four waves' (m, l, O) merge in LDS; each
+// workgroup writes one partial per query head, and the last workgroup of a
+// (sequence, kv head) -- found with a device-scope counter -- merges all the
+// partials and writes the normalized output.
 #include "kvq_internal.h"
 
 namespace kvq {
@@ -30,6 +32,7 @@ namespace {
 
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef _Float16 half2 __attribute__((ext_vector_type(2)));
+typedef float float2v __attribute__((ext_vector_type(2)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -51,12 +54,19 @@ __device__ inline half8 pack4(uint32_t a, uint32_t b, uint32_t c, uint32_t d)
     return __builtin_bit_cast(half8, v);
 }
 
-// 8 int8 codes -> 8 exact binary16 values.  Bytes are biased to unsigned,
-// placed under the exponent pattern 0x64 (binary16 1024 + u), then 1152 is
-// subtracted: exact for every code.
-__device__ inline half8 deq_q8(u32x2 w)
+// (y & mask) | (c & ~mask) in one instruction.
+__device__ inline uint32_t bfi(uint32_t mask, uint32_t y, uint32_t c)
 {
-    const uint32_t x0 = w.x ^ 0x80808080u, x1 = w.y ^ 0x80808080u;
+    uint32_t r;
+    asm("v_bfi_b32 %0, %1, %2, %3" : "=v"(r) : "v"(mask), "v"(y), "v"(c));
+    return r;
+}
+
+// 8 int8 codes -> 8 exact binary16 values: bias to unsigned, place each byte
+// under the exponent pattern 0x64 (binary16 1024 + u), subtract 1152.
+__device__ inline half8 deq_q8(uint32_t w0, uint32_t w1)
+{
+    const uint32_t x0 = w0 ^ 0x80808080u, x1 = w1 ^ 0x80808080u;
     const half2 off = {(_Float16)1152.0f, (_Float16)1152.0f};
     uint32_t r0 = h2_bits(bits_h2(__builtin_amdgcn_perm(0x64646464u, x0, 0x04010400u)) - off);
     uint32_t r1 = h2_bits(bits_h2(__builtin_amdgcn_perm(0x64646464u, x0, 0x04030402u)) - off);
@@ -65,16 +75,162 @@ __device__ inline half8 deq_q8(u32x2 w)
     return pack4(r0, r1, r2, r3);
 }
 
-// 4-bit fields at bit offsets sh and sh+16 -> binary16 pair (c - 8), exact.
-__device__ inline uint32_t nib2(uint32_t x, int sh)
+// Two q4_0 code bytes in the low bytes of each 16-bit half of y -> binary16
+// pairs (c - 8) of their low nibbles and of their high nibbles, exact:
+// low:  binary16 1024 + c       minus 1032
+// high: binary16 1024 + 16 c    times 1/16 minus 72
+__device__ inline void deq_q4_pair(uint32_t y, uint32_t &lo, uint32_t &hi)
 {
-    const half2 off = {(_Float16)1032.0f, (_Float16)1032.0f};
-    return h2_bits(bits_h2(((x >> sh) & 0x000F000Fu) | 0x64006400u) - off);
+    const uint32_t e = 0x64006400u;
+    const half2 k1032 = {(_Float16)1032.0f, (_Float16)1032.0f};
+    const half2 k16 = {(_Float16)0.0625f, (_Float16)0.0625f};
+    const half2 k72 = {(_Float16)-72.0f, (_Float16)-72.0f};
+    lo = h2_bits(bits_h2(bfi(0x000F000Fu, y, e)) - k1032);
+    hi = h2_bits(__builtin_elementwise_fma(bits_h2(bfi(0x00F000F0u, y, e)), k16, k72));
 }
 
-// One dword of 4 bytes b0..b3 -> low nibbles in order (b0, b2, b1, b3).
-__device__ inline void deq_q4_lo(uint32_t x, uint32_t &a, uint32_t &b) { a = nib2(x, 0); b = nib2(x, 8); }
-__device__ inline void deq_q4_hi(uint32_t x, uint32_t &a, uint32_t &b) { a = nib2(x, 4); b = nib2(x, 12); }
+// K codes of one block for one lane -> A operand (8 channels of one token).
+template <int KT>
+__device__ inline half8 k_operand(const uint32_t *w)
+{
+    if (KT == KVQ_F16)
+        return pack4(w[0], w[1], w[2], w[3]);
+    if (KT == KVQ_Q8_0)
+        return deq_q8(w[0], w[1]);
+    // q4_0: bytes 4j..4j+3 hold elements 4j+k (low) and 16+4j+k (high)
+    uint32_t l01, h01, l23, h23;
+    deq_q4_pair(__builtin_amdgcn_perm(w[0], w[0], 0x0C010C00u), l01, h01);
+    deq_q4_pair(__builtin_amdgcn_perm(w[0], w[0], 0x0C030C02u), l23, h23);
+    return pack4(l01, l23, h01, h23);
+}
+
+// Channel (within a 32-block) carried by k-slot r of lane group j in the Q.K
+// product; it must match how k_operand unpacks that lane's codes.
+template <int KT>
+__device__ inline int qk_chan(int j, int r)
+{
+    if (KT == KVQ_Q4_0)
+        return (r < 4) ? 4 * j + r : 16 + 4 * j + (r - 4);
+    return 8 * j + r;
+}
+
+// ------------------------------------------------------------------ tile geometry
+// One wave stages one 32-token tile in LDS: K codes (token-major rows), K
+// scales, V codes (8-token groups), V scales -- four contiguous ranges of the
+// planes, copied with direct-to-LDS 16-byte loads (every instruction reads one
+// contiguous kilobyte).  16-byte chunks are XOR-swizzled within a K row / V
+// group so that the MFMA-operand reads below hit distinct LDS banks.
+template <int KT, int VT, int D>
+struct Geo {
+    static constexpr int NB = D / 32, NCT = D / 16;
+    static constexpr int RK = (KT == KVQ_F16) ? 2 * D : (KT == KVQ_Q8_0) ? D : D / 2;  // K row code bytes
+    static constexpr int RV = (VT == KVQ_F16) ? 2 * D : (VT == KVQ_Q8_0) ? D : D / 2;  // V row code bytes
+    static constexpr int K_BYTES = TILE * RK;
+    static constexpr int KS_BYTES = (KT == KVQ_F16) ? 0 : TILE * NB * 2;
+    static constexpr int V_BYTES = TILE * RV;
+    static constexpr int VS_BYTES = (VT == KVQ_F16) ? 0 : TILE * NB * 2;
+    static constexpr int K_OFF = 0, KS_OFF = K_BYTES, V_OFF = KS_OFF + KS_BYTES, VS_OFF = V_OFF + V_BYTES;
+    static constexpr int BYTES = VS_OFF + VS_BYTES;  // one wave's tile
+    static constexpr int CPR = RK / 16;              // 16-byte chunks per K row
+    static constexpr int CPG = 8 * RV / 16;          // 16-byte chunks per 8-token V group
+    static constexpr int LDS_A = WAVES * BYTES;
+};
+
+// XOR swizzle of the chunk index within K row r (bank-conflict-free reads of
+// the Q.K operand for every type and head_dim; chosen with a bank model).
+template <int CPR>
+__device__ inline int kswz(int r)
+{
+    if (CPR <= 4)
+        return (r ^ (r >> 3)) & (CPR - 1);
+    if (CPR == 8)
+        return ((r >> 1) ^ (r >> 2)) & 7;
+    return (r ^ (r >> 1)) & (CPR - 1);
+}
+template <int VT, int CPG>
+__device__ inline int vswz(int g)
+{
+    return (VT == KVQ_F16) ? 0 : (8 * g) & (CPG - 1);
+}
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(1))) void gbl_void_t;
+
+// 64 lanes x `size` bytes from per-lane global addresses into LDS at
+// dst + lane * size (dst wave-uniform).
+template <int SIZE>
+__device__ inline void dma(const void *src, void *dst)
+{
+    static_assert(SIZE == 16 || SIZE == 4, "lane placement checked for 4- and 16-byte copies only");
+    if constexpr (SIZE == 16)
+        __builtin_amdgcn_global_load_lds((gbl_void_t *)src, (lds_void_t *)dst, 16, 0, 0);
+    else
+        __builtin_amdgcn_global_load_lds((gbl_void_t *)src, (lds_void_t *)dst, 4, 0, 0);
+}
+
+// Per-lane constant byte offsets of the tile copy (source side, relative to
+// the tile's first K row / first V group).
+template <int KT, int VT, int D>
+struct DmaOffsets {
+    using g = Geo<KT, VT, D>;
+    int k[g::K_BYTES / 1024];
+    int v[g::V_BYTES / 1024];
+    __device__ void init(int lane)
+    {
+#pragma unroll
+        for (int i = 0; i < g::K_BYTES / 1024; i++) {
+            const int sl = 64 * i + lane, r = sl / g::CPR, c = (sl % g::CPR) ^ kswz<g::CPR>(r);
+            k[i] = r * g::RK + 16 * c;
+        }
+#pragma unroll
+        for (int i = 0; i < g::V_BYTES / 1024; i++) {
+            const int sl = 64 * i + lane, grp = sl / g::CPG, c = (sl % g::CPG) ^ vswz<VT, g::CPG>(grp);
+            v[i] = grp * (8 * g::RV) + 16 * c;
+        }
+    }
+};
+
+template <int KT, int VT, int D>
+__device__ inline void issue_tile(uint8_t *buf, int tb, int lane, const DmaOffsets<KT, VT, D> &off, const uint8_t *kc,
+                                  const uint16_t *ks, const uint8_t *vc, const uint16_t *vs)
+{
+    using g = Geo<KT, VT, D>;
+    const uint8_t *ksrc = kc + (int64_t)tb * g::RK;
+#pragma unroll
+    for (int i = 0; i < g::K_BYTES / 1024; i++)
+        dma<16>(ksrc + off.k[i], buf + g::K_OFF + 1024 * i);
+    if (KT != KVQ_F16) {
+        const uint8_t *src = reinterpret_cast<const uint8_t *>(ks + (int64_t)tb * g::NB);
+        if (g::KS_BYTES == 128) {
+            if (lane < 32)  // 4 bytes on half the lanes (lane l lands at +4 l)
+                dma<4>(src + 4 * lane, buf + g::KS_OFF);
+        } else {
+#pragma unroll
+            for (int i = 0; i < g::KS_BYTES / 256; i++)
+                dma<4>(src + 256 * i + 4 * lane, buf + g::KS_OFF + 256 * i);
+        }
+    }
+    const uint8_t *vsrc = vc + (int64_t)(tb >> 3) * 8 * g::RV;
+#pragma unroll
+    for (int i = 0; i < g::V_BYTES / 1024; i++)
+        dma<16>(vsrc + off.v[i], buf + g::V_OFF + 1024 * i);
+    if (VT != KVQ_F16) {
+        const uint8_t *src = reinterpret_cast<const uint8_t *>(vs + (int64_t)(tb >> 3) * g::NB * 8);
+        if (g::VS_BYTES == 128) {
+            if (lane < 32)  // 4 bytes on half the lanes (lane l lands at +4 l)
+                dma<4>(src + 4 * lane, buf + g::VS_OFF);
+        } else {
+#pragma unroll
+            for (int i = 0; i < g::VS_BYTES / 256; i++)
+                dma<4>(src + 256 * i + 4 * lane, buf + g::VS_OFF + 256 * i);
+        }
+    }
+}
+
+// Split partials cross workgroups (and XCDs): relaxed atomics of device
+// scope, coherent between all XCDs, with no L2 writeback or invalidation.
+__device__ inline void st_dev(float *p, float v) { __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
+__device__ inline float ld_dev(const float *p) { return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
 
 __device__ inline float half_at(const uint32_t *w, int idx)
 {
@@ -82,29 +238,16 @@ __device__ inline float half_at(const uint32_t *w, int idx)
     return (float)__builtin_bit_cast(_Float16, (uint16_t)((idx & 1) ? (v >> 16) : (v & 0xffffu)));
 }
 
-// Channel (within a 32-block) feeding k-slot r of lane group j in the Q.K
-// product: it must match how that lane's K codes unpack.
-template <int KT>
-__device__ inline int qk_chan(int j, int r)
-{
-    if (KT == KVQ_Q4_0) {
-        constexpr int ord[8] = {0, 2, 1, 3, 16, 18, 17, 19};
-        return 4 * j + ord[r];
-    }
-    return 8 * j + r;
-}
-
 template <int KT, int VT, int D>
-__global__ __launch_bounds__(256) void decode_split_kernel(const DecodeArgs a)
+__global__ __launch_bounds__(64 * WAVES) void decode_kernel(const DecodeArgs a)
 {
-    constexpr int NB = D / 32;   // quant blocks per row
-    constexpr int NCT = D / 16;  // 16-channel output tiles
-    constexpr int64_t RK = (KT == KVQ_F16) ? 2 * D : (KT == KVQ_Q8_0) ? D : D / 2;
-    constexpr int64_t UV = (VT == KVQ_Q4_0) ? D / 2 : D;  // V units per row
+    using g = Geo<KT, VT, D>;
+    constexpr int NB = g::NB, NCT = g::NCT;
 
-    __shared__ float sm_o[WAVES][16][D];
+    __shared__ __attribute__((aligned(16))) uint8_t lds_a[g::LDS_A];
     __shared__ float sm_m[WAVES][16];
     __shared__ float sm_l[WAVES][16];
+    __shared__ int sm_last;
 
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int n = lane & 15, j = lane >> 4;
@@ -112,8 +255,9 @@ __global__ __launch_bounds__(256) void decode_split_kernel(const DecodeArgs a)
     const int ctx = a.ctx_len[s];
     const int t_begin = split * a.tps;
     if (t_begin >= ctx)
-        return;  // the merge reads only splits that hold tokens
+        return;  // holds no tokens: not counted by the merge
     const int t_end = min(t_begin + a.tps, ctx);
+    const int nsp = (ctx + a.tps - 1) / a.tps;
     const int G = a.G;
     const int64_t pair = (int64_t)s * a.Hkv + h;
     const int64_t Tc = a.Tc;
@@ -122,7 +266,7 @@ __global__ __launch_bounds__(256) void decode_split_kernel(const DecodeArgs a)
     half8 qb[NB];
     {
         const _Float16 *qrow =
-            reinterpret_cast<const _Float16 *>(a.q) + ((int64_t)s * a.Hq + (int64_t)h * G + n) * D;
+            reinterpret_cast<const _Float16 *>(a.q) + ((int64_t)s * a.Hq + (int64_t)h * G + min(n, G - 1)) * D;
 #pragma unroll
         for (int b = 0; b < NB; b++)
 #pragma unroll
@@ -130,97 +274,114 @@ __global__ __launch_bounds__(256) void decode_split_kernel(const DecodeArgs a)
                 qb[b][r] = (n < G) ? qrow[32 * b + qk_chan<KT>(j, r)] : (_Float16)0.0f;
     }
 
-    const uint8_t *kc = a.kc + pair * Tc * RK;
+    const uint8_t *kc = a.kc + pair * Tc * g::RK;
     const uint16_t *ks = a.ks + pair * Tc * NB;
-    const uint8_t *vc = a.vc + pair * (Tc / 8) * UV * 8 * (VT == KVQ_F16 ? 2 : 1);
+    const uint8_t *vc = a.vc + pair * (Tc / 8) * 8 * g::RV;
     const uint16_t *vs = a.vs + pair * (Tc / 8) * NB * 8;
     const float c2 = a.c2;
 
-    float m_run = -INFINITY;  // running max (base-2 units) of head n; equal in all 4 lane groups
+    DmaOffsets<KT, VT, D> doff;
+    doff.init(lane);
+    // per-lane LDS read offsets of the operands (constant over tiles)
+    int k_rd[2][NB];  // K operand of S-tile T, block b
+#pragma unroll
+    for (int T = 0; T < 2; T++) {
+        const int r = 8 * (n >> 2) + 4 * T + (n & 3);
+#pragma unroll
+        for (int b = 0; b < NB; b++) {
+            int c, within;
+            if (KT == KVQ_Q8_0) c = 2 * b + (j >> 1), within = 8 * (j & 1);
+            else if (KT == KVQ_Q4_0) c = b, within = 4 * j;
+            else c = 4 * b + j, within = 0;
+            k_rd[T][b] = g::K_OFF + (r * g::CPR + (c ^ kswz<g::CPR>(r))) * 16 + within;
+        }
+    }
+    constexpr int VL = (VT == KVQ_Q4_0) ? NB : NCT;  // V operand reads per tile
+    int v_rd[VL];
+#pragma unroll
+    for (int i = 0; i < VL; i++) {
+        const int u = 16 * i + n;  // q4_0: byte n of block i; else channel 16i+n
+        const int c = (VT == KVQ_F16) ? u : (u >> 1);
+        const int within = (VT == KVQ_F16) ? 0 : 8 * (u & 1);
+        v_rd[i] = g::V_OFF + (j * g::CPG + (c ^ vswz<VT, g::CPG>(j))) * 16 + within;
+    }
+
+    float m_run = -INFINITY;  // running max (base 2) of head n, equal in the 4 lane groups
     float l_run = 0.0f;       // this lane's share of the running sum
     floatx4 o[NCT];
 #pragma unroll
     for (int ct = 0; ct < NCT; ct++)
         o[ct] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
 
-    for (int tb = t_begin + TILE * wave; tb < t_end; tb += TILE * WAVES) {
-        // ---------------- loads
-        // K codes, A operand rows: S-tile T, row n -> token tb + 8(n/4) + 4T + n%4
-        u32x4 kraw[2][NB];
+    // The operands of one tile, read from its LDS copy into registers.
+    struct Ops {
+        u32x4 k[2][NB];                 // K codes per S-tile and block (words used by the type)
+        uint32_t ks[4 * NB];            // K scales: token r, block b at half r*NB+b
+        u32x4 v[VL];                    // V codes per read
+        u32x4 vs[NB];                   // V scales: block b, tokens 0..7
+    };
+    auto read_ops = [&](const uint8_t *buf, Ops &op) {
 #pragma unroll
-        for (int T = 0; T < 2; T++) {
-            const int64_t tok = tb + 8 * (n >> 2) + 4 * T + (n & 3);
-            const uint8_t *row = kc + tok * RK;
+        for (int T = 0; T < 2; T++)
 #pragma unroll
             for (int b = 0; b < NB; b++) {
                 if (KT == KVQ_F16) {
-                    kraw[T][b] = *reinterpret_cast<const u32x4 *>(row + 2 * (32 * b + 8 * j));
+                    op.k[T][b] = *reinterpret_cast<const u32x4 *>(buf + k_rd[T][b]);
                 } else if (KT == KVQ_Q8_0) {
-                    u32x2 w = *reinterpret_cast<const u32x2 *>(row + 32 * b + 8 * j);
-                    kraw[T][b] = u32x4{w.x, w.y, 0u, 0u};
+                    const u32x2 w = *reinterpret_cast<const u32x2 *>(buf + k_rd[T][b]);
+                    op.k[T][b] = u32x4{w.x, w.y, 0u, 0u};
                 } else {
-                    uint32_t w = *reinterpret_cast<const uint32_t *>(row + 16 * b + 4 * j);
-                    kraw[T][b] = u32x4{w, 0u, 0u, 0u};
+                    op.k[T][b] = u32x4{*reinterpret_cast<const uint32_t *>(buf + k_rd[T][b]), 0u, 0u, 0u};
                 }
             }
-        }
-        // K scales of this lane's 8 output tokens tb+8j .. tb+8j+7, all blocks
-        uint32_t ksc[4 * NB];
         if (KT != KVQ_F16) {
-            const u32x4 *p = reinterpret_cast<const u32x4 *>(ks + (int64_t)(tb + 8 * j) * NB);
+            const u32x4 *p = reinterpret_cast<const u32x4 *>(buf + g::KS_OFF + 16 * NB * j);
 #pragma unroll
             for (int i = 0; i < NB; i++) {
-                u32x4 w = p[i];
-                ksc[4 * i] = w.x, ksc[4 * i + 1] = w.y, ksc[4 * i + 2] = w.z, ksc[4 * i + 3] = w.w;
+                const u32x4 w = p[i];
+                op.ks[4 * i] = w.x, op.ks[4 * i + 1] = w.y, op.ks[4 * i + 2] = w.z, op.ks[4 * i + 3] = w.w;
             }
         }
-        // V: group of 8 tokens tb+8j.., unit (channel byte) per output tile
-        const int64_t vgrp = (int64_t)(tb >> 3) + j;
-        u32x4 vraw[NCT];
 #pragma unroll
-        for (int ct = 0; ct < NCT; ct++) {
+        for (int i = 0; i < VL; i++) {
             if (VT == KVQ_F16) {
-                vraw[ct] = *reinterpret_cast<const u32x4 *>(vc + 2 * ((vgrp * UV + 16 * ct + n) * 8));
-            } else if (VT == KVQ_Q8_0) {
-                u32x2 w = *reinterpret_cast<const u32x2 *>(vc + (vgrp * UV + 16 * ct + n) * 8);
-                vraw[ct] = u32x4{w.x, w.y, 0u, 0u};
-            } else if ((ct & 1) == 0) {
-                u32x2 w = *reinterpret_cast<const u32x2 *>(vc + (vgrp * UV + 16 * (ct >> 1) + n) * 8);
-                vraw[ct] = u32x4{w.x, w.y, 0u, 0u};
+                op.v[i] = *reinterpret_cast<const u32x4 *>(buf + v_rd[i]);
             } else {
-                vraw[ct] = vraw[ct - 1];
+                const u32x2 w = *reinterpret_cast<const u32x2 *>(buf + v_rd[i]);
+                op.v[i] = u32x4{w.x, w.y, 0u, 0u};
             }
         }
-        uint32_t vsc[4 * NB];
         if (VT != KVQ_F16) {
-            const u32x4 *p = reinterpret_cast<const u32x4 *>(vs + (vgrp * NB) * 8);
 #pragma unroll
-            for (int b = 0; b < NB; b++) {
-                u32x4 w = p[b];
-                vsc[4 * b] = w.x, vsc[4 * b + 1] = w.y, vsc[4 * b + 2] = w.z, vsc[4 * b + 3] = w.w;
-            }
+            for (int b = 0; b < NB; b++)
+                op.vs[b] = *reinterpret_cast<const u32x4 *>(buf + g::VS_OFF + (j * NB + b) * 16);
         }
+    };
 
+    // One 32-token tile starting at token tb, from its operands in registers.
+    auto process = [&](const Ops &op, const int tb) {
         // ---------------- scores: S^T tile T, lane holds tokens 8j+4T+i, head n
+        const uint32_t *ksc = op.ks;
         floatx4 sacc[2];
 #pragma unroll
         for (int T = 0; T < 2; T++) {
             sacc[T] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
             for (int b = 0; b < NB; b++) {
+                half8 ka;
                 if (KT == KVQ_F16) {
-                    sacc[T] = mfma(__builtin_bit_cast(half8, kraw[T][b]), qb[b], sacc[T]);
+                    const u32x4 w = op.k[T][b];
+                    ka = pack4(w.x, w.y, w.z, w.w);
+                } else if (KT == KVQ_Q8_0) {
+                    ka = deq_q8(op.k[T][b].x, op.k[T][b].y);
                 } else {
-                    half8 ka;
-                    if (KT == KVQ_Q8_0) {
-                        ka = deq_q8(u32x2{kraw[T][b].x, kraw[T][b].y});
-                    } else {
-                        uint32_t r0, r1, r2, r3;
-                        deq_q4_lo(kraw[T][b].x, r0, r1);
-                        deq_q4_hi(kraw[T][b].x, r2, r3);
-                        ka = pack4(r0, r1, r2, r3);
-                    }
-                    floatx4 c = mfma(ka, qb[b], floatx4{0.0f, 0.0f, 0.0f, 0.0f});
+                    const uint32_t w = op.k[T][b].x;
+                    ka = k_operand<KVQ_Q4_0>(&w);
+                }
+                if (KT == KVQ_F16) {
+                    sacc[T] = mfma(ka, qb[b], sacc[T]);
+                } else {
+                    const floatx4 c = mfma(ka, qb[b], floatx4{0.0f, 0.0f, 0.0f, 0.0f});
 #pragma unroll
                     for (int i = 0; i < 4; i++)
                         sacc[T][i] = __builtin_fmaf(half_at(ksc, (4 * T + i) * NB + b), c[i], sacc[T][i]);
@@ -228,140 +389,242 @@ __global__ __launch_bounds__(256) void decode_split_kernel(const DecodeArgs a)
             }
         }
 
-        // ---------------- online softmax (base 2), token r = 4T + i of group j
+        // ---------------- online softmax (base 2); token r of group j is tb+8j+r
         float x[8];
 #pragma unroll
         for (int r = 0; r < 8; r++)
             x[r] = sacc[r >> 2][r & 3] * c2;
-        if (tb + TILE > t_end) {
+        const bool tail = tb + TILE > t_end;
+        uint32_t keep[4] = {0xFFFFFFFFu, 0xFFFFFFFFu, 0xFFFFFFFFu, 0xFFFFFFFFu};  // per token pair
+        if (tail) {
 #pragma unroll
             for (int r = 0; r < 8; r++)
-                if (tb + 8 * j + r >= t_end)
+                if (tb + 8 * j + r >= t_end) {
                     x[r] = -INFINITY;
+                    keep[r >> 1] &= (r & 1) ? 0x0000FFFFu : 0xFFFF0000u;
+                }
         }
-        float mt = x[0];
-#pragma unroll
-        for (int r = 1; r < 8; r++)
-            mt = fmaxf(mt, x[r]);
+        float mt = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])), fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
         mt = fmaxf(mt, __shfl_xor(mt, 16));
         mt = fmaxf(mt, __shfl_xor(mt, 32));
-        const float m_new = fmaxf(m_run, mt);
-        const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+        if (__any(mt > m_run)) {
+            const float m_new = fmaxf(m_run, mt);
+            const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);  // 0 on the first tile
+            l_run *= alpha;
+#pragma unroll
+            for (int ct = 0; ct < NCT; ct++)
+                o[ct] *= alpha;
+            m_run = m_new;
+        }
         float p[8];
-        float psum = 0.0f;
 #pragma unroll
         for (int r = 0; r < 8; r++) {
-            p[r] = __builtin_amdgcn_exp2f(x[r] - m_new);
-            psum += p[r];
+            p[r] = __builtin_amdgcn_exp2f(x[r] - m_run);
+            l_run += p[r];
         }
-        l_run = l_run * alpha + psum;
-        m_run = m_new;
+        // binary16 probabilities, token pairs (0,1) (2,3) (4,5) (6,7)
+        uint32_t p16[4];
 #pragma unroll
-        for (int ct = 0; ct < NCT; ct++)
-            o[ct] *= alpha;
+        for (int i = 0; i < 4; i++)
+            p16[i] = h2_bits(__builtin_convertvector((float2v){p[2 * i], p[2 * i + 1]}, half2));
 
         // ---------------- O^T += V^T . P'
 #pragma unroll
-        for (int ct = 0; ct < NCT; ct++) {
-            const int b = ct >> 1;
-            half8 va, pb;
+        for (int b = 0; b < NB; b++) {
+            half8 pb;  // P' of block b in k-slot order = token order 0..7
             if (VT == KVQ_F16) {
-                va = __builtin_bit_cast(half8, vraw[ct]);
-#pragma unroll
-                for (int r = 0; r < 8; r++)
-                    pb[r] = (_Float16)p[r];
-            } else if (VT == KVQ_Q8_0) {
-                va = deq_q8(u32x2{vraw[ct].x, vraw[ct].y});
-#pragma unroll
-                for (int r = 0; r < 8; r++)
-                    pb[r] = (_Float16)(p[r] * half_at(vsc, 8 * b + r));
+                pb = pack4(p16[0], p16[1], p16[2], p16[3]);
             } else {
-                uint32_t r0, r1, r2, r3;
-                if ((ct & 1) == 0) {
-                    deq_q4_lo(vraw[ct].x, r0, r1);
-                    deq_q4_lo(vraw[ct].y, r2, r3);
-                } else {
-                    deq_q4_hi(vraw[ct].x, r0, r1);
-                    deq_q4_hi(vraw[ct].y, r2, r3);
-                }
-                va = pack4(r0, r1, r2, r3);  // token order 0,2,1,3,4,6,5,7
-                constexpr int ord[8] = {0, 2, 1, 3, 4, 6, 5, 7};
-#pragma unroll
-                for (int r = 0; r < 8; r++)
-                    pb[r] = (_Float16)(p[ord[r]] * half_at(vsc, 8 * b + ord[r]));
+                // positions past the context may hold any bits: a masked pair
+                // is forced to +0 instead of 0 * (scale bits)
+                const u32x4 dv = op.vs[b];
+                pb = pack4(h2_bits(bits_h2(p16[0]) * bits_h2(dv.x)) & keep[0],
+                           h2_bits(bits_h2(p16[1]) * bits_h2(dv.y)) & keep[1],
+                           h2_bits(bits_h2(p16[2]) * bits_h2(dv.z)) & keep[2],
+                           h2_bits(bits_h2(p16[3]) * bits_h2(dv.w)) & keep[3]);
             }
-            o[ct] = mfma(va, pb, o[ct]);
+            if (VT == KVQ_Q4_0) {
+                // bytes of tokens 0..3 (word 0) and 4..7 (word 1); low nibbles feed
+                // channel tile 2b, high nibbles tile 2b+1
+                const u32x4 w = op.v[b];
+                uint32_t l01, h01, l23, h23, l45, h45, l67, h67;
+                deq_q4_pair(__builtin_amdgcn_perm(w.x, w.x, 0x0C010C00u), l01, h01);
+                deq_q4_pair(__builtin_amdgcn_perm(w.x, w.x, 0x0C030C02u), l23, h23);
+                deq_q4_pair(__builtin_amdgcn_perm(w.y, w.y, 0x0C010C00u), l45, h45);
+                deq_q4_pair(__builtin_amdgcn_perm(w.y, w.y, 0x0C030C02u), l67, h67);
+                o[2 * b] = mfma(pack4(l01, l23, l45, l67), pb, o[2 * b]);
+                o[2 * b + 1] = mfma(pack4(h01, h23, h45, h67), pb, o[2 * b + 1]);
+            } else {
+#pragma unroll
+                for (int hh = 0; hh < 2; hh++) {
+                    const int ct = 2 * b + hh;
+                    half8 va;
+                    const u32x4 w = op.v[ct];
+                    if (VT == KVQ_F16) {
+                        // a masked token's value may be any bits, even NaN
+                        va = pack4(w.x & keep[0], w.y & keep[1], w.z & keep[2], w.w & keep[3]);
+                    } else {
+                        va = deq_q8(w.x, w.y);
+                    }
+                    o[ct] = mfma(va, pb, o[ct]);
+                }
+            }
         }
-    }
+    };
 
-    // ---------------- wave totals, then merge the four waves in LDS
-    float l_tot = l_run + __shfl_xor(l_run, 16);
-    l_tot += __shfl_xor(l_tot, 32);
-    if (n < G) {
-#pragma unroll
-        for (int ct = 0; ct < NCT; ct++)
-#pragma unroll
-            for (int i = 0; i < 4; i++)
-                sm_o[wave][n][16 * ct + 4 * j + i] = o[ct][i];
-        if (j == 0) {
-            sm_m[wave][n] = m_run;
-            sm_l[wave][n] = l_tot;
+    // ---------------- walk the split: this wave takes tiles wave, wave+4, ...
+    // Per tile: wait for its copy, read its operands out of LDS into
+    // registers, start copying the wave's next tile into the same LDS space,
+    // then compute -- the copy of tile i+1 streams during the math of tile i.
+    uint8_t *buf = lds_a + wave * g::BYTES;
+    const int step = TILE * WAVES;
+    int tb = t_begin + TILE * wave;
+    if (tb < t_end) {
+        issue_tile<KT, VT, D>(buf, tb, lane, doff, kc, ks, vc, vs);
+        while (true) {
+            Ops op;
+            read_ops(buf, op);
+            const int tn = tb + step;
+            if (tn < t_end) {
+                asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // LDS reads done before it is refilled
+                issue_tile<KT, VT, D>(buf, tn, lane, doff, kc, ks, vc, vs);
+            }
+            process(op, tb);
+            tb = tn;
+            if (tb >= t_end)
+                break;
         }
     }
+    // every copy into LDS has landed before the buffers are reused below
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
 
+    // ---------------- merge the four waves: scale to the common max, then
+    // accumulate in LDS one wave after the other (deterministic order)
+    float l_tot = l_run + __shfl_xor(l_run, 16);
+    l_tot += __shfl_xor(l_tot, 32);
+    if (j == 0)
+        sm_m[wave][n] = m_run;
+    __syncthreads();
+    float M = sm_m[0][n];
+#pragma unroll
+    for (int w = 1; w < WAVES; w++)
+        M = fmaxf(M, sm_m[w][n]);
+    const float e = (m_run == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(m_run - M);
+    if (j == 0)
+        sm_l[wave][n] = l_tot * e;
+    float *obuf = reinterpret_cast<float *>(lds_a);  // [16][D]
+#pragma unroll
+    for (int w = 0; w < WAVES; w++) {
+        if (wave == w && n < G) {
+#pragma unroll
+            for (int ct = 0; ct < NCT; ct++)
+#pragma unroll
+                for (int i = 0; i < 4; i++) {
+                    const int idx = n * D + 16 * ct + 4 * j + i;
+                    obuf[idx] = (w == 0 ? 0.0f : obuf[idx]) + o[ct][i] * e;
+                }
+        }
+        __syncthreads();
+    }
+
     const int Dp = D + 2;
-    float *ws = a.ws + ((((int64_t)s * a.Hq + (int64_t)h * G) * a.n_splits) + split) * Dp;
-    const int64_t head_stride = (int64_t)a.n_splits * Dp;
-    for (int idx = threadIdx.x; idx < G * D; idx += 256) {
-        const int g = idx / D, c = idx - g * D;
-        float M = sm_m[0][g];
+    const int64_t head_stride = (int64_t)a.n_splits * Dp;  // between query heads
+    float *ws_pair = a.ws + ((int64_t)s * a.Hq + (int64_t)h * G) * head_stride;
+    float *out_pair = a.out + ((int64_t)s * a.Hq + (int64_t)h * G) * D;
+    for (int idx = threadIdx.x; idx < G * D; idx += 64 * WAVES) {
+        const int gg = idx / D, c = idx - gg * D;
+        float Mg = sm_m[0][gg], lsum = 0.0f;
 #pragma unroll
         for (int w = 1; w < WAVES; w++)
-            M = fmaxf(M, sm_m[w][g]);
-        float acc = 0.0f, lsum = 0.0f;
+            Mg = fmaxf(Mg, sm_m[w][gg]);
 #pragma unroll
-        for (int w = 0; w < WAVES; w++) {
-            const float e = (sm_m[w][g] == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(sm_m[w][g] - M);
-            acc += sm_o[w][g][c] * e;
-            lsum += sm_l[w][g] * e;
-        }
-        float *dst = ws + g * head_stride;
-        dst[c] = acc;
-        if (c == 0) {
-            dst[D] = M;
-            dst[D + 1] = lsum;
+        for (int w = 0; w < WAVES; w++)
+            lsum += sm_l[w][gg];
+        const float acc = obuf[idx];
+        if (nsp == 1) {
+            out_pair[idx] = acc / lsum;  // the only split: final output
+        } else {
+            // device-scope stores: written through to the point where every
+            // XCD's loads of the same scope see them, without flushing any L2
+            float *dst = ws_pair + gg * head_stride + (int64_t)split * Dp;
+            st_dev(dst + c, acc);
+            if (c == 0) {
+                st_dev(dst + D, Mg);
+                st_dev(dst + D + 1, lsum);
+            }
         }
     }
-}
+    if (nsp == 1)
+        return;
 
-// out = sum_j O_j 2^(m_j - M) / sum_j l_j 2^(m_j - M) over the splits that
-// hold tokens.  One workgroup per (query head, sequence), one lane per channel.
-template <int D>
-__global__ __launch_bounds__(D) void decode_merge_kernel(const MergeArgs a)
-{
-    const int hq = blockIdx.x, s = blockIdx.y, c = threadIdx.x;
-    const int ctx = a.ctx_len[s];
-    const int nsp = (ctx + a.tps - 1) / a.tps;
-    const int Dp = D + 2;
-    const float *base = a.ws + (((int64_t)s * a.Hq + hq) * a.n_splits) * Dp;
-    float M = -INFINITY;
-    for (int sp = 0; sp < nsp; sp++)
-        M = fmaxf(M, base[sp * Dp + D]);
-    float acc = 0.0f, l = 0.0f;
-    for (int sp = 0; sp < nsp; sp++) {
-        const float e = __builtin_amdgcn_exp2f(base[sp * Dp + D] - M);
-        acc += base[sp * Dp + c] * e;
-        l += base[sp * Dp + D + 1] * e;
+    // ---------------- the last workgroup of this (sequence, kv head) merges
+    // Every wave waits until its partial stores are performed (acknowledged at
+    // device scope), then one lane counts the split as done; the workgroup
+    // that completes the count merges.
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        const unsigned prev = __hip_atomic_fetch_add(a.counters + pair, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        sm_last = (prev == (unsigned)(nsp - 1));
     }
-    a.out[((int64_t)s * a.Hq + hq) * D + c] = acc / l;
+    __syncthreads();
+    if (!sm_last)
+        return;
+
+    // (m_j, l_j) of every (split, head) into LDS (after the [16][D] buffer),
+    // loads issued together; the host keeps nsp * G * 8 bytes within it
+    float *wgt = reinterpret_cast<float *>(lds_a) + 16 * D;  // [nsp][G]: m_j, then 2^(m_j - M)
+    float *lj = wgt + nsp * G;                               // [nsp][G]
+    float *tot = &sm_m[0][0];                                // [16]: 1 / sum_j l_j 2^(m_j - M)
+    for (int idx = threadIdx.x; idx < nsp * G; idx += 64 * WAVES) {
+        const int sp = idx / G, gg = idx - sp * G;
+        const float *pp = ws_pair + gg * head_stride + (int64_t)sp * Dp + D;
+        wgt[idx] = ld_dev(pp);
+        lj[idx] = ld_dev(pp + 1);
+    }
+    __syncthreads();
+    if ((int)threadIdx.x < G) {
+        const int gg = threadIdx.x;
+        float Mx = -INFINITY;
+        for (int sp = 0; sp < nsp; sp++)
+            Mx = fmaxf(Mx, wgt[sp * G + gg]);
+        float l = 0.0f;
+        for (int sp = 0; sp < nsp; sp++) {
+            const float ew = __builtin_amdgcn_exp2f(wgt[sp * G + gg] - Mx);
+            wgt[sp * G + gg] = ew;
+            l += lj[sp * G + gg] * ew;
+        }
+        tot[gg] = 1.0f / l;
+    }
+    __syncthreads();
+    for (int idx = threadIdx.x; idx < G * D; idx += 64 * WAVES) {
+        const int gg = idx / D, c = idx - gg * D;
+        const float *base = ws_pair + gg * head_stride + c;
+        float acc = 0.0f;
+        int sp = 0;
+        for (; sp + 8 <= nsp; sp += 8) {  // eight loads in flight at a time
+            float v[8];
+#pragma unroll
+            for (int u = 0; u < 8; u++)
+                v[u] = ld_dev(base + (int64_t)(sp + u) * Dp);
+#pragma unroll
+            for (int u = 0; u < 8; u++)
+                acc += v[u] * wgt[(sp + u) * G + gg];
+        }
+        for (; sp < nsp; sp++)
+            acc += ld_dev(base + (int64_t)sp * Dp) * wgt[sp * G + gg];
+        out_pair[idx] = acc * tot[gg];
+    }
+    if (threadIdx.x == 0)
+        __hip_atomic_store(a.counters + pair, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 template <int KT, int VT, int D>
 hipError_t launch_dec(const DecodeArgs &a, int n_seqs, hipStream_t st)
 {
     dim3 grid(a.n_splits, a.Hkv, n_seqs);
-    hipLaunchKernelGGL((decode_split_kernel<KT, VT, D>), grid, dim3(256), 0, st, a);
+    hipLaunchKernelGGL((decode_kernel<KT, VT, D>), grid, dim3(64 * WAVES), 0, st, a);
     return hipGetLastError();
 }
 
@@ -377,7 +640,27 @@ hipError_t launch_dec_d(int kt, int vt, const DecodeArgs &a, int n_seqs, hipStre
     return hipErrorInvalidValue;
 }
 
+template <int D>
+int split_cap_d(int kt, int vt, int G)
+{
+    int bytes = 0;
+#define KVQ_C(K, V) \
+    if (kt == K && vt == V) bytes = Geo<K, V, D>::LDS_A;
+    KVQ_C(KVQ_F16, KVQ_F16) KVQ_C(KVQ_F16, KVQ_Q8_0) KVQ_C(KVQ_F16, KVQ_Q4_0)
+    KVQ_C(KVQ_Q8_0, KVQ_F16) KVQ_C(KVQ_Q8_0, KVQ_Q8_0) KVQ_C(KVQ_Q8_0, KVQ_Q4_0)
+    KVQ_C(KVQ_Q4_0, KVQ_F16) KVQ_C(KVQ_Q4_0, KVQ_Q8_0) KVQ_C(KVQ_Q4_0, KVQ_Q4_0)
+#undef KVQ_C
+    // the merge keeps a [16][D] float buffer and (m_j, l_j) per (split, head)
+    return (bytes - 16 * D * 4) / (8 * G);
+}
+
 }  // namespace
+
+int decode_split_cap(int kt, int vt, int D, int G)
+{
+    int cap = D == 64 ? split_cap_d<64>(kt, vt, G) : D == 128 ? split_cap_d<128>(kt, vt, G) : split_cap_d<256>(kt, vt, G);
+    return cap < KVQ_MAX_SPLITS ? cap : KVQ_MAX_SPLITS;
+}
 
 hipError_t launch_decode(int kt, int vt, int D, const DecodeArgs &a, int n_seqs, hipStream_t st)
 {
@@ -387,18 +670,6 @@ hipError_t launch_decode(int kt, int vt, int D, const DecodeArgs &a, int n_seqs,
     case 256: return launch_dec_d<256>(kt, vt, a, n_seqs, st);
     default: return hipErrorInvalidValue;
     }
-}
-
-hipError_t launch_merge(int D, const MergeArgs &a, int n_seqs, hipStream_t st)
-{
-    dim3 grid(a.Hq, n_seqs);
-    switch (D) {
-    case 64: hipLaunchKernelGGL((decode_merge_kernel<64>), grid, dim3(64), 0, st, a); break;
-    case 128: hipLaunchKernelGGL((decode_merge_kernel<128>), grid, dim3(128), 0, st, a); break;
-    case 256: hipLaunchKernelGGL((decode_merge_kernel<256>), grid, dim3(256), 0, st, a); break;
-    default: return hipErrorInvalidValue;
-    }
-    return hipGetLastError();
 }
 
 }  // namespace kvq

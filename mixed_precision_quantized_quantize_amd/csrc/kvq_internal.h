@@ -32,17 +32,12 @@ struct DecodeArgs {
     const uint16_t *ks;
     const uint8_t *vc;
     const uint16_t *vs;
-    const uint16_t *q;  // [S][Hq][D]
-    float *ws;          // [S][Hq][n_splits][D+2]: O (unnormalized), m (log2 units), l
+    const uint16_t *q;    // [S][Hq][D]
+    float *out;           // [S][Hq][D]
+    float *ws;            // [S][Hq][n_splits][D+2]: O (unnormalized), m (base-2 units), l
+    uint32_t *counters;   // [S][Hkv] finished-split counters, zero between calls
     int32_t Hq, Hkv, G, Tc, tps, n_splits;
     float c2;  // scale * log2(e)
-    int32_t ctx_len[KVQ_MAX_SEQS];
-};
-
-struct MergeArgs {
-    const float *ws;
-    float *out;  // [S][Hq][D]
-    int32_t Hq, tps, n_splits;
     int32_t ctx_len[KVQ_MAX_SEQS];
 };
 
@@ -61,7 +56,8 @@ struct PrefillArgs {
 // Launchers return hipSuccess or the launch error.
 hipError_t launch_append(int k_type, int v_type, const AppendArgs &a, int n_quads, hipStream_t st);
 hipError_t launch_decode(int k_type, int v_type, int D, const DecodeArgs &a, int n_seqs, hipStream_t st);
-hipError_t launch_merge(int D, const MergeArgs &a, int n_seqs, hipStream_t st);
+// Most context splits the decode kernel can merge for this configuration.
+int decode_split_cap(int k_type, int v_type, int D, int G);
 hipError_t launch_prefill(int k_type, int v_type, int D, const PrefillArgs &a, hipStream_t st);
 
 }  // namespace kvq

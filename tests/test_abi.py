@@ -138,7 +138,7 @@ def test_decode_rejections(L):
     sh = shape()
     c = make_cache(sh)
     need = kvq.kvq_decode_workspace_bytes(sh)
-    assert need == 2 * 8 * 4 * 66 * 4  # 128 tokens of capacity -> at most 4 splits of one tile
+    assert need == 256 + 2 * 8 * 4 * 66 * 4  # counters, then 128 tokens of capacity -> at most 4 one-tile splits
 
     def call(ctx=(100, 50), ws=FAKE, wsb=need, ns=0, scale=0.125, Q=FAKE, out=FAKE, layer=0):
         return kvq.kvq_attn_decode(c, layer, Q, list(ctx), scale, out, ws, wsb, ns, None)

@@ -124,3 +124,100 @@ def test_llama31_70b_32k_full_size_sampled():
 
 def test_llama3_8b_128k_decode_full_size_sampled():
     workload_layer("llama3_8b_128k_prefill", 0, [3], [0, 17])
+
+
+# ---------------------------------------------------------------- merge and graph replay
+
+def _decode_setup(S=4, Hq=32, Hkv=8, D=128, T=4096, seed=5):
+    import torch
+
+    import mixed_precision_quantized_quantize_amd as kvq
+
+    rng = np.random.default_rng(seed)
+    cache = kvq.KVCache(1, S, Hq, Hkv, D, T, ("q8_0", "q4_0"))
+    K = torch.from_numpy((rng.standard_t(4, (S, T, Hkv, D)) * 3).astype(np.float16)).cuda()
+    V = torch.from_numpy(rng.standard_normal((S, T, Hkv, D)).astype(np.float16)).cuda()
+    Q = torch.from_numpy(rng.standard_normal((S, Hq, D)).astype(np.float16)).cuda()
+    cache.append(0, K, V, [0] * S)
+    return cache, K, V, Q
+
+
+def test_decode_fused_merge_is_repeatable():
+    """The last workgroup of each (sequence, kv head) merges the split
+    partials; every call must see complete partials (results bitwise equal
+    across calls, including after calls with other split counts) and must
+    leave the counters at zero."""
+    import torch
+
+    print("decode fused-merge repeatability", flush=True)
+    cache, K, V, Q = _decode_setup()
+    ctx = [4096, 4000, 3001, 77]
+    ref = {ns: cache.decode(0, Q, ctx, 0.0883883, n_splits=ns).clone() for ns in (32, 7, 128)}
+    for it in range(30):
+        for ns in (32, 7, 128):
+            out = cache.decode(0, Q, ctx, 0.0883883, n_splits=ns)
+            assert torch.equal(out, ref[ns]), f"call {it} splits {ns} differs"
+    torch.cuda.synchronize()
+    counters = cache.workspace()[:4 * 8].view(torch.int32)
+    assert int(counters.abs().sum()) == 0
+
+
+def test_decode_graph_replay_matches_eager():
+    """append + decode captured in a HIP graph: every replay (with eager work
+    and synchronizations between replays) equals the eager result."""
+    import torch
+
+    print("decode graph replay", flush=True)
+    cache, K, V, Q = _decode_setup(seed=6)
+    ctx = [4096] * 4
+    Kn, Vn = K[:, -1:].contiguous(), V[:, -1:].contiguous()
+    eager = cache.decode(0, Q, ctx, 0.0883883).clone()
+    out = torch.empty_like(eager)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        cache.append(0, Kn, Vn, [4095] * 4)
+        cache.decode(0, Q, ctx, 0.0883883, out=out)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        cache.append(0, Kn, Vn, [4095] * 4)
+        cache.decode(0, Q, ctx, 0.0883883, out=out)
+    for i in range(5):
+        out.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, eager), f"replay {i}"
+        junk = cache.decode(0, Q, [100] * 4, 0.0883883, n_splits=3)  # eager work between replays
+        torch.cuda.synchronize()
+        del junk
+
+
+@pytest.mark.parametrize("kt,vt", [("q8_0", "q4_0"), ("f16", "f16"), ("q4_0", "q8_0")])
+def test_decode_ignores_garbage_past_context(kt, vt):
+    """Cache memory past ctx_len may hold any bits (here NaN patterns in codes
+    and scales): the ragged tail tile must not let them into the output."""
+    import torch
+
+    import mixed_precision_quantized_quantize_amd as kvq
+
+    print(f"decode garbage past context {kt}/{vt}", flush=True)
+    rng = np.random.default_rng(9)
+    S, Hq, Hkv, D, T = 2, 16, 2, 128, 256
+    cache = kvq.KVCache(1, S, Hq, Hkv, D, T, (kt, vt))
+    for b in cache.buffers[0]:
+        if b is not None:
+            b.fill_(-1)  # all bits set: binary16 NaN everywhere
+    orc = oracle.OracleLayer(kt, vt, S, Hq, Hkv, D, T)
+    ctx = [203, 77]
+    K = torch.from_numpy((rng.standard_normal((S, 203, Hkv, D)) * 2).astype(np.float16)).cuda()
+    V = torch.from_numpy(rng.standard_normal((S, 203, Hkv, D)).astype(np.float16)).cuda()
+    cache.append(0, K, V, [0, 0])
+    orc.append(bits(K), bits(V), np.zeros(S, np.int32))
+    Q = torch.from_numpy(rng.standard_normal((S, Hq, D)).astype(np.float16)).cuda()
+    ref = orc.attn_decode(bits(Q), np.array(ctx, np.int32), 0.0883883)
+    for ns in (0, 1, 3):
+        out = cache.decode(0, Q, ctx, 0.0883883, n_splits=ns)
+        torch.cuda.synchronize()
+        assert_attn_close(out.cpu().numpy(), ref, f"garbage {kt}/{vt} splits={ns}")

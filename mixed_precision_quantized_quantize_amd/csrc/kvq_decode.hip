@@ -154,18 +154,24 @@ __device__ inline int vswz(int g)
 }
 
 typedef __attribute__((address_space(3))) void lds_void_t;
-typedef __attribute__((address_space(1))) void gbl_void_t;
 
-// 64 lanes x `size` bytes from per-lane global addresses into LDS at
-// dst + lane * size (dst wave-uniform).
+// Buffer resource over one plane range [base, base + bytes): word 3 selects
+// raw 32-bit data; offsets past `bytes` read as zero instead of faulting.
+__device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void *base, int64_t bytes)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+// 64 lanes x `size` bytes (lane l from voffset_l + soffset) into LDS at
+// dst + l * size; dst and soffset are wave-uniform.
 template <int SIZE>
-__device__ inline void dma(const void *src, void *dst)
+__device__ inline void dma(__amdgpu_buffer_rsrc_t r, int voffset, int soffset, void *dst)
 {
     static_assert(SIZE == 16 || SIZE == 4, "lane placement checked for 4- and 16-byte copies only");
     if constexpr (SIZE == 16)
-        __builtin_amdgcn_global_load_lds((gbl_void_t *)src, (lds_void_t *)dst, 16, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t *)dst, 16, voffset, soffset, 0, 0);
     else
-        __builtin_amdgcn_global_load_lds((gbl_void_t *)src, (lds_void_t *)dst, 4, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t *)dst, 4, voffset, soffset, 0, 0);
 }
 
 // Per-lane constant byte offsets of the tile copy (source side, relative to
@@ -190,39 +196,43 @@ struct DmaOffsets {
     }
 };
 
+// Resources over this (sequence, kv head)'s K and V ranges.
+struct PairRsrc {
+    __amdgpu_buffer_rsrc_t kc, ks, vc, vs;
+};
+
 template <int KT, int VT, int D>
-__device__ inline void issue_tile(uint8_t *buf, int tb, int lane, const DmaOffsets<KT, VT, D> &off, const uint8_t *kc,
-                                  const uint16_t *ks, const uint8_t *vc, const uint16_t *vs)
+__device__ inline void issue_tile(uint8_t *buf, int tb, int lane, const DmaOffsets<KT, VT, D> &off, const PairRsrc &r)
 {
     using g = Geo<KT, VT, D>;
-    const uint8_t *ksrc = kc + (int64_t)tb * g::RK;
+    const int kbase = tb * g::RK;
 #pragma unroll
     for (int i = 0; i < g::K_BYTES / 1024; i++)
-        dma<16>(ksrc + off.k[i], buf + g::K_OFF + 1024 * i);
+        dma<16>(r.kc, off.k[i], kbase, buf + g::K_OFF + 1024 * i);
     if (KT != KVQ_F16) {
-        const uint8_t *src = reinterpret_cast<const uint8_t *>(ks + (int64_t)tb * g::NB);
+        const int sbase = tb * g::NB * 2;
         if (g::KS_BYTES == 128) {
             if (lane < 32)  // 4 bytes on half the lanes (lane l lands at +4 l)
-                dma<4>(src + 4 * lane, buf + g::KS_OFF);
+                dma<4>(r.ks, 4 * lane, sbase, buf + g::KS_OFF);
         } else {
 #pragma unroll
             for (int i = 0; i < g::KS_BYTES / 256; i++)
-                dma<4>(src + 256 * i + 4 * lane, buf + g::KS_OFF + 256 * i);
+                dma<4>(r.ks, 256 * i + 4 * lane, sbase, buf + g::KS_OFF + 256 * i);
         }
     }
-    const uint8_t *vsrc = vc + (int64_t)(tb >> 3) * 8 * g::RV;
+    const int vbase = (tb >> 3) * 8 * g::RV;
 #pragma unroll
     for (int i = 0; i < g::V_BYTES / 1024; i++)
-        dma<16>(vsrc + off.v[i], buf + g::V_OFF + 1024 * i);
+        dma<16>(r.vc, off.v[i], vbase, buf + g::V_OFF + 1024 * i);
     if (VT != KVQ_F16) {
-        const uint8_t *src = reinterpret_cast<const uint8_t *>(vs + (int64_t)(tb >> 3) * g::NB * 8);
+        const int sbase = (tb >> 3) * g::NB * 16;
         if (g::VS_BYTES == 128) {
-            if (lane < 32)  // 4 bytes on half the lanes (lane l lands at +4 l)
-                dma<4>(src + 4 * lane, buf + g::VS_OFF);
+            if (lane < 32)
+                dma<4>(r.vs, 4 * lane, sbase, buf + g::VS_OFF);
         } else {
 #pragma unroll
             for (int i = 0; i < g::VS_BYTES / 256; i++)
-                dma<4>(src + 256 * i + 4 * lane, buf + g::VS_OFF + 256 * i);
+                dma<4>(r.vs, 256 * i + 4 * lane, sbase, buf + g::VS_OFF + 256 * i);
         }
     }
 }
@@ -239,7 +249,7 @@ __device__ inline float half_at(const uint32_t *w, int idx)
 }
 
 template <int KT, int VT, int D>
-__global__ __launch_bounds__(64 * WAVES) void decode_kernel(const DecodeArgs a)
+__global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(D <= 128 ? 3 : 1))) void decode_kernel(const DecodeArgs a)
 {
     using g = Geo<KT, VT, D>;
     constexpr int NB = g::NB, NCT = g::NCT;
@@ -249,7 +259,8 @@ __global__ __launch_bounds__(64 * WAVES) void decode_kernel(const DecodeArgs a)
     __shared__ float sm_l[WAVES][16];
     __shared__ int sm_last;
 
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: scalar addressing
     const int n = lane & 15, j = lane >> 4;
     const int split = blockIdx.x, h = blockIdx.y, s = blockIdx.z;
     const int ctx = a.ctx_len[s];
@@ -274,10 +285,13 @@ __global__ __launch_bounds__(64 * WAVES) void decode_kernel(const DecodeArgs a)
                 qb[b][r] = (n < G) ? qrow[32 * b + qk_chan<KT>(j, r)] : (_Float16)0.0f;
     }
 
-    const uint8_t *kc = a.kc + pair * Tc * g::RK;
-    const uint16_t *ks = a.ks + pair * Tc * NB;
-    const uint8_t *vc = a.vc + pair * (Tc / 8) * 8 * g::RV;
-    const uint16_t *vs = a.vs + pair * (Tc / 8) * NB * 8;
+    PairRsrc rs;
+    rs.kc = make_rsrc(a.kc + pair * Tc * g::RK, Tc * g::RK);
+    rs.vc = make_rsrc(a.vc + pair * Tc * g::RV, Tc * g::RV);
+    if (KT != KVQ_F16)
+        rs.ks = make_rsrc(a.ks + pair * Tc * NB, Tc * NB * 2);
+    if (VT != KVQ_F16)
+        rs.vs = make_rsrc(a.vs + pair * Tc * NB, Tc * NB * 2);
     const float c2 = a.c2;
 
     DmaOffsets<KT, VT, D> doff;
@@ -306,6 +320,7 @@ __global__ __launch_bounds__(64 * WAVES) void decode_kernel(const DecodeArgs a)
         v_rd[i] = g::V_OFF + (j * g::CPG + (c ^ vswz<VT, g::CPG>(j))) * 16 + within;
     }
 
+    const int bp16 = (lane ^ 16) << 2, bp32 = (lane ^ 32) << 2;  // ds_bpermute byte addresses
     float m_run = -INFINITY;  // running max (base 2) of head n, equal in the 4 lane groups
     float l_run = 0.0f;       // this lane's share of the running sum
     floatx4 o[NCT];
@@ -405,8 +420,8 @@ __global__ __launch_bounds__(64 * WAVES) void decode_kernel(const DecodeArgs a)
                 }
         }
         float mt = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])), fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
-        mt = fmaxf(mt, __shfl_xor(mt, 16));
-        mt = fmaxf(mt, __shfl_xor(mt, 32));
+        mt = fmaxf(mt, __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(bp16, __builtin_bit_cast(int, mt))));
+        mt = fmaxf(mt, __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(bp32, __builtin_bit_cast(int, mt))));
         if (__any(mt > m_run)) {
             const float m_new = fmaxf(m_run, mt);
             const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);  // 0 on the first tile
@@ -480,14 +495,14 @@ __global__ __launch_bounds__(64 * WAVES) void decode_kernel(const DecodeArgs a)
     const int step = TILE * WAVES;
     int tb = t_begin + TILE * wave;
     if (tb < t_end) {
-        issue_tile<KT, VT, D>(buf, tb, lane, doff, kc, ks, vc, vs);
+        issue_tile<KT, VT, D>(buf, tb, lane, doff, rs);
         while (true) {
             Ops op;
             read_ops(buf, op);
             const int tn = tb + step;
             if (tn < t_end) {
                 asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // LDS reads done before it is refilled
-                issue_tile<KT, VT, D>(buf, tn, lane, doff, kc, ks, vc, vs);
+                issue_tile<KT, VT, D>(buf, tn, lane, doff, rs);
             }
             process(op, tb);
             tb = tn;

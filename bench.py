@@ -44,6 +44,9 @@ def parse():
     p.add_argument("--graph", action="store_true", help="replay each step from a captured HIP graph")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=10.0)
+    p.add_argument("--calib-copy", action="store_true",
+                   help="after timing, run three plain 1 GiB device-to-device copies (a reference for "
+                        "hardware byte counters)")
     return p.parse_args()
 
 
@@ -54,17 +57,22 @@ def kv_bytes_per_layer(w, kt, vt):
     return sum(kvq.kvq_plane_bytes(sh, kt)) + sum(kvq.kvq_plane_bytes(sh, vt))
 
 
-def traffic_from_profile(src_hash):
-    """Measured HBM bytes per decode launch from the committed counter summary,
-    or None when the decode kernel source changed since it was taken."""
-    path = os.path.join(ROOT, "profiles", "decode_traffic.json")
+def traffic_from_profile(src_hash, workload):
+    """Measured HBM bytes per decode launch from the committed counter summary
+    (FETCH_SIZE and WRITE_SIZE scaled by a plain copy of known size), or None
+    when the decode kernel source changed since the counters were taken."""
+    path = os.path.join(ROOT, "profiles", f"decode_kernel_{workload}.txt")
+    rec = {}
     try:
-        rec = json.load(open(path))
-    except (OSError, ValueError):
+        for line in open(path):
+            if ":" in line and not line.startswith("#"):
+                k, v = line.split(":", 1)
+                rec[k.strip()] = v.split("#")[0].strip()
+    except OSError:
         return None
-    if rec.get("kernel_source_sha256") != src_hash:
+    if rec.get("decode_kernel_source_sha256") != src_hash or "hbm_bytes_per_launch" not in rec:
         return None
-    return rec.get("bytes_per_launch")
+    return int(rec["hbm_bytes_per_launch"])
 
 
 def cpu_baseline(w, kt, vt, layer_kv, q_bits, seconds):
@@ -214,7 +222,7 @@ def main():
     value = kv_step / (ms_step * 1e-3) / 1e9
     achieved = alg_bytes_launch / (dec_avg_ms * 1e-3) / 1e9
     src = open(os.path.join(ROOT, "mixed_precision_quantized_quantize_amd", "csrc", "kvq_decode.hip"), "rb").read()
-    traffic = traffic_from_profile(hashlib.sha256(src).hexdigest())
+    traffic = traffic_from_profile(hashlib.sha256(src).hexdigest(), w.name)
 
     result = {
         "metric": "decode-attn KV GB/s (% HBM peak) + tok/s, K8V4 Llama-3-8B shape, 32K ctx",
@@ -238,7 +246,7 @@ def main():
         "kv_bytes_per_step": kv_step,
         "roofline": {
             "bound": "hbm",
-            "kernel": "kvq_attn_decode (split-K pass + merge), one layer",
+            "kernel": "decode_kernel (split-K flash decode with the merge folded in), one layer",
             "achieved": round(achieved, 2),
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",
@@ -251,6 +259,14 @@ def main():
     }
     log(f"step {ms_step:.3f} ms, {value:.1f} GB/s ({100 * value / HBM_PEAK_GBPS:.1f}% of peak), "
         f"decode call {dec_avg_ms * 1e3:.1f} us -> {achieved:.1f} GB/s")
+
+    if args.calib_copy:
+        x = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+        y = torch.empty_like(x)
+        for _ in range(3):
+            y.copy_(x)
+        torch.cuda.synchronize()
+        del x, y
 
     if not args.no_cpu_baseline and layer0 is not None:
         del cache

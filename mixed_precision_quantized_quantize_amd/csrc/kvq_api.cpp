@@ -272,6 +272,8 @@ int kvq_attn_prefill_chunk(const kvq_cache *cache, int32_t layer, const void *Q,
     a.Tc = (int32_t)capacity(sh.max_ctx);
     a.n_tok = n_tok;
     a.n_seqs = sh.n_seqs;
+    while ((1 << a.gp_log2) < a.G)
+        a.gp_log2++;
     a.c2 = (float)((double)scale * 1.4426950408889634);
     memcpy(a.q_pos0, q_pos0, sizeof(int32_t) * sh.n_seqs);
     hipError_t e = launch_prefill(kp.type, vp.type, sh.head_dim, a, (hipStream_t)stream);

@@ -1,0 +1,242 @@
+// kvq_device.h -- device-side building blocks shared by the decode and the
+// prefill kernels: binary16 operand unpacking of the block formats, the
+// 32-token tile geometry in LDS with its bank swizzles, and the
+// direct-to-LDS tile copy.  Internal; not part of the C ABI.
+#pragma once
+
+#include "kvq_internal.h"
+
+namespace kvq {
+namespace dev {
+
+typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef _Float16 half2 __attribute__((ext_vector_type(2)));
+typedef float float2v __attribute__((ext_vector_type(2)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int WAVES = 4;
+constexpr int TILE = 32;
+
+__device__ inline floatx4 mfma(half8 a, half8 b, floatx4 c)
+{
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+
+__device__ inline half2 bits_h2(uint32_t w) { return __builtin_bit_cast(half2, w); }
+__device__ inline uint32_t h2_bits(half2 h) { return __builtin_bit_cast(uint32_t, h); }
+
+__device__ inline half8 pack4(uint32_t a, uint32_t b, uint32_t c, uint32_t d)
+{
+    u32x4 v = {a, b, c, d};
+    return __builtin_bit_cast(half8, v);
+}
+
+// (y & mask) | (c & ~mask) in one instruction.
+__device__ inline uint32_t bfi(uint32_t mask, uint32_t y, uint32_t c)
+{
+    uint32_t r;
+    asm("v_bfi_b32 %0, %1, %2, %3" : "=v"(r) : "v"(mask), "v"(y), "v"(c));
+    return r;
+}
+
+// 8 int8 codes -> 8 exact binary16 values: bias to unsigned, place each byte
+// under the exponent pattern 0x64 (binary16 1024 + u), subtract 1152.
+__device__ inline half8 deq_q8(uint32_t w0, uint32_t w1)
+{
+    const uint32_t x0 = w0 ^ 0x80808080u, x1 = w1 ^ 0x80808080u;
+    const half2 off = {(_Float16)1152.0f, (_Float16)1152.0f};
+    uint32_t r0 = h2_bits(bits_h2(__builtin_amdgcn_perm(0x64646464u, x0, 0x04010400u)) - off);
+    uint32_t r1 = h2_bits(bits_h2(__builtin_amdgcn_perm(0x64646464u, x0, 0x04030402u)) - off);
+    uint32_t r2 = h2_bits(bits_h2(__builtin_amdgcn_perm(0x64646464u, x1, 0x04010400u)) - off);
+    uint32_t r3 = h2_bits(bits_h2(__builtin_amdgcn_perm(0x64646464u, x1, 0x04030402u)) - off);
+    return pack4(r0, r1, r2, r3);
+}
+
+// Two q4_0 code bytes in the low bytes of each 16-bit half of y -> binary16
+// pairs (c - 8) of their low nibbles and of their high nibbles, exact:
+// low:  binary16 1024 + c       minus 1032
+// high: binary16 1024 + 16 c    times 1/16 minus 72
+__device__ inline void deq_q4_pair(uint32_t y, uint32_t &lo, uint32_t &hi)
+{
+    const uint32_t e = 0x64006400u;
+    const half2 k1032 = {(_Float16)1032.0f, (_Float16)1032.0f};
+    const half2 k16 = {(_Float16)0.0625f, (_Float16)0.0625f};
+    const half2 k72 = {(_Float16)-72.0f, (_Float16)-72.0f};
+    lo = h2_bits(bits_h2(bfi(0x000F000Fu, y, e)) - k1032);
+    hi = h2_bits(__builtin_elementwise_fma(bits_h2(bfi(0x00F000F0u, y, e)), k16, k72));
+}
+
+// K codes of one block for one lane -> A operand (8 channels of one token).
+template <int KT>
+__device__ inline half8 k_operand(const uint32_t *w)
+{
+    if (KT == KVQ_F16)
+        return pack4(w[0], w[1], w[2], w[3]);
+    if (KT == KVQ_Q8_0)
+        return deq_q8(w[0], w[1]);
+    // q4_0: bytes 4j..4j+3 hold elements 4j+k (low) and 16+4j+k (high)
+    uint32_t l01, h01, l23, h23;
+    deq_q4_pair(__builtin_amdgcn_perm(w[0], w[0], 0x0C010C00u), l01, h01);
+    deq_q4_pair(__builtin_amdgcn_perm(w[0], w[0], 0x0C030C02u), l23, h23);
+    return pack4(l01, l23, h01, h23);
+}
+
+// Channel (within a 32-block) carried by k-slot r of lane group j in the Q.K
+// product; it must match how k_operand unpacks that lane's codes.
+template <int KT>
+__device__ inline int qk_chan(int j, int r)
+{
+    if (KT == KVQ_Q4_0)
+        return (r < 4) ? 4 * j + r : 16 + 4 * j + (r - 4);
+    return 8 * j + r;
+}
+
+// ------------------------------------------------------------------ tile geometry
+// One wave stages one 32-token tile in LDS: K codes (token-major rows), K
+// scales, V codes (8-token groups), V scales -- four contiguous ranges of the
+// planes, copied with direct-to-LDS 16-byte loads (every instruction reads one
+// contiguous kilobyte).  16-byte chunks are XOR-swizzled within a K row / V
+// group so that the MFMA-operand reads below hit distinct LDS banks.
+template <int KT, int VT, int D>
+struct Geo {
+    static constexpr int NB = D / 32, NCT = D / 16;
+    static constexpr int RK = (KT == KVQ_F16) ? 2 * D : (KT == KVQ_Q8_0) ? D : D / 2;  // K row code bytes
+    static constexpr int RV = (VT == KVQ_F16) ? 2 * D : (VT == KVQ_Q8_0) ? D : D / 2;  // V row code bytes
+    static constexpr int K_BYTES = TILE * RK;
+    static constexpr int KS_BYTES = (KT == KVQ_F16) ? 0 : TILE * NB * 2;
+    static constexpr int V_BYTES = TILE * RV;
+    static constexpr int VS_BYTES = (VT == KVQ_F16) ? 0 : TILE * NB * 2;
+    static constexpr int K_OFF = 0, KS_OFF = K_BYTES, V_OFF = KS_OFF + KS_BYTES, VS_OFF = V_OFF + V_BYTES;
+    static constexpr int BYTES = VS_OFF + VS_BYTES;  // one wave's tile
+    static constexpr int CPR = RK / 16;              // 16-byte chunks per K row
+    static constexpr int CPG = 8 * RV / 16;          // 16-byte chunks per 8-token V group
+    static constexpr int LDS_A = WAVES * BYTES;
+};
+
+// XOR swizzle of the chunk index within K row r (bank-conflict-free reads of
+// the Q.K operand for every type and head_dim; chosen with a bank model).
+template <int CPR>
+__device__ inline int kswz(int r)
+{
+    if (CPR <= 4)
+        return (r ^ (r >> 3)) & (CPR - 1);
+    if (CPR == 8)
+        return ((r >> 1) ^ (r >> 2)) & 7;
+    return (r ^ (r >> 1)) & (CPR - 1);
+}
+template <int VT, int CPG>
+__device__ inline int vswz(int g)
+{
+    return (VT == KVQ_F16) ? 0 : (8 * g) & (CPG - 1);
+}
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+// Buffer resource over one plane range [base, base + bytes): word 3 selects
+// raw 32-bit data; offsets past `bytes` read as zero instead of faulting.
+__device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void *base, int64_t bytes)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+// 64 lanes x `size` bytes (lane l from voffset_l + soffset) into LDS at
+// dst + l * size; dst and soffset are wave-uniform.
+template <int SIZE>
+__device__ inline void dma(__amdgpu_buffer_rsrc_t r, int voffset, int soffset, void *dst)
+{
+    static_assert(SIZE == 16 || SIZE == 4, "lane placement checked for 4- and 16-byte copies only");
+    if constexpr (SIZE == 16)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t *)dst, 16, voffset, soffset, 0, 0);
+    else
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t *)dst, 4, voffset, soffset, 0, 0);
+}
+
+// Per-lane constant byte offsets of the tile copy (source side, relative to
+// the tile's first K row / first V group).
+template <int KT, int VT, int D>
+struct DmaOffsets {
+    using g = Geo<KT, VT, D>;
+    int k[g::K_BYTES / 1024];
+    int v[g::V_BYTES / 1024];
+    __device__ void init(int lane)
+    {
+#pragma unroll
+        for (int i = 0; i < g::K_BYTES / 1024; i++) {
+            const int sl = 64 * i + lane, r = sl / g::CPR, c = (sl % g::CPR) ^ kswz<g::CPR>(r);
+            k[i] = r * g::RK + 16 * c;
+        }
+#pragma unroll
+        for (int i = 0; i < g::V_BYTES / 1024; i++) {
+            const int sl = 64 * i + lane, grp = sl / g::CPG, c = (sl % g::CPG) ^ vswz<VT, g::CPG>(grp);
+            v[i] = grp * (8 * g::RV) + 16 * c;
+        }
+    }
+};
+
+// Resources over this (sequence, kv head)'s K and V ranges.
+struct PairRsrc {
+    __amdgpu_buffer_rsrc_t kc, ks, vc, vs;
+};
+
+// Copies one tile; with nparts > 1 the copy instructions are dealt out
+// round-robin and this caller issues only those of index % nparts == part
+// (waves of one workgroup sharing a tile).
+template <int KT, int VT, int D>
+__device__ inline void issue_tile(uint8_t *buf, int tb, int lane, const DmaOffsets<KT, VT, D> &off, const PairRsrc &r,
+                                  int part = 0, int nparts = 1)
+{
+    using g = Geo<KT, VT, D>;
+    constexpr int NK = g::K_BYTES / 1024, NV = g::V_BYTES / 1024;
+    constexpr int NKS = (KT == KVQ_F16) ? 0 : (g::KS_BYTES == 128 ? 1 : g::KS_BYTES / 256);
+    const int kbase = tb * g::RK;
+#pragma unroll
+    for (int i = 0; i < NK; i++)
+        if (i % nparts == part)
+            dma<16>(r.kc, off.k[i], kbase, buf + g::K_OFF + 1024 * i);
+    if (KT != KVQ_F16) {
+        const int sbase = tb * g::NB * 2;
+        if (g::KS_BYTES == 128) {
+            if (NK % nparts == part && lane < 32)  // 4 bytes on half the lanes (lane l lands at +4 l)
+                dma<4>(r.ks, 4 * lane, sbase, buf + g::KS_OFF);
+        } else {
+#pragma unroll
+            for (int i = 0; i < g::KS_BYTES / 256; i++)
+                if ((NK + i) % nparts == part)
+                    dma<4>(r.ks, 256 * i + 4 * lane, sbase, buf + g::KS_OFF + 256 * i);
+        }
+    }
+    const int vbase = (tb >> 3) * 8 * g::RV;
+#pragma unroll
+    for (int i = 0; i < NV; i++)
+        if ((NK + NKS + i) % nparts == part)
+            dma<16>(r.vc, off.v[i], vbase, buf + g::V_OFF + 1024 * i);
+    if (VT != KVQ_F16) {
+        const int sbase = (tb >> 3) * g::NB * 16;
+        if (g::VS_BYTES == 128) {
+            if ((NK + NKS + NV) % nparts == part && lane < 32)
+                dma<4>(r.vs, 4 * lane, sbase, buf + g::VS_OFF);
+        } else {
+#pragma unroll
+            for (int i = 0; i < g::VS_BYTES / 256; i++)
+                if ((NK + NKS + NV + i) % nparts == part)
+                    dma<4>(r.vs, 256 * i + 4 * lane, sbase, buf + g::VS_OFF + 256 * i);
+        }
+    }
+}
+
+// Split partials cross workgroups (and XCDs): relaxed atomics of device
+// scope, coherent between all XCDs, with no L2 writeback or invalidation.
+__device__ inline void st_dev(float *p, float v) { __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
+__device__ inline float ld_dev(const float *p) { return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
+
+__device__ inline float half_at(const uint32_t *w, int idx)
+{
+    uint32_t v = w[idx >> 1];
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)((idx & 1) ? (v >> 16) : (v & 0xffffu)));
+}
+
+
+}  // namespace dev
+}  // namespace kvq

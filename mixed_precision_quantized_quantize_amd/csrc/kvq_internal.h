@@ -49,6 +49,7 @@ struct PrefillArgs {
     const uint16_t *q;  // [S][n_tok][Hq][D]
     float *out;         // [S][n_tok][Hq][D]
     int32_t Hq, Hkv, G, Tc, n_tok, n_seqs;
+    int32_t gp_log2;  // rows of one query token: the group padded to 2^gp_log2
     float c2;
     int32_t q_pos0[KVQ_MAX_SEQS];
 };

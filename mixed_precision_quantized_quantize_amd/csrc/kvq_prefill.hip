@@ -1,25 +1,36 @@
 // kvq_prefill.hip -- causal chunked prefill over the quantized cache.
 //
-// A chunk of n_tok new queries per sequence (the micro-batch of the llama.cpp
-// guide's "Batch-Groessen-Abstimmung"), already appended at positions
-// p0 .. p0+n_tok-1, attends causally: query i sees cache positions
-// 0 .. p0+i.  The chunk is the micro-batch of the llama.cpp guide's
-// batch-size section ("Batch-Groessen-Abstimmung", the -ub flag).  Flash
-// attention as in that guide's "Flash Attention" section: tiled, online
-// softmax, exact.
+// A chunk of n_tok new queries per sequence, already appended at positions
+// p0 .. p0+n_tok-1, attends causally: query i sees cache positions 0 .. p0+i.
+// The chunk is the micro-batch of the llama.cpp guide's batch-size section
+// ("Batch-Groessen-Abstimmung", the -ub flag).  Flash attention as in that
+// guide's "Flash Attention" section: tiled, online softmax, exact.
 //
 // Rows are (query token, head of the GQA group) pairs, so all heads that share
-// a kv head share every K/V tile.  A workgroup owns 128 rows (4 waves x 32)
-// of one (sequence, kv head) and walks the keys in 32-token tiles; each tile
-// is copied once into LDS (the four waves deal out the copy instructions) and
-// read by all four waves.  Per wave and tile, both contractions run on
-// v_mfma_f32_16x16x32_f16 exactly as in decode:
-//   S^T[key][row]  = K[key][c] . Q^T[c][row]   (raw codes, K scale per
-//                                                 (key, block) after the MFMA)
-//   O^T[c][row]   += V^T[c][key] . P'[key][row] (P' = binary16(p) * V scale)
-// with the K and V operands unpacked once and shared by the wave's row
-// blocks.  Only tiles that reach past a row's own position are masked.
+// a kv head share every K/V tile.  A workgroup owns 4 waves x 16*RB rows of
+// one (sequence, kv head) and walks the keys in 32-token tiles; each tile is
+// copied once into LDS (the four waves deal out the copy instructions) and
+// read by all four.  Per wave and tile both contractions run on
+// v_mfma_f32_16x16x32_f16, and every operand built from the tile is shared by
+// the wave's RB row blocks:
+//   S^T[key][row]  = K[key][c] . Q^T[c][row]
+//       A quantized K block enters as two binary16 operands hi + lo with
+//       hi = fl16(code * d), lo = fl16(code * d - hi) (one fused multiply-add),
+//       which together hold code * d exactly (the product has at most 8 + 11
+//       significant bits), so the scale costs a second MFMA instead of a
+//       vector multiply-add per (score, block);
+//   O^T[c][row]   += V^T[c][key] . P[key][row]
+//       with the V operand already multiplied by its block scale (binary16)
+//       and P = binary16(p); one more MFMA against an all-ones operand sums
+//       the same binary16 p into the softmax denominator.
+// Online softmax in base 2: p = 2^(s*c2 - m), the subtraction folded into one
+// fused multiply-add (a negative scale is moved onto Q, exactly).  Only tiles
+// that reach past a row's own position are masked.
+#include <type_traits>
+
 #include "kvq_device.h"
+
+#pragma clang fp contract(off)
 
 namespace kvq {
 namespace {
@@ -28,7 +39,32 @@ using namespace dev;
 
 constexpr int PW = 4;  // waves per workgroup
 
-template <int D> struct Rows { static constexpr int RB = (D == 256) ? 1 : 2; };  // 16-row blocks per wave
+// 16-row blocks per wave.  This file is compiled with the MFMA accumulators in
+// VGPRs (-amdgpu-mfma-vgpr-form): the online-softmax rescale touches them with
+// vector instructions, and with AGPR accumulators the compiler copied them
+// between the two register files on every tile.
+template <int D> struct Rows { static constexpr int RB = (D == 256) ? 1 : 4; };
+
+// max over the four lanes n, n+16, n+32, n+48 (the lane groups of one row)
+__device__ inline float max_lane_groups(float v)
+{
+    const uint32_t u = __builtin_bit_cast(uint32_t, v);
+    const auto a = __builtin_amdgcn_permlane32_swap(u, u, false, false);  // {lanes 0-31 twice}, {32-63 twice}
+    const float m = __builtin_elementwise_maximum(__builtin_bit_cast(float, (uint32_t)a[0]), __builtin_bit_cast(float, (uint32_t)a[1]));
+    const uint32_t w = __builtin_bit_cast(uint32_t, m);
+    const auto b = __builtin_amdgcn_permlane16_swap(w, w, false, false);  // rows {0,0,2,2}, {1,1,3,3}
+    return __builtin_elementwise_maximum(__builtin_bit_cast(float, (uint32_t)b[0]), __builtin_bit_cast(float, (uint32_t)b[1]));
+}
+
+// NaN-propagating maximum (v_maximum3_f32): fmaxf would first canonicalize
+// every MFMA result with an extra v_max_f32.  Scores are finite here, or
+// -inf where masked (a masked key's garbage score is replaced before).
+__device__ inline float max3(float a, float b, float c)
+{
+    return __builtin_elementwise_maximum(__builtin_elementwise_maximum(a, b), c);
+}
+
+__device__ inline half8 splat8(uint32_t pair) { return pack4(pair, pair, pair, pair); }
 
 template <int KT, int VT, int D>
 __global__ __launch_bounds__(64 * PW) void prefill_kernel(const PrefillArgs a)
@@ -38,6 +74,7 @@ __global__ __launch_bounds__(64 * PW) void prefill_kernel(const PrefillArgs a)
     constexpr int RB = Rows<D>::RB;
     constexpr int ROWS_G = 16 * RB * PW;
     constexpr int VL = (VT == KVQ_Q4_0) ? NB : NCT;
+    constexpr bool KQ = KT != KVQ_F16, VQ = VT != KVQ_F16;
 
     __shared__ __attribute__((aligned(16))) uint8_t lds[2][g::BYTES];
 
@@ -56,11 +93,14 @@ __global__ __launch_bounds__(64 * PW) void prefill_kernel(const PrefillArgs a)
     const int G = a.G, gsh = a.gp_log2;
     const int n_tok = a.n_tok, p0 = a.q_pos0[s];
     const int row0 = qblk * ROWS_G;
-    const int tok_first = row0 >> gsh;
     const int tok_last = min(n_tok - 1, (row0 + ROWS_G - 1) >> gsh);
     const int key_end = p0 + tok_last + 1;  // keys [0, key_end) are visible to some row
+    const int wrow0 = row0 + wave * 16 * RB;
+    const int wave_first = p0 + min(wrow0 >> gsh, n_tok - 1);  // smallest last-visible key of the wave
     const int64_t pair = (int64_t)s * a.Hkv + h;
     const int64_t Tc = a.Tc;
+    const float c2a = fabsf(a.c2);
+    const bool neg = a.c2 < 0.0f;
 
     // this lane's row in each row block: (token, head g) = (gr >> gsh, gr & (Gp-1))
     int tok[RB], lim[RB];
@@ -68,7 +108,7 @@ __global__ __launch_bounds__(64 * PW) void prefill_kernel(const PrefillArgs a)
     half8 qb[RB][NB];
 #pragma unroll
     for (int rb = 0; rb < RB; rb++) {
-        const int gr = row0 + wave * 16 * RB + rb * 16 + n;
+        const int gr = wrow0 + rb * 16 + n;
         tok[rb] = gr >> gsh;
         const int gg = gr & ((1 << gsh) - 1);
         valid[rb] = gg < G && tok[rb] < n_tok;
@@ -78,24 +118,29 @@ __global__ __launch_bounds__(64 * PW) void prefill_kernel(const PrefillArgs a)
 #pragma unroll
         for (int b = 0; b < NB; b++)
 #pragma unroll
-            for (int r = 0; r < 8; r++)
-                qb[rb][b][r] = valid[rb] ? qrow[32 * b + qk_chan<KT>(j, r)] : (_Float16)0.0f;
+            for (int r = 0; r < 8; r++) {
+                const _Float16 v = qrow[32 * b + qk_chan<KT>(j, r)];
+                qb[rb][b][r] = valid[rb] ? (neg ? -v : v) : (_Float16)0.0f;
+            }
     }
 
     PairRsrc rs;
     rs.kc = make_rsrc(a.kc + pair * Tc * g::RK, Tc * g::RK);
     rs.vc = make_rsrc(a.vc + pair * Tc * g::RV, Tc * g::RV);
-    if (KT != KVQ_F16)
+    if (KQ)
         rs.ks = make_rsrc(a.ks + pair * Tc * NB, Tc * NB * 2);
-    if (VT != KVQ_F16)
+    if (VQ)
         rs.vs = make_rsrc(a.vs + pair * Tc * NB, Tc * NB * 2);
     DmaOffsets<KT, VT, D> doff;
     doff.init(lane);
 
-    int k_rd[2][NB];
+    // LDS read offsets: K operand of score tile T (16 keys) and block b, the
+    // block scales of this lane's key in tile T; V operand reads as in decode
+    int k_rd[2][NB], ks_rd[2];
 #pragma unroll
     for (int T = 0; T < 2; T++) {
         const int r = 8 * (n >> 2) + 4 * T + (n & 3);
+        ks_rd[T] = g::KS_OFF + r * NB * 2;
 #pragma unroll
         for (int b = 0; b < NB; b++) {
             int c, within;
@@ -114,14 +159,13 @@ __global__ __launch_bounds__(64 * PW) void prefill_kernel(const PrefillArgs a)
         v_rd[i] = g::V_OFF + (j * g::CPG + (c ^ vswz<VT, g::CPG>(j))) * 16 + within;
     }
 
-    const int bp16 = (lane ^ 16) << 2, bp32 = (lane ^ 32) << 2;
-    const float c2 = a.c2;
-    float m_run[RB], l_run[RB];
-    floatx4 o[RB][NCT];
+    const half8 ones = splat8(0x3C003C00u);
+    float m_run[RB];
+    floatx4 o[RB][NCT], lacc[RB];
 #pragma unroll
     for (int rb = 0; rb < RB; rb++) {
         m_run[rb] = -INFINITY;
-        l_run[rb] = 0.0f;
+        lacc[rb] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
         for (int ct = 0; ct < NCT; ct++)
             o[rb][ct] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
@@ -129,20 +173,22 @@ __global__ __launch_bounds__(64 * PW) void prefill_kernel(const PrefillArgs a)
 
     const int ntile = (key_end + TILE - 1) / TILE;
     issue_tile<KT, VT, D>(lds[0], 0, lane, doff, rs, wave, PW);
-    for (int t = 0; t < ntile; t++) {
+    // One tile; DG: the tile may hold keys past a row's position (masking).
+    auto step = [&](auto diag_c, const int t) {
+        constexpr bool DG = decltype(diag_c)::value;
         const uint8_t *buf = lds[t & 1];
         const int tb = t * TILE;
         // every wave's share of this tile has landed before anyone reads it
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
 
-        // ---- operands of the tile into registers
+        // ---- raw operands of the tile into registers
         u32x4 kop[2][NB];
-        uint32_t ksc[4 * NB];
+        uint32_t ksw[2][(NB + 1) / 2];  // this lane's key's block scales, two per word
         u32x4 vop[VL];
         u32x4 vsc[NB];
 #pragma unroll
-        for (int T = 0; T < 2; T++)
+        for (int T = 0; T < 2; T++) {
 #pragma unroll
             for (int b = 0; b < NB; b++) {
                 if (KT == KVQ_F16) {
@@ -154,12 +200,16 @@ __global__ __launch_bounds__(64 * PW) void prefill_kernel(const PrefillArgs a)
                     kop[T][b] = u32x4{*reinterpret_cast<const uint32_t *>(buf + k_rd[T][b]), 0u, 0u, 0u};
                 }
             }
-        if (KT != KVQ_F16) {
-            const u32x4 *p = reinterpret_cast<const u32x4 *>(buf + g::KS_OFF + 16 * NB * j);
-#pragma unroll
-            for (int i = 0; i < NB; i++) {
-                const u32x4 w = p[i];
-                ksc[4 * i] = w.x, ksc[4 * i + 1] = w.y, ksc[4 * i + 2] = w.z, ksc[4 * i + 3] = w.w;
+            if (KQ) {
+                if (NB == 2) {
+                    ksw[T][0] = *reinterpret_cast<const uint32_t *>(buf + ks_rd[T]);
+                } else if (NB == 4) {
+                    const u32x2 w = *reinterpret_cast<const u32x2 *>(buf + ks_rd[T]);
+                    ksw[T][0] = w.x, ksw[T][1] = w.y;
+                } else {
+                    const u32x4 w = *reinterpret_cast<const u32x4 *>(buf + ks_rd[T]);
+                    ksw[T][0] = w.x, ksw[T][1] = w.y, ksw[T][2] = w.z, ksw[T][3] = w.w;
+                }
             }
         }
 #pragma unroll
@@ -171,28 +221,28 @@ __global__ __launch_bounds__(64 * PW) void prefill_kernel(const PrefillArgs a)
                 vop[i] = u32x4{w.x, w.y, 0u, 0u};
             }
         }
-        if (VT != KVQ_F16) {
+        if (VQ) {
 #pragma unroll
             for (int b = 0; b < NB; b++)
                 vsc[b] = *reinterpret_cast<const u32x4 *>(buf + g::VS_OFF + (j * NB + b) * 16);
         }
         // keys at or past key_end were never written for this chunk: their
         // value bits (and V scales) may be anything, even NaN -> force zero
-        if (tb + TILE > key_end) {
+        if (DG && tb + TILE > key_end) {
             uint32_t vk[4];
 #pragma unroll
             for (int i = 0; i < 4; i++) {
                 const int k0 = tb + 8 * j + 2 * i;
                 vk[i] = (k0 < key_end ? 0x0000FFFFu : 0u) | (k0 + 1 < key_end ? 0xFFFF0000u : 0u);
             }
-            if (VT == KVQ_F16) {
-#pragma unroll
-                for (int i = 0; i < VL; i++)
-                    vop[i] = u32x4{vop[i].x & vk[0], vop[i].y & vk[1], vop[i].z & vk[2], vop[i].w & vk[3]};
-            } else {
+            if (VQ) {
 #pragma unroll
                 for (int b = 0; b < NB; b++)
                     vsc[b] = u32x4{vsc[b].x & vk[0], vsc[b].y & vk[1], vsc[b].z & vk[2], vsc[b].w & vk[3]};
+            } else {
+#pragma unroll
+                for (int i = 0; i < VL; i++)
+                    vop[i] = u32x4{vop[i].x & vk[0], vop[i].y & vk[1], vop[i].z & vk[2], vop[i].w & vk[3]};
             }
         }
         // start the next tile's copy into the other buffer (its last readers
@@ -200,7 +250,7 @@ __global__ __launch_bounds__(64 * PW) void prefill_kernel(const PrefillArgs a)
         if (t + 1 < ntile)
             issue_tile<KT, VT, D>(lds[(t + 1) & 1], tb + TILE, lane, doff, rs, wave, PW);
 
-        // ---- scores for every row block (K operand unpacked once)
+        // ---- scores; the K operand (hi, lo) is built once for all row blocks
         floatx4 sacc[RB][2];
 #pragma unroll
         for (int rb = 0; rb < RB; rb++)
@@ -209,69 +259,75 @@ __global__ __launch_bounds__(64 * PW) void prefill_kernel(const PrefillArgs a)
         for (int T = 0; T < 2; T++)
 #pragma unroll
             for (int b = 0; b < NB; b++) {
-                half8 ka;
                 if (KT == KVQ_F16) {
-                    ka = pack4(kop[T][b].x, kop[T][b].y, kop[T][b].z, kop[T][b].w);
-                } else if (KT == KVQ_Q8_0) {
-                    ka = deq_q8(kop[T][b].x, kop[T][b].y);
-                } else {
-                    const uint32_t w = kop[T][b].x;
-                    ka = k_operand<KVQ_Q4_0>(&w);
-                }
+                    const half8 ka = pack4(kop[T][b].x, kop[T][b].y, kop[T][b].z, kop[T][b].w);
 #pragma unroll
-                for (int rb = 0; rb < RB; rb++) {
-                    if (KT == KVQ_F16) {
+                    for (int rb = 0; rb < RB; rb++)
                         sacc[rb][T] = mfma(ka, qb[rb][b], sacc[rb][T]);
+                } else {
+                    half8 ka;
+                    if (KT == KVQ_Q8_0) {
+                        ka = deq_q8(kop[T][b].x, kop[T][b].y);
                     } else {
-                        const floatx4 c = mfma(ka, qb[rb][b], floatx4{0.0f, 0.0f, 0.0f, 0.0f});
+                        const uint32_t w = kop[T][b].x;
+                        ka = k_operand<KVQ_Q4_0>(&w);
+                    }
+                    const uint32_t dw = ksw[T][b >> 1];
+                    const half8 dd = splat8(__builtin_amdgcn_perm(dw, dw, (b & 1) ? 0x07060706u : 0x05040504u));
+                    const half8 hi = ka * dd;
+                    const half8 lo = __builtin_elementwise_fma(ka, dd, -hi);
 #pragma unroll
-                        for (int i = 0; i < 4; i++)
-                            sacc[rb][T][i] = __builtin_fmaf(half_at(ksc, (4 * T + i) * NB + b), c[i], sacc[rb][T][i]);
+                    for (int rb = 0; rb < RB; rb++) {
+                        sacc[rb][T] = mfma(hi, qb[rb][b], sacc[rb][T]);
+                        sacc[rb][T] = mfma(lo, qb[rb][b], sacc[rb][T]);
                     }
                 }
             }
 
         // ---- online softmax per row block; key r of lane group j is tb+8j+r
-        uint32_t p16[RB][4];
-        const bool diag = tb + TILE - 1 > p0 + tok_first;  // some key is past some row's position
+        half8 pb[RB];
+        const bool diag = DG && tb + TILE - 1 > wave_first;  // some key of the tile is past some row's position
 #pragma unroll
         for (int rb = 0; rb < RB; rb++) {
-            float x[8];
+            float sc[8];
 #pragma unroll
             for (int r = 0; r < 8; r++)
-                x[r] = sacc[rb][r >> 2][r & 3] * c2;
+                sc[r] = sacc[rb][r >> 2][r & 3];
             if (diag) {
 #pragma unroll
                 for (int r = 0; r < 8; r++)
                     if (tb + 8 * j + r > lim[rb])
-                        x[r] = -INFINITY;
+                        sc[r] = -INFINITY;
             }
-            float mt = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])), fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
-            mt = fmaxf(mt, __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(bp16, __builtin_bit_cast(int, mt))));
-            mt = fmaxf(mt, __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(bp32, __builtin_bit_cast(int, mt))));
-            // key 0 is visible to every row, so m_run is finite after the
-            // first tile; a fully masked row of a later tile has mt = -inf
+            float mt = max3(max3(sc[0], sc[1], sc[2]), max3(sc[3], sc[4], sc[5]), max3(sc[6], sc[7], sc[7]));
+            mt = max_lane_groups(mt) * c2a;  // NaN only for a fully masked row at scale 0: no update
             if (__any(mt > m_run[rb])) {
                 const float m_new = fmaxf(m_run[rb], mt);
                 const float alpha = __builtin_amdgcn_exp2f(m_run[rb] - m_new);  // 0 on the first tile
-                l_run[rb] *= alpha;
+                lacc[rb] *= alpha;
 #pragma unroll
                 for (int ct = 0; ct < NCT; ct++)
                     o[rb][ct] *= alpha;
                 m_run[rb] = m_new;
             }
+            const float nm = -m_run[rb];
             float p[8];
 #pragma unroll
-            for (int r = 0; r < 8; r++) {
-                p[r] = __builtin_amdgcn_exp2f(x[r] - m_run[rb]);
-                l_run[rb] += p[r];
+            for (int r = 0; r < 8; r++)
+                p[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[r], c2a, nm));
+            if (diag) {
+#pragma unroll
+                for (int r = 0; r < 8; r++)
+                    p[r] = (sc[r] == -INFINITY) ? 0.0f : p[r];
             }
+            uint32_t w[4];
 #pragma unroll
             for (int i = 0; i < 4; i++)
-                p16[rb][i] = h2_bits(__builtin_convertvector((float2v){p[2 * i], p[2 * i + 1]}, half2));
+                w[i] = h2_bits(__builtin_convertvector((float2v){p[2 * i], p[2 * i + 1]}, half2));
+            pb[rb] = pack4(w[0], w[1], w[2], w[3]);
         }
 
-        // ---- O^T += V^T . P' (V operand unpacked once per block)
+        // ---- O^T += V^T . P; the V operand (times its scale) is built once
 #pragma unroll
         for (int b = 0; b < NB; b++) {
             half8 va[2];
@@ -291,32 +347,37 @@ __global__ __launch_bounds__(64 * PW) void prefill_kernel(const PrefillArgs a)
                     va[hh] = (VT == KVQ_F16) ? pack4(w.x, w.y, w.z, w.w) : deq_q8(w.x, w.y);
                 }
             }
+            if (VQ) {
+                const half8 dv = pack4(vsc[b].x, vsc[b].y, vsc[b].z, vsc[b].w);  // scales of keys 0..7
+                va[0] = va[0] * dv;
+                va[1] = va[1] * dv;
+            }
 #pragma unroll
             for (int rb = 0; rb < RB; rb++) {
-                half8 pb;
-                if (VT == KVQ_F16) {
-                    pb = pack4(p16[rb][0], p16[rb][1], p16[rb][2], p16[rb][3]);
-                } else {
-                    pb = pack4(h2_bits(bits_h2(p16[rb][0]) * bits_h2(vsc[b].x)),
-                               h2_bits(bits_h2(p16[rb][1]) * bits_h2(vsc[b].y)),
-                               h2_bits(bits_h2(p16[rb][2]) * bits_h2(vsc[b].z)),
-                               h2_bits(bits_h2(p16[rb][3]) * bits_h2(vsc[b].w)));
-                }
-                o[rb][2 * b] = mfma(va[0], pb, o[rb][2 * b]);
-                o[rb][2 * b + 1] = mfma(va[1], pb, o[rb][2 * b + 1]);
+                o[rb][2 * b] = mfma(va[0], pb[rb], o[rb][2 * b]);
+                o[rb][2 * b + 1] = mfma(va[1], pb[rb], o[rb][2 * b + 1]);
             }
         }
-    }
+#pragma unroll
+        for (int rb = 0; rb < RB; rb++)
+            lacc[rb] = mfma(ones, pb[rb], lacc[rb]);
+    };
+    // Tiles before t_d lie entirely at or below every row position of this
+    // wave and run without mask code.  Every wave still meets one barrier per
+    // tile, ntile in all.
+    const int t_d = min(ntile, (wave_first + 1) / TILE);
+    for (int t = 0; t < t_d; t++)
+        step(std::integral_constant<bool, false>(), t);
+    for (int t = t_d; t < ntile; t++)
+        step(std::integral_constant<bool, true>(), t);
 
     // ---- normalize and write this lane's rows: channels 16ct + 4j + i
 #pragma unroll
     for (int rb = 0; rb < RB; rb++) {
-        float l = l_run[rb] + __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(bp16, __builtin_bit_cast(int, l_run[rb])));
-        l += __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(bp32, __builtin_bit_cast(int, l)));
         if (valid[rb]) {
-            const int gg = (row0 + wave * 16 * RB + rb * 16 + n) & ((1 << gsh) - 1);
+            const int gg = (wrow0 + rb * 16 + n) & ((1 << gsh) - 1);
             float *dst = a.out + (((int64_t)s * n_tok + tok[rb]) * a.Hq + (int64_t)h * G + gg) * D;
-            const float inv = 1.0f / l;
+            const float inv = 1.0f / lacc[rb][0];
 #pragma unroll
             for (int ct = 0; ct < NCT; ct++)
                 *reinterpret_cast<floatx4 *>(dst + 16 * ct + 4 * j) = o[rb][ct] * inv;

@@ -21,7 +21,7 @@ pytestmark = pytest.mark.gpu
 PAIRS = list(itertools.product(["f16", "q8_0", "q4_0"], repeat=2))
 
 
-def prefill_case(kt, vt, S, Hq, Hkv, D, T, n_tok, q_pos0, seed, garbage=False, kscale=3.0):
+def prefill_case(kt, vt, S, Hq, Hkv, D, T, n_tok, q_pos0, seed, garbage=False, kscale=3.0, scale=None):
     """Append positions 0 .. max(q_pos0)+n_tok-1 of every sequence (the rest
     of the cache zero, or all-ones bytes with garbage=True), then run the
     chunk."""
@@ -46,7 +46,7 @@ def prefill_case(kt, vt, S, Hq, Hkv, D, T, n_tok, q_pos0, seed, garbage=False, k
     # the batch); past that the planes keep their initial bytes
     cache.append(0, K, V, [0] * S)
     orc.append(bits(K), bits(V), np.zeros(S, np.int32))
-    scale = 1.0 / np.sqrt(D)
+    scale = 1.0 / np.sqrt(D) if scale is None else scale
     ref = orc.attn_prefill(bits(Q), np.array(q_pos0, np.int32), scale)
     out = cache.prefill(0, Q, q_pos0, scale)
     torch.cuda.synchronize()
@@ -85,6 +85,14 @@ def test_prefill_ignores_garbage_past_chunk(kt, vt):
     set, NaN as binary16): the diagonal tiles must keep them out."""
     print(f"prefill garbage past chunk {kt}/{vt}", flush=True)
     prefill_case(kt, vt, S=2, Hq=16, Hkv=2, D=128, T=512, n_tok=50, q_pos0=[150, 131], seed=3, garbage=True)
+
+
+@pytest.mark.parametrize("scale", [-0.0883883, 0.0])
+def test_prefill_scale_sign(scale):
+    """A negative scale (moved onto Q by the kernel) and scale 0 (uniform
+    weights over the visible keys; masked keys must still get none)."""
+    print(f"prefill scale {scale}", flush=True)
+    prefill_case("q8_0", "q4_0", S=2, Hq=16, Hkv=2, D=128, T=300, n_tok=40, q_pos0=[200, 9], seed=31, scale=scale)
 
 
 def test_prefill_matches_decode_for_one_query():

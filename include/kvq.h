@@ -146,12 +146,11 @@ int kvq_append(const kvq_cache *cache, int32_t layer, const void *K, const void 
                const int32_t *pos, int32_t k_type, int32_t v_type, void *stream);
 
 /* Workspace bytes that kvq_attn_decode needs for any ctx_len <= max_ctx and
- * any split count: a counter region of n_seqs*n_kv_heads*4 bytes rounded up
- * to 256, then n_seqs*n_q_heads*splits*(head_dim+2)*4 bytes of split
- * partials.  The counter region must be zero-filled before the first call
- * (e.g. allocate the workspace zeroed); every call leaves it zero again.
- * A workspace serves one call at a time: calls that overlap in time (other
- * streams) need workspaces of their own. */
+ * any n_splits: (W + n_seqs*n_kv_heads) partial slots of
+ * (n_q_heads/n_kv_heads) * (head_dim+4) floats, W being the most waves a call
+ * can use (see kvq_attn_decode).  No initialization is needed.  A workspace
+ * serves one call at a time: calls that overlap in time (other streams)
+ * need workspaces of their own. */
 int kvq_decode_workspace_bytes(const kvq_shape *shape, size_t *bytes);
 
 /* Flash-decode one query token per sequence over layer `layer`.
@@ -161,14 +160,18 @@ int kvq_decode_workspace_bytes(const kvq_shape *shape, size_t *bytes);
  *             token's K/V first: ctx_len counts it)
  *   scale   : multiplies Q.K (typically 1/sqrt(head_dim)), used as passed
  *   out     : device float32 [n_seqs][n_q_heads][head_dim]
- *   workspace, workspace_bytes: device scratch for split partials
- *   n_splits: context splits per (sequence, kv head); 0 chooses; the
- *             library may use fewer than asked (never more than its merge
- *             can combine for this type pair, head_dim and head group)
- * Query head hq reads kv head hq / (n_q_heads/n_kv_heads).  One launch: each
- * workgroup handles one context split of one (sequence, kv head) and writes a
- * (max, sum, unnormalized output) partial; the last workgroup of each
- * (sequence, kv head) merges the partials (log-sum-exp) into `out`. */
+ *   workspace, workspace_bytes: device scratch for the partials
+ *   n_splits: about how many pieces the context of one (sequence, kv head)
+ *             is cut into; 0 chooses (fill the device).  The call never uses
+ *             more waves than the cache has 32-token tiles in use.
+ * Query head hq reads kv head hq / (n_q_heads/n_kv_heads).  Two launches.
+ * The first streams the 32-token tiles of all (sequence, kv head) pairs, one
+ * pair after the other, cut into W equal contiguous pieces, one per wave
+ * (W = n_splits * n_seqs * n_kv_heads, or the automatic choice); a wave
+ * writes a (max, sum, unnormalized output) partial for every pair its piece
+ * touches.  The second merges the partials of each pair (log-sum-exp) into
+ * `out`.  Errors: KVQ_E_RANGE (ctx_len, n_splits > KVQ_MAX_SPLITS),
+ * KVQ_E_WORKSPACE, KVQ_E_SHAPE (2^31 or more tiles in use). */
 int kvq_attn_decode(const kvq_cache *cache, int32_t layer, const void *Q, const int32_t *ctx_len, float scale,
                     float *out, void *workspace, size_t workspace_bytes, int32_t n_splits, void *stream);
 

@@ -185,8 +185,7 @@ class KVCache:
     def workspace(self):
         if self._ws is None:
             nb = kvq_decode_workspace_bytes(self.shape)
-            # zero-filled: the leading counter region must start at zero
-            self._ws = self.torch.zeros(nb // 4, dtype=self.torch.float32, device=self.device)
+            self._ws = self.torch.empty(max(nb, 16) // 4, dtype=self.torch.float32, device=self.device)
         return self._ws
 
     def decode(self, layer, Q, ctx_len, scale, out=None, n_splits=0):

@@ -75,33 +75,56 @@ int check_layer(const kvq_cache *c, int32_t layer)
     return KVQ_OK;
 }
 
-// Split plan of a decode call: tokens per split (a multiple of the 32-token
-// tile) and the split count covering the longest context.
-void decode_plan(const kvq_shape &sh, int max_len, int32_t req, int cap, int *n_splits, int *tps)
+// Decode work split (the kernels describe it): k waves per (sequence, kv
+// head) pair, the same k for the pairs of one sequence.  n_splits > 0 asks
+// for k = n_splits; 0 fills the device (WAVES_PER_CU waves per CU, k about
+// proportional to each sequence's tiles, at least four tiles per wave).
+// Never more waves for a pair than it has tiles.
+constexpr int AUTO_WAVES_MAX = 4096;
+// One workgroup (four waves, one per SIMD) per CU streams best: more waves
+// per CU measured slower (more concurrent streams, no more bandwidth).
+constexpr int WAVES_PER_CU = 4;
+
+int device_cus()
 {
-    const int64_t units = (int64_t)sh.n_seqs * sh.n_kv_heads;
-    int want = req;
-    if (want <= 0) {
-        // enough workgroups to fill 256 CUs several times over, at least
-        // 128 tokens (one tile per wave) per split
-        const int64_t target = 2048;
-        want = (int)std::min<int64_t>(KVQ_MAX_SPLITS, (target + units - 1) / units);
-        want = std::min(want, std::max(1, (max_len + 127) / 128));
+    static int cached[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64)
+        return 256;
+    if (!cached[dev]) {
+        int cus = 0;
+        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
+            cus = 256;
+        cached[dev] = cus;
     }
-    want = std::max(1, std::min(want, std::min(KVQ_MAX_SPLITS, cap)));
-    int t = (max_len + want - 1) / want;
-    t = (t + 31) / 32 * 32;
-    *tps = t;
-    *n_splits = (max_len + t - 1) / t;
+    return cached[dev];
 }
 
-// Workspace: per-(sequence, kv head) counters first (their zero state must
-// survive calls with different split counts), then the split partials.
-size_t counters_bytes(const kvq_shape &sh) { return ((size_t)sh.n_seqs * sh.n_kv_heads * 4 + 255) / 256 * 256; }
-
-size_t workspace_need(const kvq_shape &sh, int n_splits)
+// Fills wave_start[0..n_seqs] and returns the wave count W.
+int64_t decode_plan(const kvq_shape &sh, const int32_t *ctx_len, int32_t req, int32_t *wave_start)
 {
-    return counters_bytes(sh) + (size_t)sh.n_seqs * sh.n_q_heads * n_splits * (sh.head_dim + 2) * sizeof(float);
+    int64_t T = 0;
+    for (int s = 0; s < sh.n_seqs; s++)
+        T += (int64_t)sh.n_kv_heads * ((ctx_len[s] + 31) / 32);
+    const int per_cu = sh.head_dim <= 128 ? WAVES_PER_CU : 4;
+    const int64_t target = std::min<int64_t>((int64_t)device_cus() * per_cu, AUTO_WAVES_MAX);
+    int64_t W = 0;
+    for (int s = 0; s < sh.n_seqs; s++) {
+        const int64_t nt = (ctx_len[s] + 31) / 32;
+        int64_t k = req > 0 ? req : std::min<int64_t>(target * nt / T, nt / 4);
+        k = std::max<int64_t>(1, std::min<int64_t>(k, nt));
+        wave_start[s] = (int32_t)W;
+        W += k * sh.n_kv_heads;
+    }
+    wave_start[sh.n_seqs] = (int32_t)W;
+    return W;
+}
+
+// Workspace: one partial slot of [G][head_dim + 4] floats per wave.
+size_t workspace_need(const kvq_shape &sh, int64_t W)
+{
+    const int64_t G = sh.n_q_heads / sh.n_kv_heads;
+    return (size_t)(W * G * (sh.head_dim + 4) * (int64_t)sizeof(float));
 }
 
 }  // namespace
@@ -186,9 +209,13 @@ int kvq_decode_workspace_bytes(const kvq_shape *shape, size_t *bytes)
         return rc;
     if (!bytes)
         return KVQ_E_ARG;
-    // the most splits any call can use: KVQ_MAX_SPLITS, or one per tile
-    const int most = (int)std::min<int64_t>(KVQ_MAX_SPLITS, capacity(shape->max_ctx) / 32);
-    *bytes = workspace_need(*shape, most);
+    // the most waves any call can use: at most one per tile of a full cache,
+    // KVQ_MAX_SPLITS per pair, or the automatic choice (which may round up to
+    // one wave per pair)
+    const int64_t pairs = (int64_t)shape->n_seqs * shape->n_kv_heads;
+    const int64_t t_max = pairs * (capacity(shape->max_ctx) / 32);
+    const int64_t w_max = std::min<int64_t>(t_max, std::max<int64_t>(AUTO_WAVES_MAX + pairs, (int64_t)KVQ_MAX_SPLITS * pairs));
+    *bytes = workspace_need(*shape, w_max);
     return KVQ_OK;
 }
 
@@ -205,38 +232,43 @@ int kvq_attn_decode(const kvq_cache *cache, int32_t layer, const void *Q, const 
         return KVQ_E_ARG;
     if (n_splits < 0 || n_splits > KVQ_MAX_SPLITS)
         return KVQ_E_RANGE;
-    int max_len = 0;
-    for (int s = 0; s < sh.n_seqs; s++) {
+    DecodeArgs a;
+    MergeArgs m;
+    memset(&a, 0, sizeof(a));
+    memset(&m, 0, sizeof(m));
+    for (int s = 0; s < sh.n_seqs; s++)
         if (ctx_len[s] < 1 || ctx_len[s] > sh.max_ctx)
             return KVQ_E_RANGE;
-        max_len = std::max(max_len, ctx_len[s]);
-    }
-    const kvq_plane &kp = cache->k[layer], &vp = cache->v[layer];
-    const int cap = decode_split_cap(kp.type, vp.type, sh.head_dim, sh.n_q_heads / sh.n_kv_heads);
-    int nsp, tps;
-    decode_plan(sh, max_len, n_splits, cap, &nsp, &tps);
-    if (!workspace || !aligned16(workspace) || workspace_bytes < workspace_need(sh, nsp))
+    const int64_t W = decode_plan(sh, ctx_len, n_splits, a.wave_start);
+    if (W >= ((int64_t)1 << 31) / 64)
+        return KVQ_E_SHAPE;
+    if (!workspace || !aligned16(workspace) || workspace_bytes < workspace_need(sh, W))
         return KVQ_E_WORKSPACE;
 
-    DecodeArgs a;
-    memset(&a, 0, sizeof(a));
+    const kvq_plane &kp = cache->k[layer], &vp = cache->v[layer];
     a.kc = (const uint8_t *)kp.codes;
     a.ks = (const uint16_t *)kp.scales;
     a.vc = (const uint8_t *)vp.codes;
     a.vs = (const uint16_t *)vp.scales;
     a.q = (const uint16_t *)Q;
-    a.out = out;
-    a.counters = (uint32_t *)workspace;
-    a.ws = (float *)((char *)workspace + counters_bytes(sh));
+    a.ws = (float *)workspace;
     a.Hq = sh.n_q_heads;
     a.Hkv = sh.n_kv_heads;
     a.G = sh.n_q_heads / sh.n_kv_heads;
     a.Tc = (int32_t)capacity(sh.max_ctx);
-    a.tps = tps;
-    a.n_splits = nsp;
+    a.n_seqs = sh.n_seqs;
+    a.W = (int32_t)W;
     a.c2 = (float)((double)scale * 1.4426950408889634);
     memcpy(a.ctx_len, ctx_len, sizeof(int32_t) * sh.n_seqs);
-    hipError_t e = launch_decode(kp.type, vp.type, sh.head_dim, a, sh.n_seqs, (hipStream_t)stream);
+
+    m.ws = a.ws;
+    m.out = out;
+    m.Hq = a.Hq;
+    m.Hkv = a.Hkv;
+    m.G = a.G;
+    m.D = sh.head_dim;
+    memcpy(m.wave_start, a.wave_start, sizeof(int32_t) * (sh.n_seqs + 1));
+    hipError_t e = launch_decode(kp.type, vp.type, sh.head_dim, a, m, sh.n_seqs * sh.n_kv_heads, (hipStream_t)stream);
     return e == hipSuccess ? KVQ_OK : KVQ_E_HIP;
 }
 

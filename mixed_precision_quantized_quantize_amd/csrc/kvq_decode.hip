@@ -1,5 +1,5 @@
-// kvq_decode.hip -- split-K flash decode over the quantized cache with the
-// log-sum-exp merge of the split partials folded into the same launch.
+// kvq_decode.hip -- flash decode over the quantized cache: one persistent
+// streaming kernel and one log-sum-exp merge kernel.
 //
 // Flash attention in the sense of the llama.cpp guide's "Flash Attention"
 // section (tiled, the score matrix never materialized, exactly softmax
@@ -7,10 +7,17 @@
 // discussion expects the gain "integrated directly into FlashAttention", and
 // the llama.cpp issue shows a quantized V cache is only usable that way.
 //
-// One workgroup = (split of the context, kv head, sequence), four waves.
-// Each wave walks 32-token tiles of its split and serves the whole GQA group
-// (up to 16 query heads) of its kv head with two matrix-core contractions
-// per tile, both v_mfma_f32_16x16x32_f16:
+// Work split.  Every (sequence, kv head) pair gets k waves (k per sequence,
+// about proportional to its context, at least one tile per wave); wave r of
+// a pair takes the pair's 32-token tiles r, r+k, r+2k, ... so that the k
+// waves stream neighbouring tiles at any moment.  Each wave writes one
+// partial -- running max m (base 2), sum l and the unnormalized output O of
+// each query head -- into its own slot, and the merge kernel combines the k
+// partials of each pair.  A wave keeps the copies of its next two tiles in
+// flight while it computes the current one.
+//
+// Per tile a wave serves the whole GQA group (up to 16 query heads) of its kv
+// head with two matrix-core contractions, both v_mfma_f32_16x16x32_f16:
 //   S^T[token][head] = K[token][c] . Q^T[c][head]  -- one MFMA per 16 tokens
 //       and 32-channel block; the raw codes are exact in binary16 and the
 //       block's K scale multiplies the MFMA result per token;
@@ -20,11 +27,9 @@
 // second, so probabilities never leave registers.  The V plane stores 8
 // tokens interleaved, so a lane's P.V operand (8 tokens of one channel) is
 // one 8- or 16-byte load.  Online softmax runs in base 2 (scores times
-// scale*log2 e).  The next tile's codes and scales are loaded while the
-// current one is computed.  The four waves' (m, l, O) merge in LDS; each
-// workgroup writes one partial per query head, and the last workgroup of a
-// (sequence, kv head) -- found with a device-scope counter -- merges all the
-// partials and writes the normalized output.
+// scale*log2 e).
+#include <type_traits>
+
 #include "kvq_device.h"
 
 namespace kvq {
@@ -33,41 +38,45 @@ namespace {
 using namespace dev;
 
 template <int KT, int VT, int D>
-__global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(D <= 128 ? 3 : 1))) void decode_kernel(const DecodeArgs a)
+__global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(D <= 128 ? 2 : 1))) void decode_kernel(const DecodeArgs a)
 {
     using g = Geo<KT, VT, D>;
     constexpr int NB = g::NB, NCT = g::NCT;
 
+    // two tile buffers per wave where they fit (two separate arrays, so that
+    // the compiler sees that a read of one does not wait for the other)
+    constexpr bool DB = 2 * g::LDS_A <= 160 * 1024;
     __shared__ __attribute__((aligned(16))) uint8_t lds_a[g::LDS_A];
-    __shared__ float sm_m[WAVES][16];
-    __shared__ float sm_l[WAVES][16];
-    __shared__ int sm_last;
+    __shared__ __attribute__((aligned(16))) uint8_t lds_b[DB ? g::LDS_A : 16];
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: scalar addressing
     const int n = lane & 15, j = lane >> 4;
-    const int split = blockIdx.x, h = blockIdx.y, s = blockIdx.z;
-    const int ctx = a.ctx_len[s];
-    const int t_begin = split * a.tps;
-    if (t_begin >= ctx)
-        return;  // holds no tokens: not counted by the merge
-    const int t_end = min(t_begin + a.tps, ctx);
-    const int nsp = (ctx + a.tps - 1) / a.tps;
-    const int G = a.G;
-    const int64_t pair = (int64_t)s * a.Hkv + h;
+    const int gw = blockIdx.x * WAVES + wave;
+    if (gw >= a.W)
+        return;
+    const int G = a.G, Hkv = a.Hkv;
     const int64_t Tc = a.Tc;
 
-    // Q^T operand: lane (n = head, j) holds 8 channels of each block.
-    half8 qb[NB];
+    // this wave's pair (s, h), its index r among the pair's k waves
+    int s = 0;
     {
-        const _Float16 *qrow =
-            reinterpret_cast<const _Float16 *>(a.q) + ((int64_t)s * a.Hq + (int64_t)h * G + min(n, G - 1)) * D;
-#pragma unroll
-        for (int b = 0; b < NB; b++)
-#pragma unroll
-            for (int r = 0; r < 8; r++)
-                qb[b][r] = (n < G) ? qrow[32 * b + qk_chan<KT>(j, r)] : (_Float16)0.0f;
+        int hi = a.n_seqs;  // wave_start[s] <= gw < wave_start[hi]
+        while (hi - s > 1) {
+            const int mid = (s + hi) >> 1;
+            if (a.wave_start[mid] <= gw)
+                s = mid;
+            else
+                hi = mid;
+        }
     }
+    const int k = (a.wave_start[s + 1] - a.wave_start[s]) / Hkv;
+    const int local = gw - a.wave_start[s];
+    const int h = local / k, r = local - h * k;
+    const int ctx = a.ctx_len[s];
+    const int nt = (ctx + TILE - 1) / TILE;
+    const int n_mine = (nt - r + k - 1) / k;  // tiles r, r+k, ... below nt (>= 1)
+    const int64_t pair = (int64_t)s * Hkv + h;
 
     PairRsrc rs;
     rs.kc = make_rsrc(a.kc + pair * Tc * g::RK, Tc * g::RK);
@@ -76,6 +85,29 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(D <=
         rs.ks = make_rsrc(a.ks + pair * Tc * NB, Tc * NB * 2);
     if (VT != KVQ_F16)
         rs.vs = make_rsrc(a.vs + pair * Tc * NB, Tc * NB * 2);
+
+    // Q^T operand: lane (n = head, j) holds 8 channels of each block (the
+    // channels qk_chan picks: 8j.. for f16/q8_0, 4j.. and 16+4j.. for q4_0);
+    // buffer loads from the scalar base of the pair's Q rows
+    half8 qb[NB];
+    {
+        const __amdgpu_buffer_rsrc_t rq =
+            make_rsrc(reinterpret_cast<const _Float16 *>(a.q) + ((int64_t)s * a.Hq + (int64_t)h * G) * D, G * D * 2);
+        const int qoff = 2 * (n * D + (KT == KVQ_Q4_0 ? 4 * j : 8 * j));
+#pragma unroll
+        for (int b = 0; b < NB; b++) {
+            qb[b] = half8{};
+            if (n < G) {  // lanes past the group keep zeros (their loads are not issued)
+                if (KT == KVQ_Q4_0) {
+                    const u32x2 lo = __builtin_amdgcn_raw_buffer_load_b64(rq, qoff + 64 * b, 0, 0);
+                    const u32x2 hi2 = __builtin_amdgcn_raw_buffer_load_b64(rq, qoff + 64 * b + 32, 0, 0);
+                    qb[b] = pack4(lo.x, lo.y, hi2.x, hi2.y);
+                } else {
+                    qb[b] = __builtin_bit_cast(half8, __builtin_amdgcn_raw_buffer_load_b128(rq, qoff + 64 * b, 0, 0));
+                }
+            }
+        }
+    }
     const float c2 = a.c2;
 
     DmaOffsets<KT, VT, D> doff;
@@ -105,12 +137,16 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(D <=
     }
 
     const int bp16 = (lane ^ 16) << 2, bp32 = (lane ^ 32) << 2;  // ds_bpermute byte addresses
-    float m_run = -INFINITY;  // running max (base 2) of head n, equal in the 4 lane groups
-    float l_run = 0.0f;       // this lane's share of the running sum
+    float m_run;    // running max (base 2) of head n, equal in the 4 lane groups
+    float l_run;    // this lane's share of the running sum
     floatx4 o[NCT];
+    auto reset = [&]() {
+        m_run = -INFINITY;
+        l_run = 0.0f;
 #pragma unroll
-    for (int ct = 0; ct < NCT; ct++)
-        o[ct] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
+        for (int ct = 0; ct < NCT; ct++)
+            o[ct] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
+    };
 
     // The operands of one tile, read from its LDS copy into registers.
     struct Ops {
@@ -158,7 +194,7 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(D <=
     };
 
     // One 32-token tile starting at token tb, from its operands in registers.
-    auto process = [&](const Ops &op, const int tb) {
+    auto process = [&](const Ops &op, const int tb, const int t_end) {
         // ---------------- scores: S^T tile T, lane holds tokens 8j+4T+i, head n
         const uint32_t *ksc = op.ks;
         floatx4 sacc[2];
@@ -271,167 +307,162 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(D <=
         }
     };
 
-    // ---------------- walk the split: this wave takes tiles wave, wave+4, ...
-    // Per tile: wait for its copy, read its operands out of LDS into
-    // registers, start copying the wave's next tile into the same LDS space,
-    // then compute -- the copy of tile i+1 streams during the math of tile i.
-    uint8_t *buf = lds_a + wave * g::BYTES;
-    const int step = TILE * WAVES;
-    int tb = t_begin + TILE * wave;
-    if (tb < t_end) {
-        issue_tile<KT, VT, D>(buf, tb, lane, doff, rs);
-        while (true) {
-            Ops op;
-            read_ops(buf, op);
-            const int tn = tb + step;
-            if (tn < t_end) {
-                asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // LDS reads done before it is refilled
-                issue_tile<KT, VT, D>(buf, tn, lane, doff, rs);
-            }
-            process(op, tb);
-            tb = tn;
-            if (tb >= t_end)
-                break;
-        }
-    }
-    // every copy into LDS has landed before the buffers are reused below
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
+    // ---------------- stream the wave's tiles.  Per tile: wait for its copy,
+    // read its operands out of LDS into registers, start the copy of a later
+    // tile into the freed LDS space, then compute.  With two LDS buffers per
+    // wave the copies of the next two tiles are in flight during the math of
+    // the current one.
+    //
+    // The waits are explicit: the compiler does not reliably track
+    // direct-to-LDS copies against LDS reads.  Vector-memory loads complete
+    // in issue order, so "at most NDMA outstanding" (the count of one tile's
+    // copy instructions) means every load issued before the newer tile's copy
+    // has completed.
+    constexpr int NKS = (KT == KVQ_F16) ? 0 : (g::KS_BYTES == 128 ? 1 : g::KS_BYTES / 256);
+    constexpr int NVS = (VT == KVQ_F16) ? 0 : (g::VS_BYTES == 128 ? 1 : g::VS_BYTES / 256);
+    constexpr int NDMA = g::K_BYTES / 1024 + NKS + g::V_BYTES / 1024 + NVS;
+    static_assert(NDMA < 64, "vmcnt holds 6 bits");
+    constexpr int WAIT_NEWER = (NDMA & 15) | ((NDMA >> 4) << 14) | 0x70 | 0xF00;  // vmcnt(NDMA)
+    constexpr int WAIT_ALL = 0x70 | 0xF00;                                          // vmcnt(0)
 
-    // ---------------- merge the four waves: scale to the common max, then
-    // accumulate in LDS one wave after the other (deterministic order)
+    reset();
+    // Tile i (of n_mine) sits in `buf`; the copy of tile i+1 was issued after
+    // it; tile i+DIST goes into `buf` once tile i's operands are in registers.
+    auto step = [&](uint8_t *buf, auto dist_c, const int i) {
+        constexpr int DIST = decltype(dist_c)::value;
+        if (DIST == 2 && i + 1 < n_mine)
+            __builtin_amdgcn_s_waitcnt(WAIT_NEWER);
+        else
+            __builtin_amdgcn_s_waitcnt(WAIT_ALL);
+        Ops op;
+        read_ops(buf, op);
+        if (i + DIST < n_mine) {
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // LDS reads done before it is refilled
+            issue_tile<KT, VT, D>(buf, (r + (i + DIST) * k) * TILE, lane, doff, rs);
+        }
+        process(op, (r + i * k) * TILE, ctx);
+    };
+    uint8_t *buf_a = lds_a + wave * g::BYTES;
+    issue_tile<KT, VT, D>(buf_a, r * TILE, lane, doff, rs);
+    if constexpr (DB) {
+        uint8_t *buf_b = lds_b + wave * g::BYTES;
+        if (n_mine > 1)
+            issue_tile<KT, VT, D>(buf_b, (r + k) * TILE, lane, doff, rs);
+        int i = 0;
+        for (; i + 1 < n_mine; i += 2) {
+            step(buf_a, std::integral_constant<int, 2>(), i);
+            step(buf_b, std::integral_constant<int, 2>(), i + 1);
+        }
+        if (i < n_mine)
+            step(buf_a, std::integral_constant<int, 2>(), i);
+    } else {
+        for (int i = 0; i < n_mine; i++)
+            step(buf_a, std::integral_constant<int, 1>(), i);
+    }
+
+    // ---------------- the wave's partial: O of head n (channels 16ct + 4j + i),
+    // m, l -- buffer stores from the scalar base of the slot
     float l_tot = l_run + __shfl_xor(l_run, 16);
     l_tot += __shfl_xor(l_tot, 32);
-    if (j == 0)
-        sm_m[wave][n] = m_run;
+    if (n < G) {
+        const __amdgpu_buffer_rsrc_t rw = make_rsrc(a.ws + (int64_t)gw * G * (D + 4), G * (D + 4) * 4);
+        const int off = 4 * (n * (D + 4) + 4 * j);
+#pragma unroll
+        for (int ct = 0; ct < NCT; ct++)
+            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, o[ct]), rw, off + 64 * ct, 0, 0);
+        if (j == 0) {
+            __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, m_run), rw, off + 4 * D, 0, 0);
+            __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, l_tot), rw, off + 4 * D + 4, 0, 0);
+        }
+    }
+}
+
+// Log-sum-exp merge of the partials of one (sequence, kv head) pair for one
+// query head: workgroup = (pair, head), thread = output channel.  The slot
+// weights 2^(m_j - M) go through LDS in chunks, so that every thread's loads
+// of its channel's partial outputs are independent and issued together.
+constexpr int MERGE_CHUNK = 512;
+
+__device__ inline float block_reduce(float v, float *sh, bool is_max)
+{
+    // wave64 butterfly, then across the waves of the workgroup through LDS
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) {
+        const float u = __shfl_xor(v, o);
+        v = is_max ? fmaxf(v, u) : v + u;
+    }
+    const int wave = threadIdx.x >> 6, nw = (blockDim.x + 63) >> 6;
     __syncthreads();
-    float M = sm_m[0][n];
-#pragma unroll
-    for (int w = 1; w < WAVES; w++)
-        M = fmaxf(M, sm_m[w][n]);
-    const float e = (m_run == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(m_run - M);
-    if (j == 0)
-        sm_l[wave][n] = l_tot * e;
-    float *obuf = reinterpret_cast<float *>(lds_a);  // [16][D]
-#pragma unroll
-    for (int w = 0; w < WAVES; w++) {
-        if (wave == w && n < G) {
-#pragma unroll
-            for (int ct = 0; ct < NCT; ct++)
-#pragma unroll
-                for (int i = 0; i < 4; i++) {
-                    const int idx = n * D + 16 * ct + 4 * j + i;
-                    obuf[idx] = (w == 0 ? 0.0f : obuf[idx]) + o[ct][i] * e;
-                }
+    if ((threadIdx.x & 63) == 0)
+        sh[wave] = v;
+    __syncthreads();
+    float r = sh[0];
+    for (int w = 1; w < nw; w++)
+        r = is_max ? fmaxf(r, sh[w]) : r + sh[w];
+    return r;
+}
+
+__global__ __launch_bounds__(256) void merge_kernel(const MergeArgs a)
+{
+    __shared__ float wts[MERGE_CHUNK];
+    __shared__ float red[4];
+    const int G = a.G, D = a.D, Dp = a.D + 4;
+    const int pair = blockIdx.x / G, gg = blockIdx.x - pair * G;
+    const int s = pair / a.Hkv, h = pair - s * a.Hkv;
+    const int k = (a.wave_start[s + 1] - a.wave_start[s]) / a.Hkv;  // the pair's waves = its slots
+    const int w0 = a.wave_start[s] + h * k;
+    const int nslot = k;
+    const int64_t stride = (int64_t)G * Dp;  // floats between consecutive slots
+    const float *base = a.ws + ((int64_t)w0 * G + gg) * Dp;
+    const int c = threadIdx.x;  // blockDim.x == D
+
+    float mx = -INFINITY;
+    for (int k = c; k < nslot; k += D)
+        mx = fmaxf(mx, base[k * stride + D]);
+    const float M = block_reduce(mx, red, true);
+
+    float lsum = 0.0f, acc = 0.0f;
+    for (int k0 = 0; k0 < nslot; k0 += MERGE_CHUNK) {
+        const int chunk = min(MERGE_CHUNK, nslot - k0);
+        __syncthreads();  // the previous chunk's weights are no longer read
+        for (int k = c; k < chunk; k += D) {
+            const float *pk = base + (int64_t)(k0 + k) * stride;
+            const float w = __builtin_amdgcn_exp2f(pk[D] - M);
+            wts[k] = w;
+            lsum += pk[D + 1] * w;
         }
         __syncthreads();
-    }
-
-    const int Dp = D + 2;
-    const int64_t head_stride = (int64_t)a.n_splits * Dp;  // between query heads
-    float *ws_pair = a.ws + ((int64_t)s * a.Hq + (int64_t)h * G) * head_stride;
-    float *out_pair = a.out + ((int64_t)s * a.Hq + (int64_t)h * G) * D;
-    for (int idx = threadIdx.x; idx < G * D; idx += 64 * WAVES) {
-        const int gg = idx / D, c = idx - gg * D;
-        float Mg = sm_m[0][gg], lsum = 0.0f;
-#pragma unroll
-        for (int w = 1; w < WAVES; w++)
-            Mg = fmaxf(Mg, sm_m[w][gg]);
-#pragma unroll
-        for (int w = 0; w < WAVES; w++)
-            lsum += sm_l[w][gg];
-        const float acc = obuf[idx];
-        if (nsp == 1) {
-            out_pair[idx] = acc / lsum;  // the only split: final output
-        } else {
-            // device-scope stores: written through to the point where every
-            // XCD's loads of the same scope see them, without flushing any L2
-            float *dst = ws_pair + gg * head_stride + (int64_t)split * Dp;
-            st_dev(dst + c, acc);
-            if (c == 0) {
-                st_dev(dst + D, Mg);
-                st_dev(dst + D + 1, lsum);
-            }
-        }
-    }
-    if (nsp == 1)
-        return;
-
-    // ---------------- the last workgroup of this (sequence, kv head) merges
-    // Every wave waits until its partial stores are performed (acknowledged at
-    // device scope), then one lane counts the split as done; the workgroup
-    // that completes the count merges.
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        const unsigned prev = __hip_atomic_fetch_add(a.counters + pair, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        sm_last = (prev == (unsigned)(nsp - 1));
-    }
-    __syncthreads();
-    if (!sm_last)
-        return;
-
-    // (m_j, l_j) of every (split, head) into LDS (after the [16][D] buffer),
-    // loads issued together; the host keeps nsp * G * 8 bytes within it
-    float *wgt = reinterpret_cast<float *>(lds_a) + 16 * D;  // [nsp][G]: m_j, then 2^(m_j - M)
-    float *lj = wgt + nsp * G;                               // [nsp][G]
-    float *tot = &sm_m[0][0];                                // [16]: 1 / sum_j l_j 2^(m_j - M)
-    for (int idx = threadIdx.x; idx < nsp * G; idx += 64 * WAVES) {
-        const int sp = idx / G, gg = idx - sp * G;
-        const float *pp = ws_pair + gg * head_stride + (int64_t)sp * Dp + D;
-        wgt[idx] = ld_dev(pp);
-        lj[idx] = ld_dev(pp + 1);
-    }
-    __syncthreads();
-    if ((int)threadIdx.x < G) {
-        const int gg = threadIdx.x;
-        float Mx = -INFINITY;
-        for (int sp = 0; sp < nsp; sp++)
-            Mx = fmaxf(Mx, wgt[sp * G + gg]);
-        float l = 0.0f;
-        for (int sp = 0; sp < nsp; sp++) {
-            const float ew = __builtin_amdgcn_exp2f(wgt[sp * G + gg] - Mx);
-            wgt[sp * G + gg] = ew;
-            l += lj[sp * G + gg] * ew;
-        }
-        tot[gg] = 1.0f / l;
-    }
-    __syncthreads();
-    for (int idx = threadIdx.x; idx < G * D; idx += 64 * WAVES) {
-        const int gg = idx / D, c = idx - gg * D;
-        const float *base = ws_pair + gg * head_stride + c;
-        float acc = 0.0f;
-        int sp = 0;
-        for (; sp + 8 <= nsp; sp += 8) {  // eight loads in flight at a time
+        const float *pc = base + (int64_t)k0 * stride + c;
+        int k = 0;
+        for (; k + 8 <= chunk; k += 8) {  // eight independent loads in flight
             float v[8];
 #pragma unroll
             for (int u = 0; u < 8; u++)
-                v[u] = ld_dev(base + (int64_t)(sp + u) * Dp);
+                v[u] = pc[(int64_t)(k + u) * stride];
 #pragma unroll
             for (int u = 0; u < 8; u++)
-                acc += v[u] * wgt[(sp + u) * G + gg];
+                acc += v[u] * wts[k + u];
         }
-        for (; sp < nsp; sp++)
-            acc += ld_dev(base + (int64_t)sp * Dp) * wgt[sp * G + gg];
-        out_pair[idx] = acc * tot[gg];
+        for (; k < chunk; k++)
+            acc += pc[(int64_t)k * stride] * wts[k];
     }
-    if (threadIdx.x == 0)
-        __hip_atomic_store(a.counters + pair, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const float L = block_reduce(lsum, red, false);
+    a.out[((int64_t)s * a.Hq + (int64_t)h * G + gg) * D + c] = acc / L;
 }
 
 template <int KT, int VT, int D>
-hipError_t launch_dec(const DecodeArgs &a, int n_seqs, hipStream_t st)
+hipError_t launch_dec(const DecodeArgs &a, hipStream_t st)
 {
-    dim3 grid(a.n_splits, a.Hkv, n_seqs);
+    dim3 grid((a.W + WAVES - 1) / WAVES);
     hipLaunchKernelGGL((decode_kernel<KT, VT, D>), grid, dim3(64 * WAVES), 0, st, a);
     return hipGetLastError();
 }
 
 template <int D>
-hipError_t launch_dec_d(int kt, int vt, const DecodeArgs &a, int n_seqs, hipStream_t st)
+hipError_t launch_dec_d(int kt, int vt, const DecodeArgs &a, hipStream_t st)
 {
 #define KVQ_D(K, V) \
-    if (kt == K && vt == V) return launch_dec<K, V, D>(a, n_seqs, st);
+    if (kt == K && vt == V) return launch_dec<K, V, D>(a, st);
     KVQ_D(KVQ_F16, KVQ_F16) KVQ_D(KVQ_F16, KVQ_Q8_0) KVQ_D(KVQ_F16, KVQ_Q4_0)
     KVQ_D(KVQ_Q8_0, KVQ_F16) KVQ_D(KVQ_Q8_0, KVQ_Q8_0) KVQ_D(KVQ_Q8_0, KVQ_Q4_0)
     KVQ_D(KVQ_Q4_0, KVQ_F16) KVQ_D(KVQ_Q4_0, KVQ_Q8_0) KVQ_D(KVQ_Q4_0, KVQ_Q4_0)
@@ -439,36 +470,21 @@ hipError_t launch_dec_d(int kt, int vt, const DecodeArgs &a, int n_seqs, hipStre
     return hipErrorInvalidValue;
 }
 
-template <int D>
-int split_cap_d(int kt, int vt, int G)
-{
-    int bytes = 0;
-#define KVQ_C(K, V) \
-    if (kt == K && vt == V) bytes = Geo<K, V, D>::LDS_A;
-    KVQ_C(KVQ_F16, KVQ_F16) KVQ_C(KVQ_F16, KVQ_Q8_0) KVQ_C(KVQ_F16, KVQ_Q4_0)
-    KVQ_C(KVQ_Q8_0, KVQ_F16) KVQ_C(KVQ_Q8_0, KVQ_Q8_0) KVQ_C(KVQ_Q8_0, KVQ_Q4_0)
-    KVQ_C(KVQ_Q4_0, KVQ_F16) KVQ_C(KVQ_Q4_0, KVQ_Q8_0) KVQ_C(KVQ_Q4_0, KVQ_Q4_0)
-#undef KVQ_C
-    // the merge keeps a [16][D] float buffer and (m_j, l_j) per (split, head)
-    return (bytes - 16 * D * 4) / (8 * G);
-}
-
 }  // namespace
 
-int decode_split_cap(int kt, int vt, int D, int G)
+hipError_t launch_decode(int kt, int vt, int D, const DecodeArgs &a, const MergeArgs &m, int n_pairs, hipStream_t st)
 {
-    int cap = D == 64 ? split_cap_d<64>(kt, vt, G) : D == 128 ? split_cap_d<128>(kt, vt, G) : split_cap_d<256>(kt, vt, G);
-    return cap < KVQ_MAX_SPLITS ? cap : KVQ_MAX_SPLITS;
-}
-
-hipError_t launch_decode(int kt, int vt, int D, const DecodeArgs &a, int n_seqs, hipStream_t st)
-{
+    hipError_t e;
     switch (D) {
-    case 64: return launch_dec_d<64>(kt, vt, a, n_seqs, st);
-    case 128: return launch_dec_d<128>(kt, vt, a, n_seqs, st);
-    case 256: return launch_dec_d<256>(kt, vt, a, n_seqs, st);
+    case 64: e = launch_dec_d<64>(kt, vt, a, st); break;
+    case 128: e = launch_dec_d<128>(kt, vt, a, st); break;
+    case 256: e = launch_dec_d<256>(kt, vt, a, st); break;
     default: return hipErrorInvalidValue;
     }
+    if (e != hipSuccess)
+        return e;
+    hipLaunchKernelGGL(merge_kernel, dim3(n_pairs * m.G), dim3(m.D), 0, st, m);
+    return hipGetLastError();
 }
 
 }  // namespace kvq

@@ -27,18 +27,29 @@ struct AppendArgs {
     int32_t pos[KVQ_MAX_SEQS];
 };
 
+// Decode work split: every (sequence, kv head) pair of sequence s gets k_s
+// waves; wave r of a pair streams its tiles r, r + k_s, ... and writes one
+// partial into slot (its global wave index).  wave_start[s] = first wave of
+// sequence s (n_kv_heads * the k of every earlier sequence); wave_start[n_seqs]
+// = W, the number of waves.
 struct DecodeArgs {
     const uint8_t *kc;
     const uint16_t *ks;
     const uint8_t *vc;
     const uint16_t *vs;
     const uint16_t *q;    // [S][Hq][D]
-    float *out;           // [S][Hq][D]
-    float *ws;            // [S][Hq][n_splits][D+2]: O (unnormalized), m (base-2 units), l
-    uint32_t *counters;   // [S][Hkv] finished-split counters, zero between calls
-    int32_t Hq, Hkv, G, Tc, tps, n_splits;
+    float *ws;            // partial slots [W][G][D+4]: O (unnormalized), m (base 2), l
+    int32_t Hq, Hkv, G, Tc, n_seqs, W;
     float c2;  // scale * log2(e)
     int32_t ctx_len[KVQ_MAX_SEQS];
+    int32_t wave_start[KVQ_MAX_SEQS + 1];
+};
+
+struct MergeArgs {
+    const float *ws;
+    float *out;  // [S][Hq][D]
+    int32_t Hq, Hkv, G, D;
+    int32_t wave_start[KVQ_MAX_SEQS + 1];
 };
 
 struct PrefillArgs {
@@ -56,9 +67,9 @@ struct PrefillArgs {
 
 // Launchers return hipSuccess or the launch error.
 hipError_t launch_append(int k_type, int v_type, const AppendArgs &a, int n_quads, hipStream_t st);
-hipError_t launch_decode(int k_type, int v_type, int D, const DecodeArgs &a, int n_seqs, hipStream_t st);
-// Most context splits the decode kernel can merge for this configuration.
-int decode_split_cap(int k_type, int v_type, int D, int G);
+// The streaming kernel, then the merge kernel (one workgroup per pair).
+hipError_t launch_decode(int k_type, int v_type, int D, const DecodeArgs &a, const MergeArgs &m, int n_pairs,
+                         hipStream_t st);
 hipError_t launch_prefill(int k_type, int v_type, int D, const PrefillArgs &a, hipStream_t st);
 
 }  // namespace kvq

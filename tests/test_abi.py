@@ -138,7 +138,9 @@ def test_decode_rejections(L):
     sh = shape()
     c = make_cache(sh)
     need = kvq.kvq_decode_workspace_bytes(sh)
-    assert need == 256 + 2 * 8 * 4 * 66 * 4  # counters, then 128 tokens of capacity -> at most 4 one-tile splits
+    # 2 seqs x 2 kv heads, 128 tokens of capacity: at most 16 one-tile
+    # waves, one partial slot each of 4 heads x (64 + 4) floats
+    assert need == 16 * 4 * 68 * 4
 
     def call(ctx=(100, 50), ws=FAKE, wsb=need, ns=0, scale=0.125, Q=FAKE, out=FAKE, layer=0):
         return kvq.kvq_attn_decode(c, layer, Q, list(ctx), scale, out, ws, wsb, ns, None)

@@ -142,24 +142,22 @@ def _decode_setup(S=4, Hq=32, Hkv=8, D=128, T=4096, seed=5):
     return cache, K, V, Q
 
 
-def test_decode_fused_merge_is_repeatable():
-    """The last workgroup of each (sequence, kv head) merges the split
-    partials; every call must see complete partials (results bitwise equal
-    across calls, including after calls with other split counts) and must
-    leave the counters at zero."""
+def test_decode_merge_is_repeatable():
+    """Waves write one partial per (sequence, kv head) they touch and the
+    merge kernel combines them in a fixed order: results are bitwise equal
+    across calls, also interleaved with calls that split the work
+    differently."""
     import torch
 
-    print("decode fused-merge repeatability", flush=True)
+    print("decode merge repeatability", flush=True)
     cache, K, V, Q = _decode_setup()
     ctx = [4096, 4000, 3001, 77]
-    ref = {ns: cache.decode(0, Q, ctx, 0.0883883, n_splits=ns).clone() for ns in (32, 7, 128)}
+    ref = {ns: cache.decode(0, Q, ctx, 0.0883883, n_splits=ns).clone() for ns in (32, 7, 128, 0)}
     for it in range(30):
-        for ns in (32, 7, 128):
+        for ns in (32, 7, 128, 0):
             out = cache.decode(0, Q, ctx, 0.0883883, n_splits=ns)
             assert torch.equal(out, ref[ns]), f"call {it} splits {ns} differs"
     torch.cuda.synchronize()
-    counters = cache.workspace()[:4 * 8].view(torch.int32)
-    assert int(counters.abs().sum()) == 0
 
 
 def test_decode_graph_replay_matches_eager():

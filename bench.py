@@ -9,9 +9,11 @@ context, batch 16, K q8_0 / V q4_0 -- on seeded synthetic inputs that are
 resident in HBM before the timed region starts.
 
 Prints ONE JSON line.  `value` = algorithmic KV bytes per step / step time
-(GB/s); `roofline` covers the decode kernel, timed with HIP events on the
-stream it runs on; `cpu_baseline` times the CPU oracle on a bounded sample of
-the same workload on this host.
+(GB/s); `roofline` covers the decode call (streaming kernel + merge kernel),
+timed with HIP events on the stream it runs on; `cpu_baseline` times the CPU
+oracle on a bounded sample of the same workload on this host; `prefill`
+times the causal chunked prefill (512 queries per sequence at the end of a
+131072-token K4V4 cache, one layer) against the dense binary16 MFMA peak.
 
     python bench.py [--steps K] [--warmup W] [--gpus 1]
 """
@@ -43,6 +45,9 @@ def parse():
     p.add_argument("--splits", type=int, default=0, help="decode splits per (seq, kv head); 0 = automatic")
     p.add_argument("--graph", action="store_true", help="replay each step from a captured HIP graph")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-prefill", action="store_true", help="skip the prefill measurement")
+    p.add_argument("--prefill-only", action="store_true",
+                   help="measure only the chunked prefill (prints a JSON line with the `prefill` object)")
     p.add_argument("--cpu-seconds", type=float, default=10.0)
     p.add_argument("--calib-copy", action="store_true",
                    help="after timing, run three plain 1 GiB device-to-device copies (a reference for "
@@ -58,10 +63,11 @@ def kv_bytes_per_layer(w, kt, vt):
 
 
 def traffic_from_profile(src_hash, workload):
-    """Measured HBM bytes per decode launch from the committed counter summary
-    (FETCH_SIZE and WRITE_SIZE scaled by a plain copy of known size), or None
-    when the decode kernel source changed since the counters were taken."""
-    path = os.path.join(ROOT, "profiles", f"decode_kernel_{workload}.txt")
+    """Measured HBM bytes per decode call (both kernels) from the committed
+    counter summary (FETCH_SIZE and WRITE_SIZE scaled by a plain copy of known
+    size), or None when the decode source changed since the counters were
+    taken."""
+    path = os.path.join(ROOT, "profiles", f"decode_merge_kernels_{workload}.txt")
     rec = {}
     try:
         for line in open(path):
@@ -73,6 +79,54 @@ def traffic_from_profile(src_hash, workload):
     if rec.get("decode_kernel_source_sha256") != src_hash or "hbm_bytes_per_launch" not in rec:
         return None
     return int(rec["hbm_bytes_per_launch"])
+
+
+MFMA_F16_PEAK_TFLOPS = 2500.0  # dense binary16 matrix peak
+
+
+def prefill_measure(dev, calls=5):
+    """Causal chunked prefill on one layer of the long-context workload: the
+    last 512-query chunk of each of 4 sequences over 131072 K4V4 positions.
+    Algorithmic flop = 4 * head_dim * n_q_heads * (visible keys summed over
+    the chunk's queries) per sequence (Q.K and P.V, multiply-add = 2)."""
+    import torch
+
+    import mixed_precision_quantized_quantize_amd as kvq
+    from mixed_precision_quantized_quantize_amd import synth
+
+    w = synth.WORKLOADS["llama3_8b_128k_prefill"]
+    kt, vt = w.type_pairs[0]
+    n_tok, T, S = w.prefill, w.ctx, w.batch
+    cache = kvq.KVCache(1, S, w.n_q_heads, w.n_kv_heads, w.head_dim, T, (kt, vt), device=dev)
+    for c0 in range(0, T, synth.CHUNK):
+        K, V = synth.kv_batch(w, 0, c0, min(synth.CHUNK, T - c0), device=dev)
+        cache.append(0, K, V, [c0] * S)
+        del K, V
+    Q = synth.queries(w, 0, n_tok=n_tok, device=dev)
+    out = torch.empty(tuple(Q.shape), dtype=torch.float32, device=dev)
+    p0 = [T - n_tok] * S
+    stream = torch.cuda.current_stream(dev)
+    for _ in range(2):
+        cache.prefill(0, Q, p0, w.scale, out=out)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(calls):
+        cache.prefill(0, Q, p0, w.scale, out=out)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / calls
+    keys = sum(T - n_tok + i + 1 for i in range(n_tok))
+    flop = 4.0 * w.head_dim * w.n_q_heads * keys * S
+    tflops = flop / (ms * 1e-3) / 1e12
+    del cache, Q, out
+    torch.cuda.empty_cache()
+    return {
+        "workload": w.name, "layer": 0, "batch": S, "n_tok": n_tok, "q_pos0": T - n_tok, "ctx": T,
+        "k_type": kt, "v_type": vt, "ms_per_call": round(ms, 4), "alg_flop_per_call": flop,
+        "roofline": {"bound": "mfma", "kernel": "prefill_kernel, one layer", "achieved": round(tflops, 1),
+                     "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(tflops / MFMA_F16_PEAK_TFLOPS, 4)},
+    }
 
 
 def cpu_baseline(w, kt, vt, layer_kv, q_bits, seconds):
@@ -129,6 +183,9 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
     kvq.lib()  # fail loudly if the HIP library is missing
+    if args.prefill_only:
+        print(json.dumps({"prefill": prefill_measure(torch.device("cuda:0"))}), flush=True)
+        return
     w = synth.WORKLOADS[args.workload]
     kt, vt = w.type_pairs[0]
     L, S, T = w.n_layers, w.batch, w.ctx
@@ -246,7 +303,7 @@ def main():
         "kv_bytes_per_step": kv_step,
         "roofline": {
             "bound": "hbm",
-            "kernel": "decode_kernel (split-K flash decode with the merge folded in), one layer",
+            "kernel": "kvq_attn_decode call (decode_kernel streaming the tiles + merge_kernel), one layer",
             "achieved": round(achieved, 2),
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",
@@ -256,6 +313,7 @@ def main():
             "avg_launch_ms": round(dec_avg_ms, 5),
         },
         "cpu_baseline": None,
+        "prefill": None,
     }
     log(f"step {ms_step:.3f} ms, {value:.1f} GB/s ({100 * value / HBM_PEAK_GBPS:.1f}% of peak), "
         f"decode call {dec_avg_ms * 1e3:.1f} us -> {achieved:.1f} GB/s")
@@ -268,9 +326,13 @@ def main():
         torch.cuda.synchronize()
         del x, y
 
-    if not args.no_cpu_baseline and layer0 is not None:
+    if not args.no_cpu_baseline or not args.no_prefill:
         del cache
         torch.cuda.empty_cache()
+    if not args.no_prefill:
+        log("timing the chunked prefill ...")
+        result["prefill"] = prefill_measure(dev)
+    if not args.no_cpu_baseline and layer0 is not None:
         from mixed_precision_quantized_quantize_amd.synth import as_bits
 
         K0 = as_bits(torch.cat(layer0[0], dim=1))

@@ -1,0 +1,58 @@
+"""Key-versus-value sensitivity on synthetic caches (oracle only, binary64).
+
+The KVSplit page's central finding ("Wissenschaftliche Einsichten und
+Versuchsergebnisse") is that keys are more sensitive to quantization than
+values, so spending the bits on K (K8V4) beats the reverse (K4V8).  Without
+model weights this can only be reproduced in direction: the attention output
+of every K/V type pair is compared with unquantized (f16/f16) attention on the
+same seeded inputs, for the two synthetic key distributions the workloads use
+(TinyLlama-shaped outlier channels; Student-t keys with per-channel scales).
+The numbers are a report; the asserted part is the ordering the page states.
+Run with -s to see the table."""
+import itertools
+
+import numpy as np
+
+import oracle
+from mixed_precision_quantized_quantize_amd import synth
+
+TYPES = ["f16", "q8_0", "q4_0"]
+
+
+def rel_errors(wname, n_tok, n_seqs):
+    w = synth.WORKLOADS[wname]
+    K, V = synth.kv_batch(w, 0, 0, n_tok, device="cpu", seqs=range(n_seqs))
+    Q = synth.queries(w, 0, device="cpu")[:n_seqs].contiguous()
+    Kb, Vb, Qb = synth.as_bits(K), synth.as_bits(V), synth.as_bits(Q)
+    ctx = np.full(n_seqs, n_tok, np.int32)
+    outs = {}
+    for kt, vt in itertools.product(TYPES, repeat=2):
+        orc = oracle.OracleLayer(kt, vt, n_seqs, w.n_q_heads, w.n_kv_heads, w.head_dim, n_tok)
+        orc.append(Kb, Vb, np.zeros(n_seqs, np.int32))
+        outs[(kt, vt)] = orc.attn_decode(Qb, ctx, w.scale)
+    ref = outs[("f16", "f16")]
+    return {p: float(np.linalg.norm(o - ref) / np.linalg.norm(ref)) for p, o in outs.items()}
+
+
+def check_ordering(err, what):
+    rows = "\n".join(f"  K {kt:5s} V {vt:5s}  rel. RMS error {err[(kt, vt)]:.3e}"
+                     for kt, vt in itertools.product(TYPES, repeat=2))
+    print(f"\n{what}\n{rows}")
+    assert err[("f16", "f16")] == 0.0
+    # keys are the sensitive half: the same bits spent on K lose less
+    assert err[("q8_0", "q4_0")] < err[("q4_0", "q8_0")], what
+    assert err[("f16", "q4_0")] < err[("q4_0", "f16")], what
+    assert err[("f16", "q8_0")] < err[("q8_0", "f16")], what
+    # and more bits on either side lose less
+    assert err[("q8_0", "q8_0")] < err[("q8_0", "q4_0")] < err[("q4_0", "q4_0")], what
+    assert err[("q8_0", "q8_0")] < err[("q4_0", "q8_0")], what
+
+
+def test_keys_more_sensitive_outlier_channels():
+    # TinyLlama-shaped: 32 query / 4 kv heads, head_dim 64, 4 outlier channels x8 per kv head
+    check_ordering(rel_errors("tinyllama_8k", 2048, 1), "tinyllama_8k inputs, 2048 tokens")
+
+
+def test_keys_more_sensitive_student_t_keys():
+    # Llama-3-8B-shaped: 32 / 8 heads, head_dim 128, Student-t keys x per-channel U(0.5, 8)
+    check_ordering(rel_errors("llama3_8b_32k", 2048, 2), "llama3_8b_32k inputs, 2048 tokens, 2 sequences")

@@ -292,7 +292,8 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f16 MFMA, f32 accumulate; q8_0 K / q4_0 V storage",
+        "dtype": "f16",
+        "dtype_note": "binary16 MFMA inputs with float32 accumulation and softmax; the cache stores q8_0 keys and q4_0 values",
         "data": "synthetic (seeded: K Student-t nu=4 x per-channel U(0.5,8), V and Q N(0,1), binary16)",
         "config": {"workload": w.name, "layers": L, "batch": S, "ctx": T, "q_heads": w.n_q_heads,
                    "kv_heads": w.n_kv_heads, "head_dim": w.head_dim, "k_type": kt, "v_type": vt,

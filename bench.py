@@ -1,15 +1,17 @@
 #!/usr/bin/env python3
 """Decode-attention benchmark over the mixed-precision quantized KV cache.
 
-One step = for every layer: quantize-append the new token's K/V row for
-every sequence (kvq_append), then flash-decode every sequence's query over
-the whole cache (kvq_attn_decode).  Default workload: the Llama-3-8B-shaped
+One step = for every layer: quantize the new token's K/V row of every
+sequence into the cache and flash-decode every sequence's query over the
+whole cache, both in one kvq_attn_decode_append call (--unfused: kvq_append
+then kvq_attn_decode, the same work in two calls).  Default workload: the Llama-3-8B-shaped
 decode -- 32 layers, 32 query / 8 kv heads, head_dim 128, 32768-token
 context, batch 16, K q8_0 / V q4_0 -- on seeded synthetic inputs that are
 resident in HBM before the timed region starts.
 
 Prints ONE JSON line.  `value` = algorithmic KV bytes per step / step time
 (GB/s); `roofline` covers the decode call (streaming kernel + merge kernel),
+(kvq_attn_decode_append: append + streaming kernel, then merge kernel)
 timed with HIP events on the stream it runs on; `cpu_baseline` times the CPU
 oracle on a bounded sample of the same workload on this host; `prefill`
 times the causal chunked prefill (512 queries per sequence at the end of a
@@ -44,6 +46,8 @@ def parse():
     p.add_argument("--workload", default="llama3_8b_32k")
     p.add_argument("--splits", type=int, default=0, help="decode splits per (seq, kv head); 0 = automatic")
     p.add_argument("--graph", action="store_true", help="replay each step from a captured HIP graph")
+    p.add_argument("--unfused", action="store_true",
+                   help="append with kvq_append, then decode with kvq_attn_decode (two calls per layer)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-prefill", action="store_true", help="skip the prefill measurement")
     p.add_argument("--prefill-only", action="store_true",
@@ -60,6 +64,12 @@ def kv_bytes_per_layer(w, kt, vt):
 
     sh = kvq.kvq_shape(1, w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim, w.ctx)
     return sum(kvq.kvq_plane_bytes(sh, kt)) + sum(kvq.kvq_plane_bytes(sh, vt))
+
+
+def row_bytes(w, t):
+    """Bytes of one cached row (one position, one kv head) of type t."""
+    return {"f16": 2 * w.head_dim, "q8_0": w.head_dim + w.head_dim // 16,
+            "q4_0": w.head_dim // 2 + w.head_dim // 16}[t]
 
 
 def traffic_from_profile(src_hash, workload):
@@ -210,7 +220,7 @@ def main():
     torch.cuda.synchronize()
     log(f"cache filled: {L} layers x {kv_bytes_per_layer(w, kt, vt) / 2**20:.1f} MiB in {time.perf_counter() - t0:.1f} s")
 
-    Knew, Vnew, Qs = [], [], []
+    Knew, Vnew, Qs = [], [], []  # new rows [S][1][Hkv][D]
     for l in range(L):
         K, V = synth.kv_batch(w, l, T - 1, 1, device=dev, step=0)
         Knew.append(K)
@@ -222,14 +232,18 @@ def main():
     stream = torch.cuda.current_stream(dev)
 
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(L)]
-    dec_ms = []
 
     def step(timed):
         for l in range(L):
-            cache.append(l, Knew[l], Vnew[l], pos)
+            if args.unfused:
+                cache.append(l, Knew[l], Vnew[l], pos)
             if timed:
                 ev[l][0].record(stream)
-            cache.decode(l, Qs[l], ctx, w.scale, out=out[l], n_splits=args.splits)
+            if args.unfused:
+                cache.decode(l, Qs[l], ctx, w.scale, out=out[l], n_splits=args.splits)
+            else:
+                cache.decode_append(l, Knew[l][:, 0], Vnew[l][:, 0], Qs[l], ctx, w.scale, out=out[l],
+                                    n_splits=args.splits)
             if timed:
                 ev[l][1].record(stream)
 
@@ -242,39 +256,47 @@ def main():
             step(False)
         torch.cuda.synchronize()
 
-    def run(timed):
+    def run():
         if graph is not None:
             graph.replay()
         else:
-            step(timed)
+            step(False)
 
     for _ in range(args.warmup):
-        run(False)
+        run()
     torch.cuda.synchronize()
+    # The timed region holds the K steps and nothing else: timing events
+    # between the layers' calls would cost several microseconds each.
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     start.record(stream)
     for _ in range(args.steps):
-        run(True)
-        if graph is None:
-            # per-launch durations of the decode call, collected without
-            # stalling the queue (events are read after the step drains)
-            pass
+        run()
     end.record(stream)
     torch.cuda.synchronize()
     ms_total = start.elapsed_time(end)
     ms_step = ms_total / args.steps
 
-    # decode-call durations of the last timed step (graph mode: one extra eager step)
-    if graph is not None:
+    if args.unfused:
+        # the step also holds append launches: bracket each decode call with
+        # events in one extra step after the timed region
         step(True)
         torch.cuda.synchronize()
-    dec_ms = [ev[l][0].elapsed_time(ev[l][1]) for l in range(L)]
-    dec_avg_ms = sum(dec_ms) / len(dec_ms)
+        dec_avg_ms = sum(ev[l][0].elapsed_time(ev[l][1]) for l in range(L)) / L
+        call_timing = "HIP events around each kvq_attn_decode call of one extra step (events add a few us)"
+    else:
+        # a step is exactly L back-to-back kvq_attn_decode_append calls on
+        # `stream`: the timed region's events give their average duration
+        # (gaps between calls included)
+        dec_avg_ms = ms_step / L
+        call_timing = "HIP events around the timed region / (steps x layers); gaps between calls included"
 
     kv_layer = kv_bytes_per_layer(w, kt, vt)
     q_bytes = S * w.n_q_heads * w.head_dim * 2
     o_bytes = S * w.n_q_heads * w.head_dim * 4
-    alg_bytes_launch = kv_layer + q_bytes + o_bytes
+    # the fused call also reads the new binary16 rows and writes their codes
+    new_bytes = 0 if args.unfused else (S * w.n_kv_heads * w.head_dim * 2 * 2 +
+                                        S * w.n_kv_heads * (row_bytes(w, kt) + row_bytes(w, vt)))
+    alg_bytes_launch = kv_layer + q_bytes + o_bytes + new_bytes
     kv_step = kv_layer * L
     value = kv_step / (ms_step * 1e-3) / 1e9
     achieved = alg_bytes_launch / (dec_avg_ms * 1e-3) / 1e9
@@ -297,14 +319,18 @@ def main():
         "data": "synthetic (seeded: K Student-t nu=4 x per-channel U(0.5,8), V and Q N(0,1), binary16)",
         "config": {"workload": w.name, "layers": L, "batch": S, "ctx": T, "q_heads": w.n_q_heads,
                    "kv_heads": w.n_kv_heads, "head_dim": w.head_dim, "k_type": kt, "v_type": vt,
-                   "splits": args.splits or "auto", "graph": bool(graph is not None)},
+                   "splits": args.splits or "auto", "graph": bool(graph is not None),
+                   "append": "separate kvq_append" if args.unfused else "fused into the decode call"},
         "pct_hbm_peak": round(100 * value / HBM_PEAK_GBPS, 2),
         "tok_per_s": round(S / (ms_step * 1e-3), 1),
         "tok_per_s_note": "attention-only: append + decode of all layers, no projections or MLP",
         "kv_bytes_per_step": kv_step,
         "roofline": {
             "bound": "hbm",
-            "kernel": "kvq_attn_decode call (decode_kernel streaming the tiles + merge_kernel), one layer",
+            "kernel": ("kvq_attn_decode call (decode_kernel streaming the tiles + merge_kernel), one layer"
+                       if args.unfused else
+                       "kvq_attn_decode_append call (decode_kernel: row append + streaming the tiles; "
+                       "merge_kernel), one layer"),
             "achieved": round(achieved, 2),
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",
@@ -312,6 +338,7 @@ def main():
             "traffic": traffic,
             "alg_bytes_per_launch": alg_bytes_launch,
             "avg_launch_ms": round(dec_avg_ms, 5),
+            "avg_launch_timing": call_timing,
         },
         "cpu_baseline": None,
         "prefill": None,

@@ -145,15 +145,16 @@ int kvq_cache_check(const kvq_cache *cache);
 int kvq_append(const kvq_cache *cache, int32_t layer, const void *K, const void *V, int32_t n_new,
                const int32_t *pos, int32_t k_type, int32_t v_type, void *stream);
 
-/* Workspace bytes that kvq_attn_decode needs for any ctx_len <= max_ctx and
- * any n_splits: (W + n_seqs*n_kv_heads) partial slots of
- * (n_q_heads/n_kv_heads) * (head_dim+4) floats, W being the most waves a call
- * can use (see kvq_attn_decode).  No initialization is needed.  A workspace
- * serves one call at a time: calls that overlap in time (other streams)
- * need workspaces of their own. */
+/* Workspace bytes that kvq_attn_decode (and kvq_attn_decode_append) need for
+ * any ctx_len <= max_ctx and any n_splits: one partial slot of
+ * (n_q_heads/n_kv_heads) * (head_dim+4) floats per wave, for the most waves
+ * a call can use (see kvq_attn_decode).  No initialization is needed.  A
+ * workspace serves one call at a time: calls that overlap in time (other
+ * streams) need workspaces of their own. */
 int kvq_decode_workspace_bytes(const kvq_shape *shape, size_t *bytes);
 
-/* Flash-decode one query token per sequence over layer `layer`.
+/* Flash-decode one query token per sequence over layer `layer` (the
+ * split-K flash decoding the llama.cpp guide runs on the quantized cache).
  *   Q       : device binary16 [n_seqs][n_q_heads][head_dim]
  *   ctx_len : host int32 [n_seqs], 1 <= ctx_len[s] <= max_ctx; query s
  *             attends to cache positions 0 .. ctx_len[s]-1 (append the new
@@ -161,19 +162,34 @@ int kvq_decode_workspace_bytes(const kvq_shape *shape, size_t *bytes);
  *   scale   : multiplies Q.K (typically 1/sqrt(head_dim)), used as passed
  *   out     : device float32 [n_seqs][n_q_heads][head_dim]
  *   workspace, workspace_bytes: device scratch for the partials
- *   n_splits: about how many pieces the context of one (sequence, kv head)
- *             is cut into; 0 chooses (fill the device).  The call never uses
- *             more waves than the cache has 32-token tiles in use.
- * Query head hq reads kv head hq / (n_q_heads/n_kv_heads).  Two launches.
- * The first streams the 32-token tiles of all (sequence, kv head) pairs, one
- * pair after the other, cut into W equal contiguous pieces, one per wave
- * (W = n_splits * n_seqs * n_kv_heads, or the automatic choice); a wave
- * writes a (max, sum, unnormalized output) partial for every pair its piece
- * touches.  The second merges the partials of each pair (log-sum-exp) into
- * `out`.  Errors: KVQ_E_RANGE (ctx_len, n_splits > KVQ_MAX_SPLITS),
- * KVQ_E_WORKSPACE, KVQ_E_SHAPE (2^31 or more tiles in use). */
+ *   n_splits: how many waves share the context of one (sequence, kv head)
+ *             pair; 0 chooses (about four waves per compute unit over the
+ *             whole batch, shared in proportion to each sequence's context,
+ *             at least four tiles per wave).  Never more than the pair's
+ *             32-token tiles.
+ * Query head hq reads kv head hq / (n_q_heads/n_kv_heads).  Two launches on
+ * `stream`.  In the first, the k waves of a pair take its tiles round robin
+ * (wave r: tiles r, r+k, ...), and each writes one (max, sum, unnormalized
+ * output) partial.  The second merges the k partials of every pair and
+ * query head (log-sum-exp) into `out`.  Errors: KVQ_E_RANGE (ctx_len,
+ * n_splits > KVQ_MAX_SPLITS), KVQ_E_WORKSPACE, KVQ_E_SHAPE (2^25 or more
+ * waves). */
 int kvq_attn_decode(const kvq_cache *cache, int32_t layer, const void *Q, const int32_t *ctx_len, float scale,
                     float *out, void *workspace, size_t workspace_bytes, int32_t n_splits, void *stream);
+
+/* One decode step of layer `layer` with the new token's append folded in:
+ * quantizes K[s], V[s] into position ctx_len[s]-1 and then attends as
+ * kvq_attn_decode does.  The planes and `out` come out bit-identical to
+ * kvq_append(n_new = 1, pos[s] = ctx_len[s]-1) followed by kvq_attn_decode
+ * with the same arguments (same quantizer, same work split), with one launch
+ * fewer: the wave that reads a pair's last tile writes the row before it
+ * copies that tile.
+ *   K, V : device binary16 [n_seqs][n_kv_heads][head_dim], 16-byte aligned
+ * Other arguments and errors as kvq_attn_decode.  The rows of K and V must
+ * not overlap the cache planes. */
+int kvq_attn_decode_append(const kvq_cache *cache, int32_t layer, const void *K, const void *V, const void *Q,
+                           const int32_t *ctx_len, float scale, float *out, void *workspace,
+                           size_t workspace_bytes, int32_t n_splits, void *stream);
 
 /* Causal attention for a chunk of n_tok queries per sequence whose K/V rows
  * are already appended at positions q_pos0[s] .. q_pos0[s]+n_tok-1 (the

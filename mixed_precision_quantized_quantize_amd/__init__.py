@@ -25,7 +25,7 @@ KVQ_OK, KVQ_E_ARG, KVQ_E_TYPE, KVQ_E_SHAPE, KVQ_E_RANGE, KVQ_E_WORKSPACE, KVQ_E_
 KVQ_MAX_SEQS, KVQ_MAX_GROUP, KVQ_MAX_SPLITS = 256, 16, 256
 
 EXPORTS = ["kvq_strerror", "kvq_plane_bytes", "kvq_cache_check", "kvq_append", "kvq_decode_workspace_bytes",
-           "kvq_attn_decode", "kvq_attn_prefill_chunk"]
+           "kvq_attn_decode", "kvq_attn_decode_append", "kvq_attn_prefill_chunk"]
 
 
 class KvqLibraryMissing(RuntimeError):
@@ -74,6 +74,8 @@ def lib():
             L.kvq_decode_workspace_bytes.argtypes = [P(kvq_shape), P(sz)]
             L.kvq_attn_decode.argtypes = [P(kvq_cache), i32, vp, P(ctypes.c_int32), ctypes.c_float, vp, vp, sz,
                                           i32, vp]
+            L.kvq_attn_decode_append.argtypes = [P(kvq_cache), i32, vp, vp, vp, P(ctypes.c_int32), ctypes.c_float,
+                                                 vp, vp, sz, i32, vp]
             L.kvq_attn_prefill_chunk.argtypes = [P(kvq_cache), i32, vp, i32, P(ctypes.c_int32), ctypes.c_float,
                                                  vp, vp]
             for name in EXPORTS:
@@ -132,6 +134,12 @@ def kvq_attn_decode(cache: kvq_cache, layer: int, Q_ptr: int, ctx_len, scale: fl
                                  ws_ptr, int(ws_bytes), int(n_splits), stream)
 
 
+def kvq_attn_decode_append(cache: kvq_cache, layer: int, K_ptr: int, V_ptr: int, Q_ptr: int, ctx_len,
+                           scale: float, out_ptr: int, ws_ptr: int, ws_bytes: int, n_splits: int, stream: int) -> int:
+    return lib().kvq_attn_decode_append(ctypes.byref(cache), int(layer), K_ptr, V_ptr, Q_ptr, _i32_array(ctx_len),
+                                        float(scale), out_ptr, ws_ptr, int(ws_bytes), int(n_splits), stream)
+
+
 def kvq_attn_prefill_chunk(cache: kvq_cache, layer: int, Q_ptr: int, n_tok: int, q_pos0, scale: float,
                            out_ptr: int, stream: int) -> int:
     return lib().kvq_attn_prefill_chunk(ctypes.byref(cache), int(layer), Q_ptr, int(n_tok), _i32_array(q_pos0),
@@ -188,16 +196,32 @@ class KVCache:
             self._ws = self.torch.empty(max(nb, 16) // 4, dtype=self.torch.float32, device=self.device)
         return self._ws
 
-    def decode(self, layer, Q, ctx_len, scale, out=None, n_splits=0):
-        """Q: binary16 [S][Hq][D] -> float32 [S][Hq][D]."""
+    def _decode_args(self, Q, out):
         sh = self.shape
         assert Q.dtype == self.torch.float16 and Q.is_contiguous()
         assert tuple(Q.shape) == (sh.n_seqs, sh.n_q_heads, sh.head_dim)
         if out is None:
             out = self.torch.empty(tuple(Q.shape), dtype=self.torch.float32, device=self.device)
-        ws = self.workspace()
+        return out, self.workspace()
+
+    def decode(self, layer, Q, ctx_len, scale, out=None, n_splits=0):
+        """Q: binary16 [S][Hq][D] -> float32 [S][Hq][D]."""
+        out, ws = self._decode_args(Q, out)
         _check(kvq_attn_decode(self.desc, layer, Q.data_ptr(), ctx_len, scale, out.data_ptr(), ws.data_ptr(),
                                ws.numel() * 4, n_splits, self._stream()), "kvq_attn_decode")
+        return out
+
+    def decode_append(self, layer, K, V, Q, ctx_len, scale, out=None, n_splits=0):
+        """Writes K, V (binary16 [S][Hkv][D]) at positions ctx_len[s]-1, then
+        decodes Q: binary16 [S][Hq][D] -> float32 [S][Hq][D]."""
+        sh = self.shape
+        for x in (K, V):
+            assert x.dtype == self.torch.float16 and x.is_contiguous()
+            assert tuple(x.shape) == (sh.n_seqs, sh.n_kv_heads, sh.head_dim)
+        out, ws = self._decode_args(Q, out)
+        _check(kvq_attn_decode_append(self.desc, layer, K.data_ptr(), V.data_ptr(), Q.data_ptr(), ctx_len, scale,
+                                      out.data_ptr(), ws.data_ptr(), ws.numel() * 4, n_splits, self._stream()),
+               "kvq_attn_decode_append")
         return out
 
     def prefill(self, layer, Q, q_pos0, scale, out=None):

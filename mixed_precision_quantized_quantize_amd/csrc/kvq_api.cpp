@@ -219,8 +219,13 @@ int kvq_decode_workspace_bytes(const kvq_shape *shape, size_t *bytes)
     return KVQ_OK;
 }
 
-int kvq_attn_decode(const kvq_cache *cache, int32_t layer, const void *Q, const int32_t *ctx_len, float scale,
-                    float *out, void *workspace, size_t workspace_bytes, int32_t n_splits, void *stream)
+}  // extern "C"
+
+namespace {
+
+int attn_decode(const kvq_cache *cache, int32_t layer, const void *K, const void *V, const void *Q,
+                const int32_t *ctx_len, float scale, float *out, void *workspace, size_t workspace_bytes,
+                int32_t n_splits, void *stream)
 {
     int rc = check_layer(cache, layer);
     if (rc)
@@ -251,6 +256,8 @@ int kvq_attn_decode(const kvq_cache *cache, int32_t layer, const void *Q, const 
     a.vc = (const uint8_t *)vp.codes;
     a.vs = (const uint16_t *)vp.scales;
     a.q = (const uint16_t *)Q;
+    a.knew = (const uint16_t *)K;
+    a.vnew = (const uint16_t *)V;
     a.ws = (float *)workspace;
     a.Hq = sh.n_q_heads;
     a.Hkv = sh.n_kv_heads;
@@ -270,6 +277,26 @@ int kvq_attn_decode(const kvq_cache *cache, int32_t layer, const void *Q, const 
     memcpy(m.wave_start, a.wave_start, sizeof(int32_t) * (sh.n_seqs + 1));
     hipError_t e = launch_decode(kp.type, vp.type, sh.head_dim, a, m, sh.n_seqs * sh.n_kv_heads, (hipStream_t)stream);
     return e == hipSuccess ? KVQ_OK : KVQ_E_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+int kvq_attn_decode(const kvq_cache *cache, int32_t layer, const void *Q, const int32_t *ctx_len, float scale,
+                    float *out, void *workspace, size_t workspace_bytes, int32_t n_splits, void *stream)
+{
+    return attn_decode(cache, layer, nullptr, nullptr, Q, ctx_len, scale, out, workspace, workspace_bytes, n_splits,
+                       stream);
+}
+
+int kvq_attn_decode_append(const kvq_cache *cache, int32_t layer, const void *K, const void *V, const void *Q,
+                           const int32_t *ctx_len, float scale, float *out, void *workspace,
+                           size_t workspace_bytes, int32_t n_splits, void *stream)
+{
+    if (!K || !V || !aligned16(K) || !aligned16(V))
+        return KVQ_E_ARG;
+    return attn_decode(cache, layer, K, V, Q, ctx_len, scale, out, workspace, workspace_bytes, n_splits, stream);
 }
 
 int kvq_attn_prefill_chunk(const kvq_cache *cache, int32_t layer, const void *Q, int32_t n_tok,

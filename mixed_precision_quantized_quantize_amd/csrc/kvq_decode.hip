@@ -31,6 +31,7 @@
 #include <type_traits>
 
 #include "kvq_device.h"
+#include "kvq_quant.h"
 
 namespace kvq {
 namespace {
@@ -77,6 +78,26 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(D <=
     const int nt = (ctx + TILE - 1) / TILE;
     const int n_mine = (nt - r + k - 1) / k;  // tiles r, r+k, ... below nt (>= 1)
     const int64_t pair = (int64_t)s * Hkv + h;
+
+    // Fused one-row append: the wave that reads the pair's last tile first
+    // quantizes the new row into position ctx-1 (one quad of lanes per
+    // 32-element block, K blocks then V blocks, the append kernel's
+    // quantizer), and waits until the stores are performed before any copy
+    // of that tile is issued.  No other wave reads that tile.
+    if (a.knew != nullptr && r == (nt - 1) % k) {
+        const int quad = lane >> 2, q = lane & 3;
+        if (quad < 2 * NB) {
+            const int role = quad >= NB, b = quad - role * NB;
+            const uint16_t *blk = (role ? a.vnew : a.knew) + pair * D + 32 * b;
+            if (role == 0)
+                quant::quant_store<KT, 0>(blk, q, const_cast<uint8_t *>(a.kc), const_cast<uint16_t *>(a.ks), pair,
+                                          ctx - 1, b, D, a.Tc);
+            else
+                quant::quant_store<VT, 1>(blk, q, const_cast<uint8_t *>(a.vc), const_cast<uint16_t *>(a.vs), pair,
+                                          ctx - 1, b, D, a.Tc);
+        }
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    }
 
     PairRsrc rs;
     rs.kc = make_rsrc(a.kc + pair * Tc * g::RK, Tc * g::RK);

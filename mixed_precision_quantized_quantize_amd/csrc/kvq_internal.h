@@ -38,6 +38,8 @@ struct DecodeArgs {
     const uint8_t *vc;
     const uint16_t *vs;
     const uint16_t *q;    // [S][Hq][D]
+    const uint16_t *knew, *vnew;  // NULL, or the new row of every sequence, binary16 [S][Hkv][D],
+                                  // to quantize into position ctx_len[s] - 1 first
     float *ws;            // partial slots [W][G][D+4]: O (unnormalized), m (base 2), l
     int32_t Hq, Hkv, G, Tc, n_seqs, W;
     float c2;  // scale * log2(e)

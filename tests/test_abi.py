@@ -157,6 +157,26 @@ def test_decode_rejections(L):
     assert call(layer=5) == kvq.KVQ_E_RANGE
 
 
+def test_decode_append_rejections(L):
+    sh = shape()
+    c = make_cache(sh)
+    need = kvq.kvq_decode_workspace_bytes(sh)
+
+    def call(K=FAKE, V=FAKE, ctx=(100, 50), ws=FAKE, wsb=need, ns=0, Q=FAKE, layer=1):
+        return kvq.kvq_attn_decode_append(c, layer, K, V, Q, list(ctx), 0.125, FAKE, ws, wsb, ns, None)
+
+    assert call(K=None) == kvq.KVQ_E_ARG
+    assert call(V=None) == kvq.KVQ_E_ARG
+    assert call(K=FAKE + 8) == kvq.KVQ_E_ARG
+    assert call(V=FAKE + 2) == kvq.KVQ_E_ARG
+    assert call(ctx=(0, 5)) == kvq.KVQ_E_RANGE  # no position ctx-1 to write
+    assert call(ctx=(101, 5)) == kvq.KVQ_E_RANGE
+    assert call(wsb=16) == kvq.KVQ_E_WORKSPACE
+    assert call(ns=257) == kvq.KVQ_E_RANGE
+    assert call(Q=None) == kvq.KVQ_E_ARG
+    assert call(layer=2) == kvq.KVQ_E_RANGE
+
+
 def test_prefill_rejections(L):
     sh = shape()
     c = make_cache(sh)

@@ -359,16 +359,16 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(D <=
         read_ops(buf, op);
         if (i + DIST < n_mine) {
             asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // LDS reads done before it is refilled
-            issue_tile<KT, VT, D>(buf, (r + (i + DIST) * k) * TILE, lane, doff, rs);
+            issue_tile<KT, VT, D, CPOL_STREAM>(buf, (r + (i + DIST) * k) * TILE, lane, doff, rs);
         }
         process(op, (r + i * k) * TILE, ctx);
     };
     uint8_t *buf_a = lds_a + wave * g::BYTES;
-    issue_tile<KT, VT, D>(buf_a, r * TILE, lane, doff, rs);
+    issue_tile<KT, VT, D, CPOL_STREAM>(buf_a, r * TILE, lane, doff, rs);
     if constexpr (DB) {
         uint8_t *buf_b = lds_b + wave * g::BYTES;
         if (n_mine > 1)
-            issue_tile<KT, VT, D>(buf_b, (r + k) * TILE, lane, doff, rs);
+            issue_tile<KT, VT, D, CPOL_STREAM>(buf_b, (r + k) * TILE, lane, doff, rs);
         int i = 0;
         for (; i + 1 < n_mine; i += 2) {
             step(buf_a, std::integral_constant<int, 2>(), i);

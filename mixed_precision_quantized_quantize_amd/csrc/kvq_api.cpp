@@ -100,8 +100,10 @@ int device_cus()
     return cached[dev];
 }
 
-// Fills wave_start[0..n_seqs] and returns the wave count W.
-int64_t decode_plan(const kvq_shape &sh, const int32_t *ctx_len, int32_t req, int32_t *wave_start)
+// Fills wave_start[0..n_seqs] and returns the wave count W; *k_uniform is
+// the waves per pair when all sequences have the same number, else 0.
+int64_t decode_plan(const kvq_shape &sh, const int32_t *ctx_len, int32_t req, int32_t *wave_start,
+                    int32_t *k_uniform)
 {
     int64_t T = 0;
     for (int s = 0; s < sh.n_seqs; s++)
@@ -113,6 +115,10 @@ int64_t decode_plan(const kvq_shape &sh, const int32_t *ctx_len, int32_t req, in
         const int64_t nt = (ctx_len[s] + 31) / 32;
         int64_t k = req > 0 ? req : std::min<int64_t>(target * nt / T, nt / 4);
         k = std::max<int64_t>(1, std::min<int64_t>(k, nt));
+        if (s == 0)
+            *k_uniform = (int32_t)k;
+        else if (*k_uniform != k)
+            *k_uniform = 0;
         wave_start[s] = (int32_t)W;
         W += k * sh.n_kv_heads;
     }
@@ -244,7 +250,7 @@ int attn_decode(const kvq_cache *cache, int32_t layer, const void *K, const void
     for (int s = 0; s < sh.n_seqs; s++)
         if (ctx_len[s] < 1 || ctx_len[s] > sh.max_ctx)
             return KVQ_E_RANGE;
-    const int64_t W = decode_plan(sh, ctx_len, n_splits, a.wave_start);
+    const int64_t W = decode_plan(sh, ctx_len, n_splits, a.wave_start, &a.k_uniform);
     if (W >= ((int64_t)1 << 31) / 64)
         return KVQ_E_SHAPE;
     if (!workspace || !aligned16(workspace) || workspace_bytes < workspace_need(sh, W))

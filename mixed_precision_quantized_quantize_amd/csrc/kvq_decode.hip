@@ -38,17 +38,38 @@ namespace {
 
 using namespace dev;
 
+#ifndef KVQ_DECODE_NBUF
+#define KVQ_DECODE_NBUF 2
+#endif
+
+// Tile buffers per wave: up to KVQ_DECODE_NBUF, as many as fit in LDS and
+// in the vmcnt counter's range.
+template <int KT, int VT, int D>
+constexpr int decode_nbuf()
+{
+    using g = Geo<KT, VT, D>;
+    constexpr int NKS = (KT == KVQ_F16) ? 0 : (g::KS_BYTES == 128 ? 1 : g::KS_BYTES / 256);
+    constexpr int NVS = (VT == KVQ_F16) ? 0 : (g::VS_BYTES == 128 ? 1 : g::VS_BYTES / 256);
+    constexpr int NDMA = g::K_BYTES / 1024 + NKS + g::V_BYTES / 1024 + NVS;
+    int n = KVQ_DECODE_NBUF;
+    while (n > 1 && (n * g::LDS_A > 160 * 1024 || (n - 1) * NDMA >= 64))
+        n--;
+    return n;
+}
+
 template <int KT, int VT, int D>
 __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(D <= 128 ? 2 : 1))) void decode_kernel(const DecodeArgs a)
 {
     using g = Geo<KT, VT, D>;
     constexpr int NB = g::NB, NCT = g::NCT;
 
-    // two tile buffers per wave where they fit (two separate arrays, so that
-    // the compiler sees that a read of one does not wait for the other)
-    constexpr bool DB = 2 * g::LDS_A <= 160 * 1024;
+    // NBUF tile buffers per wave, as many as fit (up to KVQ_DECODE_NBUF), in
+    // separate arrays so that the compiler sees that a read of one does not
+    // wait for another
+    constexpr int NBUF = decode_nbuf<KT, VT, D>();
     __shared__ __attribute__((aligned(16))) uint8_t lds_a[g::LDS_A];
-    __shared__ __attribute__((aligned(16))) uint8_t lds_b[DB ? g::LDS_A : 16];
+    __shared__ __attribute__((aligned(16))) uint8_t lds_b[NBUF >= 2 ? g::LDS_A : 16];
+    __shared__ __attribute__((aligned(16))) uint8_t lds_c[NBUF >= 3 ? g::LDS_A : 16];
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: scalar addressing
@@ -59,9 +80,14 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(D <=
     const int G = a.G, Hkv = a.Hkv;
     const int64_t Tc = a.Tc;
 
-    // this wave's pair (s, h), its index r among the pair's k waves
-    int s = 0;
-    {
+    // this wave's pair (s, h), its index r among the pair's k waves: a
+    // division when every sequence has k waves per pair, else a binary
+    // search of the sequences' first waves (dependent scalar loads)
+    int s = 0, k = a.k_uniform, local;
+    if (k > 0) {
+        s = gw / (k * Hkv);
+        local = gw - s * k * Hkv;
+    } else {
         int hi = a.n_seqs;  // wave_start[s] <= gw < wave_start[hi]
         while (hi - s > 1) {
             const int mid = (s + hi) >> 1;
@@ -70,9 +96,9 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(D <=
             else
                 hi = mid;
         }
+        k = (a.wave_start[s + 1] - a.wave_start[s]) / Hkv;
+        local = gw - a.wave_start[s];
     }
-    const int k = (a.wave_start[s + 1] - a.wave_start[s]) / Hkv;
-    const int local = gw - a.wave_start[s];
     const int h = local / k, r = local - h * k;
     const int ctx = a.ctx_len[s];
     const int nt = (ctx + TILE - 1) / TILE;
@@ -330,56 +356,63 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(D <=
 
     // ---------------- stream the wave's tiles.  Per tile: wait for its copy,
     // read its operands out of LDS into registers, start the copy of a later
-    // tile into the freed LDS space, then compute.  With two LDS buffers per
-    // wave the copies of the next two tiles are in flight during the math of
+    // tile into the freed LDS space, then compute.  With NBUF LDS buffers per
+    // wave the copies of the next NBUF tiles are in flight during the math of
     // the current one.
     //
     // The waits are explicit: the compiler does not reliably track
     // direct-to-LDS copies against LDS reads.  Vector-memory loads complete
-    // in issue order, so "at most NDMA outstanding" (the count of one tile's
-    // copy instructions) means every load issued before the newer tile's copy
-    // has completed.
+    // in issue order, so "at most n*NDMA outstanding" (NDMA = the count of
+    // one tile's copy instructions) means every load issued before the n
+    // newer tiles' copies has completed.
     constexpr int NKS = (KT == KVQ_F16) ? 0 : (g::KS_BYTES == 128 ? 1 : g::KS_BYTES / 256);
     constexpr int NVS = (VT == KVQ_F16) ? 0 : (g::VS_BYTES == 128 ? 1 : g::VS_BYTES / 256);
     constexpr int NDMA = g::K_BYTES / 1024 + NKS + g::V_BYTES / 1024 + NVS;
-    static_assert(NDMA < 64, "vmcnt holds 6 bits");
-    constexpr int WAIT_NEWER = (NDMA & 15) | ((NDMA >> 4) << 14) | 0x70 | 0xF00;  // vmcnt(NDMA)
-    constexpr int WAIT_ALL = 0x70 | 0xF00;                                          // vmcnt(0)
+    static_assert((NBUF - 1) * NDMA < 64, "vmcnt holds 6 bits");
+    constexpr int WAIT_ALL = 0x70 | 0xF00;  // vmcnt(0), expcnt and lgkmcnt untouched
+    constexpr int WAIT_1 = (NDMA & 15) | ((NDMA >> 4) << 14) | 0x70 | 0xF00;                    // vmcnt(NDMA)
+    constexpr int WAIT_2 = ((2 * NDMA) & 15) | (((2 * NDMA) >> 4) << 14) | 0x70 | 0xF00;        // vmcnt(2*NDMA)
 
     reset();
-    // Tile i (of n_mine) sits in `buf`; the copy of tile i+1 was issued after
-    // it; tile i+DIST goes into `buf` once tile i's operands are in registers.
-    auto step = [&](uint8_t *buf, auto dist_c, const int i) {
-        constexpr int DIST = decltype(dist_c)::value;
-        if (DIST == 2 && i + 1 < n_mine)
-            __builtin_amdgcn_s_waitcnt(WAIT_NEWER);
+    // Tile i (of n_mine) sits in `buf`; the copies of tiles i+1 .. i+NBUF-1
+    // (those below n_mine) were issued after it; tile i+NBUF goes into `buf`
+    // once tile i's operands are in registers.
+    auto step = [&](uint8_t *buf, const int i) {
+        const int newer = min(NBUF - 1, n_mine - 1 - i);
+        if (NBUF >= 3 && newer >= 2)
+            __builtin_amdgcn_s_waitcnt(WAIT_2);
+        else if (NBUF >= 2 && newer >= 1)
+            __builtin_amdgcn_s_waitcnt(WAIT_1);
         else
             __builtin_amdgcn_s_waitcnt(WAIT_ALL);
         Ops op;
         read_ops(buf, op);
-        if (i + DIST < n_mine) {
+        if (i + NBUF < n_mine) {
             asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // LDS reads done before it is refilled
-            issue_tile<KT, VT, D, CPOL_STREAM>(buf, (r + (i + DIST) * k) * TILE, lane, doff, rs);
+            issue_tile<KT, VT, D, CPOL_STREAM>(buf, (r + (i + NBUF) * k) * TILE, lane, doff, rs);
         }
         process(op, (r + i * k) * TILE, ctx);
     };
-    uint8_t *buf_a = lds_a + wave * g::BYTES;
+    uint8_t *const buf_a = lds_a + wave * g::BYTES;
+    uint8_t *const buf_b = lds_b + wave * g::BYTES;
+    uint8_t *const buf_c = lds_c + wave * g::BYTES;
     issue_tile<KT, VT, D, CPOL_STREAM>(buf_a, r * TILE, lane, doff, rs);
-    if constexpr (DB) {
-        uint8_t *buf_b = lds_b + wave * g::BYTES;
-        if (n_mine > 1)
-            issue_tile<KT, VT, D, CPOL_STREAM>(buf_b, (r + k) * TILE, lane, doff, rs);
-        int i = 0;
-        for (; i + 1 < n_mine; i += 2) {
-            step(buf_a, std::integral_constant<int, 2>(), i);
-            step(buf_b, std::integral_constant<int, 2>(), i + 1);
-        }
-        if (i < n_mine)
-            step(buf_a, std::integral_constant<int, 2>(), i);
-    } else {
-        for (int i = 0; i < n_mine; i++)
-            step(buf_a, std::integral_constant<int, 1>(), i);
+    if (NBUF >= 2 && n_mine > 1)
+        issue_tile<KT, VT, D, CPOL_STREAM>(buf_b, (r + k) * TILE, lane, doff, rs);
+    if (NBUF >= 3 && n_mine > 2)
+        issue_tile<KT, VT, D, CPOL_STREAM>(buf_c, (r + 2 * k) * TILE, lane, doff, rs);
+    int i = 0;
+    for (; i + NBUF <= n_mine; i += NBUF) {
+        step(buf_a, i);
+        if constexpr (NBUF >= 2)
+            step(buf_b, i + 1);
+        if constexpr (NBUF >= 3)
+            step(buf_c, i + 2);
     }
+    if (NBUF >= 2 && i < n_mine)
+        step(buf_a, i++);
+    if (NBUF >= 3 && i < n_mine)
+        step(buf_b, i++);
 
     // ---------------- the wave's partial: O of head n (channels 16ct + 4j + i),
     // m, l -- buffer stores from the scalar base of the slot

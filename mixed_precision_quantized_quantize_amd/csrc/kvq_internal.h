@@ -42,6 +42,7 @@ struct DecodeArgs {
                                   // to quantize into position ctx_len[s] - 1 first
     float *ws;            // partial slots [W][G][D+4]: O (unnormalized), m (base 2), l
     int32_t Hq, Hkv, G, Tc, n_seqs, W;
+    int32_t k_uniform;  // waves per pair when every sequence has the same count, else 0
     float c2;  // scale * log2(e)
     int32_t ctx_len[KVQ_MAX_SEQS];
     int32_t wave_start[KVQ_MAX_SEQS + 1];

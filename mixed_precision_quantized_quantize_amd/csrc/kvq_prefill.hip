@@ -9,10 +9,12 @@
 // Rows are (query token, head of the GQA group) pairs, so all heads that share
 // a kv head share every K/V tile.  A workgroup owns 4 waves x 16*RB rows of
 // one (sequence, kv head) and walks the keys in 32-token tiles; each tile is
-// copied once into LDS (the four waves deal out the copy instructions) and
-// read by all four.  Per wave and tile both contractions run on
-// v_mfma_f32_16x16x32_f16, and every operand built from the tile is shared by
-// the wave's RB row blocks:
+// copied once into LDS (the four waves deal out the copy instructions), its
+// quantized blocks are turned into MFMA operands once for the workgroup (the
+// four waves deal out those jobs too and write the operands back to LDS), and
+// all four waves read them.  Per wave and tile both contractions run on
+// v_mfma_f32_16x16x32_f16, and every operand is shared by the wave's RB row
+// blocks:
 //   S^T[key][row]  = K[key][c] . Q^T[c][row]
 //       A quantized K block enters as two binary16 operands hi + lo with
 //       hi = fl16(code * d), lo = fl16(code * d - hi) (one fused multiply-add),
@@ -39,11 +41,13 @@ using namespace dev;
 
 constexpr int PW = 4;  // waves per workgroup
 
-// 16-row blocks per wave.  This file is compiled with the MFMA accumulators in
-// VGPRs (-amdgpu-mfma-vgpr-form): the online-softmax rescale touches them with
-// vector instructions, and with AGPR accumulators the compiler copied them
-// between the two register files on every tile.
-template <int D> struct Rows { static constexpr int RB = (D == 256) ? 1 : 4; };
+// 16-row blocks per wave: two at head_dim <= 128, so that a wave fits in 256
+// registers and two workgroups share each CU (one wave's softmax then runs
+// beside another's MFMAs).  This file is compiled with the MFMA accumulators
+// in VGPRs (-amdgpu-mfma-vgpr-form): the online-softmax rescale touches them
+// with vector instructions, and with AGPR accumulators the compiler copied
+// them between the two register files on every tile.
+template <int D> struct Rows { static constexpr int RB = (D == 256) ? 1 : 2; };
 
 // max over the four lanes n, n+16, n+32, n+48 (the lane groups of one row)
 __device__ inline float max_lane_groups(float v)
@@ -67,7 +71,7 @@ __device__ inline float max3(float a, float b, float c)
 __device__ inline half8 splat8(uint32_t pair) { return pack4(pair, pair, pair, pair); }
 
 template <int KT, int VT, int D>
-__global__ __launch_bounds__(64 * PW) void prefill_kernel(const PrefillArgs a)
+__global__ __launch_bounds__(64 * PW) __attribute__((amdgpu_waves_per_eu(D <= 128 ? 2 : 1))) void prefill_kernel(const PrefillArgs a)
 {
     using g = Geo<KT, VT, D>;
     constexpr int NB = g::NB, NCT = g::NCT;
@@ -77,6 +81,13 @@ __global__ __launch_bounds__(64 * PW) void prefill_kernel(const PrefillArgs a)
     constexpr bool KQ = KT != KVQ_F16, VQ = VT != KVQ_F16;
 
     __shared__ __attribute__((aligned(16))) uint8_t lds[2][g::BYTES];
+    // Dequantized operands of the current tile, built once per workgroup:
+    // K hi and lo per (score tile T, block b), V (times scale) per (block b,
+    // half hh); each set is one MFMA operand, 16 bytes per lane, lane-major.
+    constexpr int NKSET = KQ ? 2 * NB : 0, NVSET = VQ ? 2 * NB : 0;
+    constexpr int DQ_KHI = 0, DQ_KLO = DQ_KHI + NKSET * 1024, DQ_V = DQ_KLO + NKSET * 1024;
+    constexpr int DQ_BYTES = DQ_V + NVSET * 1024;
+    __shared__ __attribute__((aligned(16))) uint8_t dq[DQ_BYTES > 0 ? DQ_BYTES : 16];
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -134,13 +145,12 @@ __global__ __launch_bounds__(64 * PW) void prefill_kernel(const PrefillArgs a)
     DmaOffsets<KT, VT, D> doff;
     doff.init(lane);
 
-    // LDS read offsets: K operand of score tile T (16 keys) and block b, the
-    // block scales of this lane's key in tile T; V operand reads as in decode
-    int k_rd[2][NB], ks_rd[2];
+    // LDS read offsets of the raw tile: K codes of score tile T (16 keys) and
+    // block b; V codes as in decode
+    int k_rd[2][NB];
 #pragma unroll
     for (int T = 0; T < 2; T++) {
         const int r = 8 * (n >> 2) + 4 * T + (n & 3);
-        ks_rd[T] = g::KS_OFF + r * NB * 2;
 #pragma unroll
         for (int b = 0; b < NB; b++) {
             int c, within;
@@ -182,75 +192,102 @@ __global__ __launch_bounds__(64 * PW) void prefill_kernel(const PrefillArgs a)
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
 
-        // ---- raw operands of the tile into registers
-        u32x4 kop[2][NB];
-        uint32_t ksw[2][(NB + 1) / 2];  // this lane's key's block scales, two per word
-        u32x4 vop[VL];
-        u32x4 vsc[NB];
+        // ---- the wave's share of the tile's dequantization (jobs dealt
+        // round-robin over the waves: K sets (T, b) then V blocks b)
+        constexpr int NJOB = (KQ ? 2 * NB : 0) + (VQ ? NB : 0);
 #pragma unroll
-        for (int T = 0; T < 2; T++) {
-#pragma unroll
-            for (int b = 0; b < NB; b++) {
-                if (KT == KVQ_F16) {
-                    kop[T][b] = *reinterpret_cast<const u32x4 *>(buf + k_rd[T][b]);
-                } else if (KT == KVQ_Q8_0) {
+        for (int job = 0; job < NJOB; job++) {
+            if (job % PW != wave)
+                continue;
+            if (KQ && job < 2 * NB) {
+                const int T = job / NB, b = job - T * NB;
+                half8 ka;
+                if (KT == KVQ_Q8_0) {
                     const u32x2 w = *reinterpret_cast<const u32x2 *>(buf + k_rd[T][b]);
-                    kop[T][b] = u32x4{w.x, w.y, 0u, 0u};
+                    ka = deq_q8(w.x, w.y);
                 } else {
-                    kop[T][b] = u32x4{*reinterpret_cast<const uint32_t *>(buf + k_rd[T][b]), 0u, 0u, 0u};
+                    const uint32_t w = *reinterpret_cast<const uint32_t *>(buf + k_rd[T][b]);
+                    ka = k_operand<KVQ_Q4_0>(&w);
                 }
-            }
-            if (KQ) {
-                if (NB == 2) {
-                    ksw[T][0] = *reinterpret_cast<const uint32_t *>(buf + ks_rd[T]);
-                } else if (NB == 4) {
-                    const u32x2 w = *reinterpret_cast<const u32x2 *>(buf + ks_rd[T]);
-                    ksw[T][0] = w.x, ksw[T][1] = w.y;
+                const int r = 8 * (n >> 2) + 4 * T + (n & 3);
+                const uint16_t dbits = *reinterpret_cast<const uint16_t *>(buf + g::KS_OFF + (r * NB + b) * 2);
+                const half8 dd = splat8(dbits * 0x00010001u);
+                const half8 hi = ka * dd;
+                const half8 lo = __builtin_elementwise_fma(ka, dd, -hi);
+                *reinterpret_cast<half8 *>(dq + DQ_KHI + (job * 64 + lane) * 16) = hi;
+                *reinterpret_cast<half8 *>(dq + DQ_KLO + (job * 64 + lane) * 16) = lo;
+            } else if (VQ) {
+                const int b = job - (KQ ? 2 * NB : 0);
+                u32x4 vsc = *reinterpret_cast<const u32x4 *>(buf + g::VS_OFF + (j * NB + b) * 16);
+                // keys at or past key_end were never written for this chunk:
+                // their scale bits may be anything, even NaN -> force zero
+                if (DG && tb + TILE > key_end) {
+                    uint32_t vk[4];
+#pragma unroll
+                    for (int i = 0; i < 4; i++) {
+                        const int k0 = tb + 8 * j + 2 * i;
+                        vk[i] = (k0 < key_end ? 0x0000FFFFu : 0u) | (k0 + 1 < key_end ? 0xFFFF0000u : 0u);
+                    }
+                    vsc = u32x4{vsc.x & vk[0], vsc.y & vk[1], vsc.z & vk[2], vsc.w & vk[3]};
+                }
+                half8 va[2];
+                if (VT == KVQ_Q4_0) {
+                    const u32x2 w = *reinterpret_cast<const u32x2 *>(buf + v_rd[b]);
+                    uint32_t l01, h01, l23, h23, l45, h45, l67, h67;
+                    deq_q4_pair(__builtin_amdgcn_perm(w.x, w.x, 0x0C010C00u), l01, h01);
+                    deq_q4_pair(__builtin_amdgcn_perm(w.x, w.x, 0x0C030C02u), l23, h23);
+                    deq_q4_pair(__builtin_amdgcn_perm(w.y, w.y, 0x0C010C00u), l45, h45);
+                    deq_q4_pair(__builtin_amdgcn_perm(w.y, w.y, 0x0C030C02u), l67, h67);
+                    va[0] = pack4(l01, l23, l45, l67);
+                    va[1] = pack4(h01, h23, h45, h67);
                 } else {
-                    const u32x4 w = *reinterpret_cast<const u32x4 *>(buf + ks_rd[T]);
-                    ksw[T][0] = w.x, ksw[T][1] = w.y, ksw[T][2] = w.z, ksw[T][3] = w.w;
+#pragma unroll
+                    for (int hh = 0; hh < 2; hh++) {
+                        const u32x2 w = *reinterpret_cast<const u32x2 *>(buf + v_rd[2 * b + hh]);
+                        va[hh] = deq_q8(w.x, w.y);
+                    }
                 }
+                const half8 dv = pack4(vsc.x, vsc.y, vsc.z, vsc.w);  // scales of keys 0..7
+#pragma unroll
+                for (int hh = 0; hh < 2; hh++)
+                    *reinterpret_cast<half8 *>(dq + DQ_V + ((2 * b + hh) * 64 + lane) * 16) = va[hh] * dv;
             }
         }
+        // raw f16 operands (no dequantization) stay in the raw tile
+        u32x4 kop[2][NB];
+        u32x4 vop[VL];
+        if (!KQ) {
 #pragma unroll
-        for (int i = 0; i < VL; i++) {
-            if (VT == KVQ_F16) {
-                vop[i] = *reinterpret_cast<const u32x4 *>(buf + v_rd[i]);
-            } else {
-                const u32x2 w = *reinterpret_cast<const u32x2 *>(buf + v_rd[i]);
-                vop[i] = u32x4{w.x, w.y, 0u, 0u};
-            }
-        }
-        if (VQ) {
-#pragma unroll
-            for (int b = 0; b < NB; b++)
-                vsc[b] = *reinterpret_cast<const u32x4 *>(buf + g::VS_OFF + (j * NB + b) * 16);
-        }
-        // keys at or past key_end were never written for this chunk: their
-        // value bits (and V scales) may be anything, even NaN -> force zero
-        if (DG && tb + TILE > key_end) {
-            uint32_t vk[4];
-#pragma unroll
-            for (int i = 0; i < 4; i++) {
-                const int k0 = tb + 8 * j + 2 * i;
-                vk[i] = (k0 < key_end ? 0x0000FFFFu : 0u) | (k0 + 1 < key_end ? 0xFFFF0000u : 0u);
-            }
-            if (VQ) {
+            for (int T = 0; T < 2; T++)
 #pragma unroll
                 for (int b = 0; b < NB; b++)
-                    vsc[b] = u32x4{vsc[b].x & vk[0], vsc[b].y & vk[1], vsc[b].z & vk[2], vsc[b].w & vk[3]};
-            } else {
+                    kop[T][b] = *reinterpret_cast<const u32x4 *>(buf + k_rd[T][b]);
+        }
+        if (!VQ) {
+#pragma unroll
+            for (int i = 0; i < VL; i++)
+                vop[i] = *reinterpret_cast<const u32x4 *>(buf + v_rd[i]);
+            if (DG && tb + TILE > key_end) {
+                uint32_t vk[4];
+#pragma unroll
+                for (int i = 0; i < 4; i++) {
+                    const int k0 = tb + 8 * j + 2 * i;
+                    vk[i] = (k0 < key_end ? 0x0000FFFFu : 0u) | (k0 + 1 < key_end ? 0xFFFF0000u : 0u);
+                }
 #pragma unroll
                 for (int i = 0; i < VL; i++)
                     vop[i] = u32x4{vop[i].x & vk[0], vop[i].y & vk[1], vop[i].z & vk[2], vop[i].w & vk[3]};
             }
         }
+        // the shared operands are complete before anyone reads them
+        if (KQ || VQ)
+            __syncthreads();
         // start the next tile's copy into the other buffer (its last readers
-        // finished before this iteration's barrier)
+        // finished before this iteration's first barrier)
         if (t + 1 < ntile)
             issue_tile<KT, VT, D>(lds[(t + 1) & 1], tb + TILE, lane, doff, rs, wave, PW);
 
-        // ---- scores; the K operand (hi, lo) is built once for all row blocks
+        // ---- scores
         floatx4 sacc[RB][2];
 #pragma unroll
         for (int rb = 0; rb < RB; rb++)
@@ -265,17 +302,9 @@ __global__ __launch_bounds__(64 * PW) void prefill_kernel(const PrefillArgs a)
                     for (int rb = 0; rb < RB; rb++)
                         sacc[rb][T] = mfma(ka, qb[rb][b], sacc[rb][T]);
                 } else {
-                    half8 ka;
-                    if (KT == KVQ_Q8_0) {
-                        ka = deq_q8(kop[T][b].x, kop[T][b].y);
-                    } else {
-                        const uint32_t w = kop[T][b].x;
-                        ka = k_operand<KVQ_Q4_0>(&w);
-                    }
-                    const uint32_t dw = ksw[T][b >> 1];
-                    const half8 dd = splat8(__builtin_amdgcn_perm(dw, dw, (b & 1) ? 0x07060706u : 0x05040504u));
-                    const half8 hi = ka * dd;
-                    const half8 lo = __builtin_elementwise_fma(ka, dd, -hi);
+                    const int set = T * NB + b;
+                    const half8 hi = *reinterpret_cast<const half8 *>(dq + DQ_KHI + (set * 64 + lane) * 16);
+                    const half8 lo = *reinterpret_cast<const half8 *>(dq + DQ_KLO + (set * 64 + lane) * 16);
 #pragma unroll
                     for (int rb = 0; rb < RB; rb++) {
                         sacc[rb][T] = mfma(hi, qb[rb][b], sacc[rb][T]);
@@ -327,30 +356,20 @@ __global__ __launch_bounds__(64 * PW) void prefill_kernel(const PrefillArgs a)
             pb[rb] = pack4(w[0], w[1], w[2], w[3]);
         }
 
-        // ---- O^T += V^T . P; the V operand (times its scale) is built once
+        // ---- O^T += V^T . P
 #pragma unroll
         for (int b = 0; b < NB; b++) {
             half8 va[2];
-            if (VT == KVQ_Q4_0) {
-                const u32x4 w = vop[b];
-                uint32_t l01, h01, l23, h23, l45, h45, l67, h67;
-                deq_q4_pair(__builtin_amdgcn_perm(w.x, w.x, 0x0C010C00u), l01, h01);
-                deq_q4_pair(__builtin_amdgcn_perm(w.x, w.x, 0x0C030C02u), l23, h23);
-                deq_q4_pair(__builtin_amdgcn_perm(w.y, w.y, 0x0C010C00u), l45, h45);
-                deq_q4_pair(__builtin_amdgcn_perm(w.y, w.y, 0x0C030C02u), l67, h67);
-                va[0] = pack4(l01, l23, l45, l67);
-                va[1] = pack4(h01, h23, h45, h67);
+            if (VQ) {
+#pragma unroll
+                for (int hh = 0; hh < 2; hh++)
+                    va[hh] = *reinterpret_cast<const half8 *>(dq + DQ_V + ((2 * b + hh) * 64 + lane) * 16);
             } else {
 #pragma unroll
                 for (int hh = 0; hh < 2; hh++) {
                     const u32x4 w = vop[2 * b + hh];
-                    va[hh] = (VT == KVQ_F16) ? pack4(w.x, w.y, w.z, w.w) : deq_q8(w.x, w.y);
+                    va[hh] = pack4(w.x, w.y, w.z, w.w);
                 }
-            }
-            if (VQ) {
-                const half8 dv = pack4(vsc[b].x, vsc[b].y, vsc[b].z, vsc[b].w);  // scales of keys 0..7
-                va[0] = va[0] * dv;
-                va[1] = va[1] * dv;
             }
 #pragma unroll
             for (int rb = 0; rb < RB; rb++) {
@@ -363,8 +382,8 @@ __global__ __launch_bounds__(64 * PW) void prefill_kernel(const PrefillArgs a)
             lacc[rb] = mfma(ones, pb[rb], lacc[rb]);
     };
     // Tiles before t_d lie entirely at or below every row position of this
-    // wave and run without mask code.  Every wave still meets one barrier per
-    // tile, ntile in all.
+    // wave and run without mask code.  Every wave still meets the same
+    // barriers, those of ntile tiles.
     const int t_d = min(ntile, (wave_first + 1) / TILE);
     for (int t = 0; t < t_d; t++)
         step(std::integral_constant<bool, false>(), t);

@@ -23,10 +23,11 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "kvq_oracle.c")
 _LIB = os.path.join(_HERE, "libkvq_oracle.so")
 
-F16, Q8_0, Q4_0 = 0, 1, 2
-TYPES = {"f16": F16, "q8_0": Q8_0, "q4_0": Q4_0}
+F16, Q8_0, Q4_0, Q5_0 = 0, 1, 2, 3
+TYPES = {"f16": F16, "q8_0": Q8_0, "q4_0": Q4_0, "q5_0": Q5_0}
 ROLE_K, ROLE_V = 0, 1
-BLOCK_CODE_BYTES = {F16: 64, Q8_0: 32, Q4_0: 16}
+# q5_0 blocks: 16 nibble bytes, then the 32 high bits as 4 little-endian bytes
+BLOCK_CODE_BYTES = {F16: 64, Q8_0: 32, Q4_0: 16, Q5_0: 20}
 
 _lock = threading.Lock()
 _lib = None
@@ -114,8 +115,9 @@ def quantize_blocks(t, x_bits) -> tuple[np.ndarray, np.ndarray]:
     """Quantize blocks x [n, 32] (binary16 bits) -> (scale bits [n], codes [n, cb]).
 
     q8_0 / q4_0 as llama.cpp's 32-element block formats named on the llama.cpp
-    optimization page ("KV-Cache-Praezision"); the formulas and op order are
-    the readings listed in kvq_oracle.c.
+    optimization page ("KV-Cache-Praezision"); q5_0, the 5-bit block named in
+    the llama.cpp issue's comment thread; the formulas and op order are the
+    readings listed in kvq_oracle.c.
     """
     t = _type_id(t)
     x = np.ascontiguousarray(x_bits, dtype=np.uint16).reshape(-1, 32)
@@ -127,7 +129,8 @@ def quantize_blocks(t, x_bits) -> tuple[np.ndarray, np.ndarray]:
 
 
 def dequantize_blocks(t, d_bits, codes) -> np.ndarray:
-    """Dequantized values [n, 32] in float64: d*q (q8_0), d*(c-8) (q4_0)."""
+    """Dequantized values [n, 32] in float64: d*q (q8_0), d*(c-8) (q4_0),
+    d*(c-16) (q5_0)."""
     t = _type_id(t)
     d = np.ascontiguousarray(d_bits, dtype=np.uint16).reshape(-1)
     c = np.ascontiguousarray(codes, dtype=np.uint8).reshape(d.size, BLOCK_CODE_BYTES[t])
@@ -145,7 +148,8 @@ def capacity(max_ctx: int) -> int:
 def plane_bytes(t, n_seqs, n_kv_heads, head_dim, max_ctx) -> tuple[int, int]:
     """(codes bytes, scale bytes) of one plane: 34 B / 18 B per 32 elements for
     q8_0 / q4_0 and 2 B per element for f16 (KVSplit page, "Vergleich der
-    Speicherersparnis"; llama.cpp issue, llama_kv_cache size lines)."""
+    Speicherersparnis"; llama.cpp issue, llama_kv_cache size lines); 22 B for
+    q5_0 (its block layout, not printed on the pages)."""
     a, b = ctypes.c_int64(), ctypes.c_int64()
     lib().kvqo_plane_bytes(_type_id(t), n_seqs, n_kv_heads, head_dim, max_ctx,
                            ctypes.byref(a), ctypes.byref(b))

@@ -42,6 +42,13 @@
  *     clamped to their ranges (only reachable with subnormal scales).
  *     Nibble order: byte i of a block holds element i (low nibble) and
  *     element i+16 (high nibble).
+ *   - q5_0 (a fourth type; the pages only name it: a comment in [Issue]'s
+ *     thread reports q5_0/q5_0 as the working middle ground): ggml's 5-bit
+ *     32-element block, read the way q4_0 is read above with the
+ *     5-bit range: d = (signed value of largest magnitude)/(-16),
+ *     code = clamp(trunc(x*id + 16.5), 0, 31), value d*(code - 16); 22 bytes
+ *     per 32 elements (16 bytes of low nibbles in q4_0's order, 32 high bits,
+ *     the binary16 scale).  Parity with llama.cpp's own q5_0 is unpinned.
  *   - Attention: flash attention is exactly standard softmax attention
  *     ([Tokios] Flash Attention: mathematically equivalent, no
  *     approximation), so decode is textbook softmax attention over the
@@ -53,13 +60,17 @@
  *
  * Storage layout (the library's written contract, re-implemented here):
  *   Tc = max_ctx rounded up to a multiple of 32; nb = head_dim/32;
- *   row code bytes R = 2*D (f16), D (q8_0), D/2 (q4_0).
+ *   row code bytes R = 2*D (f16), D (q8_0), D/2 (q4_0 and the q5_0 nibbles).
  *   K plane, token-major:  code byte r of token t of (s,h) at
  *       ((s*H + h)*Tc + t)*R + r;  scale of block b at ((s*H+h)*Tc + t)*nb + b.
  *   V plane, 8-token interleaved: with unit size w = 2 (f16) or 1 byte,
  *       U = R/w units per row, unit u of token t at unit index
  *       (((s*H + h)*(Tc/8) + t/8)*U + u)*8 + t%8;
  *       scale of block b at (((s*H + h)*(Tc/8) + t/8)*nb + b)*8 + t%8.
+ *   q5_0: the code stream holds the nibble rows exactly as q4_0 does, then,
+ *   from byte S*H*Tc*R on, one little-endian 32-bit word of high bits per
+ *   (token, block), indexed like that block's scale (bit i = bit 4 of the
+ *   code of element i).
  *
  * Build: gcc -O2 -ffp-contract=off -fopenmp -shared -fPIC (no -ffast-math).
  */
@@ -71,6 +82,7 @@
 #define KVQO_F16 0
 #define KVQO_Q8_0 1
 #define KVQO_Q4_0 2
+#define KVQO_Q5_0 3
 #define KVQO_ROLE_K 0
 #define KVQO_ROLE_V 1
 
@@ -195,6 +207,45 @@ void kvqo_quantize_q4_0(const uint16_t *x16, uint16_t *d_out, uint8_t *packed)
     *d_out = d16;
 }
 
+/* q5_0: as q4_0 with 32 levels.  Output: 16 nibble bytes (element i low,
+ * i+16 high, low 4 bits of each code) and the 32 high bits in *qh. */
+void kvqo_quantize_q5_0(const uint16_t *x16, uint16_t *d_out, uint8_t *packed, uint32_t *qh)
+{
+    float x[32];
+    float amax = 0.0f;
+    float m = 0.0f; /* +0 unless some |x_i| > 0 */
+    for (int i = 0; i < 32; i++) {
+        x[i] = kvqo_f16_to_f32(x16[i]);
+        float a = fabsf(x[i]);
+        if (a > amax) { /* strict: the lowest index wins a tie */
+            amax = a;
+            m = x[i];
+        }
+    }
+    float d32 = m / -16.0f;
+    uint16_t d16 = kvqo_f32_to_f16(d32);
+    float d = kvqo_f16_to_f32(d16);
+    float id = (d != 0.0f) ? 1.0f / d : 0.0f;
+    int c[32];
+    for (int i = 0; i < 32; i++) {
+        float t = x[i] * id;
+        float u = t + 16.5f;
+        int ci = (int)truncf(u);
+        if (ci > 31)
+            ci = 31;
+        if (ci < 0)
+            ci = 0;
+        c[i] = ci;
+    }
+    uint32_t h = 0;
+    for (int i = 0; i < 16; i++)
+        packed[i] = (uint8_t)((c[i] & 15) | ((c[i + 16] & 15) << 4));
+    for (int i = 0; i < 32; i++)
+        h |= (uint32_t)(c[i] >> 4) << i;
+    *qh = h;
+    *d_out = d16;
+}
+
 /* f16 "quantizer": the block is stored as is. */
 static void store_f16_block(const uint16_t *x16, uint8_t *codes)
 {
@@ -203,7 +254,8 @@ static void store_f16_block(const uint16_t *x16, uint8_t *codes)
 
 int kvqo_block_code_bytes(int type)
 {
-    return type == KVQO_F16 ? 64 : type == KVQO_Q8_0 ? 32 : type == KVQO_Q4_0 ? 16 : -1;
+    /* q5_0: 16 nibble bytes, then the 32 high bits as 4 little-endian bytes */
+    return type == KVQO_F16 ? 64 : type == KVQO_Q8_0 ? 32 : type == KVQO_Q4_0 ? 16 : type == KVQO_Q5_0 ? 20 : -1;
 }
 
 /* Contiguous blocks: x [n][32] -> codes [n][block_code_bytes], d [n]. */
@@ -215,7 +267,12 @@ void kvqo_quantize_blocks(int type, const uint16_t *x, int64_t n, uint16_t *d, u
             kvqo_quantize_q8_0(x + 32 * i, d + i, (int8_t *)(codes + cb * i));
         else if (type == KVQO_Q4_0)
             kvqo_quantize_q4_0(x + 32 * i, d + i, codes + cb * i);
-        else {
+        else if (type == KVQO_Q5_0) {
+            uint32_t qh = 0;
+            kvqo_quantize_q5_0(x + 32 * i, d + i, codes + cb * i, &qh);
+            for (int k = 0; k < 4; k++)
+                codes[cb * i + 16 + k] = (uint8_t)(qh >> (8 * k));
+        } else {
             store_f16_block(x + 32 * i, codes + cb * i);
             d[i] = 0;
         }
@@ -233,7 +290,11 @@ static double dequant_elem(int type, uint16_t d16, const uint8_t *bc, int e)
     if (type == KVQO_Q8_0)
         return d * (double)(int8_t)bc[e];
     int c = (e < 16) ? (bc[e] & 0x0f) : (bc[e - 16] >> 4);
-    return d * (double)(c - 8);
+    if (type == KVQO_Q4_0)
+        return d * (double)(c - 8);
+    /* q5_0: bit e of the little-endian word at bytes 16..19 is bit 4 */
+    c |= ((bc[16 + e / 8] >> (e % 8)) & 1) << 4;
+    return d * (double)(c - 16);
 }
 
 void kvqo_dequantize_blocks(int type, const uint16_t *d, const uint8_t *codes, int64_t n, double *out)
@@ -263,7 +324,7 @@ int64_t kvqo_capacity(int64_t max_ctx) { return (max_ctx + 31) / 32 * 32; }
 
 int64_t kvqo_row_code_bytes(int type, int64_t D)
 {
-    return type == KVQO_F16 ? 2 * D : type == KVQO_Q8_0 ? D : D / 2;
+    return type == KVQO_F16 ? 2 * D : type == KVQO_Q8_0 ? D : D / 2; /* q5_0: nibble rows */
 }
 
 void kvqo_plane_bytes(int type, int64_t n_seqs, int64_t n_kv_heads, int64_t head_dim, int64_t max_ctx,
@@ -271,6 +332,8 @@ void kvqo_plane_bytes(int type, int64_t n_seqs, int64_t n_kv_heads, int64_t head
 {
     int64_t rows = n_seqs * n_kv_heads * kvqo_capacity(max_ctx);
     *codes_bytes = rows * kvqo_row_code_bytes(type, head_dim);
+    if (type == KVQO_Q5_0)
+        *codes_bytes += rows * (head_dim / 32) * 4; /* the high-bit words */
     *scale_bytes = (type == KVQO_F16) ? 0 : rows * (head_dim / 32) * 2;
 }
 
@@ -299,6 +362,14 @@ static int64_t scale_index(const kvqo_plane *p, const kvqo_shape *sh, int s, int
     return ((pair * (Tc / 8) + t / 8) * nb + b) * 8 + t % 8;
 }
 
+/* q5_0: byte address of the first byte of the high-bit word of block b of
+ * token t of pair (s,h): after all nibble rows, indexed like the scale. */
+static int64_t qh_byte_addr(const kvqo_plane *p, const kvqo_shape *sh, int s, int h, int64_t t, int b)
+{
+    int64_t rows = (int64_t)sh->n_seqs * sh->n_kv_heads * kvqo_capacity(sh->max_ctx);
+    return rows * kvqo_row_code_bytes(p->type, sh->head_dim) + 4 * scale_index(p, sh, s, h, t, b);
+}
+
 /* Quantize new rows x [S][n_new][H][D] (binary16 bits) into positions
  * pos[s] .. pos[s]+n_new-1 of plane p.  Caller guarantees the range. */
 void kvqo_append(const kvqo_plane *p, const kvqo_shape *sh, const uint16_t *x, int n_new, const int32_t *pos)
@@ -315,8 +386,12 @@ void kvqo_append(const kvqo_plane *p, const kvqo_shape *sh, const uint16_t *x, i
                     uint8_t bc[64];
                     uint16_t d16 = 0;
                     kvqo_quantize_blocks(p->type, row + 32 * b, 1, &d16, bc);
-                    for (int r = 0; r < cb; r++)
-                        p->codes[code_byte_addr(p, sh, s, h, t, (int64_t)b * cb + r)] = bc[r];
+                    int nib = (p->type == KVQO_Q5_0) ? 16 : cb; /* bytes that live in the rows */
+                    for (int r = 0; r < nib; r++)
+                        p->codes[code_byte_addr(p, sh, s, h, t, (int64_t)b * nib + r)] = bc[r];
+                    if (p->type == KVQO_Q5_0)
+                        for (int k = 0; k < 4; k++)
+                            p->codes[qh_byte_addr(p, sh, s, h, t, b) + k] = bc[16 + k];
                     if (p->type != KVQO_F16)
                         p->scales[scale_index(p, sh, s, h, t, b)] = d16;
                 }
@@ -333,8 +408,12 @@ void kvqo_read_rows(const kvqo_plane *p, const kvqo_shape *sh, int s, int h, int
         int64_t t = t0 + k;
         for (int b = 0; b < nb; b++) {
             uint8_t bc[64];
-            for (int r = 0; r < cb; r++)
-                bc[r] = p->codes[code_byte_addr(p, sh, s, h, t, (int64_t)b * cb + r)];
+            int nib = (p->type == KVQO_Q5_0) ? 16 : cb;
+            for (int r = 0; r < nib; r++)
+                bc[r] = p->codes[code_byte_addr(p, sh, s, h, t, (int64_t)b * nib + r)];
+            if (p->type == KVQO_Q5_0)
+                for (int k = 0; k < 4; k++)
+                    bc[16 + k] = p->codes[qh_byte_addr(p, sh, s, h, t, b) + k];
             uint16_t d16 = (p->type == KVQO_F16) ? 0 : p->scales[scale_index(p, sh, s, h, t, b)];
             for (int e = 0; e < 32; e++)
                 out[k * D + 32 * b + e] = dequant_elem(p->type, d16, bc, e);

@@ -18,7 +18,7 @@ import numpy as np
 import pytest
 import torch
 
-PAIRS = list(itertools.product(["f16", "q8_0", "q4_0"], repeat=2))
+PAIRS = list(itertools.product(["f16", "q8_0", "q4_0", "q5_0"], repeat=2))
 
 
 def rand_f16(rng, shape, scale=1.0):
@@ -79,7 +79,7 @@ def test_quantized_decode_equals_sdpa_over_dequantized(orc, kt, vt):
 
 
 @pytest.mark.parametrize("t", ["K", "V"])
-@pytest.mark.parametrize("typ", ["f16", "q8_0", "q4_0"])
+@pytest.mark.parametrize("typ", ["f16", "q8_0", "q4_0", "q5_0"])
 def test_rows_read_back_as_their_blocks(orc, t, typ):
     """append writes each row's blocks; read_rows returns their dequantized
     values (block quantizer applied row by row, independent of layout)."""
@@ -98,8 +98,16 @@ def numpy_read_plane(codes, scales, typ, role, S, H, D, max_ctx):
     """Loop-free numpy reading of a plane from the header's layout formula."""
     Tc = (max_ctx + 31) // 32 * 32
     nb = D // 32
-    R = {"f16": 2 * D, "q8_0": D, "q4_0": D // 2}[typ]
-    t = np.arange(Tc)
+    R = {"f16": 2 * D, "q8_0": D, "q4_0": D // 2, "q5_0": D // 2}[typ]
+    qh = None
+    if typ == "q5_0":
+        # the nibble rows, then one 32-bit high-bit word per (row, block),
+        # indexed like the scales
+        n_rows = S * H * Tc
+        qh = codes[n_rows * R:].view(np.uint32)
+        codes = codes[:n_rows * R]
+        qh = qh.reshape(S, H, Tc, nb) if role == "K" else \
+            qh.reshape(S, H, Tc // 8, nb, 8).transpose(0, 1, 2, 4, 3).reshape(S, H, Tc, nb)
     if role == "K":
         rows = codes.reshape(S, H, Tc, R)
         sc = None if typ == "f16" else scales.reshape(S, H, Tc, nb)
@@ -118,8 +126,12 @@ def numpy_read_plane(codes, scales, typ, role, S, H, D, max_ctx):
     blk = rows.reshape(S, H, Tc, nb, R // nb)
     if typ == "q8_0":
         q = blk.view(np.int8).astype(np.float64)
-    else:
+    elif typ == "q4_0":
         q = np.concatenate([(blk & 0xF), (blk >> 4)], axis=-1).astype(np.float64) - 8
+    else:
+        lo = np.concatenate([(blk & 0xF), (blk >> 4)], axis=-1).astype(np.int64)
+        hi = (qh[..., None].astype(np.int64) >> np.arange(32)) & 1
+        q = (lo | (hi << 4)).astype(np.float64) - 16
     return (q * d[..., None]).reshape(S, H, Tc, D)
 
 

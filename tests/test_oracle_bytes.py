@@ -52,3 +52,17 @@ def test_capacity_rounds_to_tiles(orc):
     assert orc.capacity(1) == 32 and orc.capacity(32) == 32 and orc.capacity(33) == 64
     kc, ks = orc.plane_bytes("q4_0", 2, 3, 64, 33)
     assert kc == 2 * 3 * 64 * 32 and ks == 2 * 3 * 64 * 2 * 2
+
+
+def test_q5_0_plane_bytes(orc):
+    """q5_0 (no byte totals on the pages): 16 nibble bytes + 4 high-bit bytes in
+    the code stream and a 2-byte scale per 32 elements = 22 B, between q4_0's
+    18 and q8_0's 34."""
+    S, H, D, T = 2, 8, 128, 4096
+    c, s = orc.plane_bytes("q5_0", S, H, D, T)
+    elems = S * H * D * T
+    assert c == elems // 32 * 20 and s == elems // 32 * 2
+    c4, s4 = orc.plane_bytes("q4_0", S, H, D, T)
+    c8, s8 = orc.plane_bytes("q8_0", S, H, D, T)
+    assert (c4 + s4) < (c + s) < (c8 + s8)
+    assert (c + s) * 32 == 22 * elems

@@ -1,11 +1,13 @@
-"""Pins the oracle's q8_0 / q4_0 block quantizers to what the definitions and
-the mathematics fix (the pages print no worked example of a block):
+"""Pins the oracle's q8_0 / q4_0 / q5_0 block quantizers to what the
+definitions and the mathematics fix (the pages print no worked example of a
+block; q5_0's format is not on the pages at all, so it is pinned only by
+these invariants, and its parity with llama.cpp's q5_0 is unpinned):
 
 - integer-grid blocks round-trip exactly with known codes and scales;
 - brute force: each code is the nearest grid point of the stored scale
   (q8_0, ties away from zero) / the truncation rule with clamp (q4_0),
   checked in float64 against the exact binary16 scale;
-- round-trip error bounds |x - x^| <= d/2 (q8_0) and <= |d| (q4_0);
+- round-trip error bounds |x - x^| <= d/2 (q8_0) and <= |d| (q4_0, q5_0);
 - invariants and special cases (all-zero blocks, sign ties, clamps).
 """
 import numpy as np
@@ -158,3 +160,65 @@ def test_f16_blocks_are_copies(orc):
     d, codes = orc.quantize_blocks("f16", xb)
     assert (codes.view(np.uint16) == xb).all()
     assert (orc.dequantize_blocks("f16", d, codes) == xb.view(np.float16).astype(np.float64)).all()
+
+
+def q5_codes(codes):
+    """Codes [n, 32] of q5_0 blocks (16 nibble bytes, then 4 bytes of high bits)."""
+    lo = q4_codes(codes[:, :16])
+    qh = codes[:, 16:20].copy().view("<u4").astype(np.int64)  # [n, 1]
+    hi = (qh >> np.arange(32)) & 1
+    return lo | (hi << 4)
+
+
+@pytest.mark.parametrize("k", [-6, -1, 0, 3])
+def test_q5_0_integer_grid(orc, k):
+    rng = np.random.default_rng(k + 300)
+    n = rng.integers(-15, 16, size=(64, 32))
+    n[:, 11] = -16  # the signed maximum is -16*2^k  ->  d = 2^k
+    x = n * 2.0**k
+    d, codes = orc.quantize_blocks("q5_0", f16(x))
+    assert (dval(d) == 2.0**k).all()
+    assert (q5_codes(codes) == n + 16).all()
+    assert (orc.dequantize_blocks("q5_0", d, codes) == x).all()
+    # mirrored block: the signed max is +16*2^k -> d = -2^k; element -16 -> 32 -> clamped
+    d2, codes2 = orc.quantize_blocks("q5_0", f16(-x))
+    assert (dval(d2) == -(2.0**k)).all()
+    assert (q5_codes(codes2) == np.minimum(31, n + 16)).all()
+
+
+def test_q5_0_rule_and_bound(orc):
+    xb = _random_blocks(4)
+    x = xb.view(np.float16).astype(np.float64)
+    d, codes = orc.quantize_blocks("q5_0", xb)
+    dv = dval(d)[:, None]
+    c = q5_codes(codes)
+    idx = np.argmax(np.abs(x), axis=1)
+    m = x[np.arange(len(x)), idx][:, None]
+    assert (dv == m / -16).all()  # exact: |m|/16 stays in binary16's normal range here
+    u = x / dv + 16.5
+    rule = np.clip(np.floor(u), 0, 31)
+    near = np.abs(u - np.round(u)) < 2.0**-18
+    assert ((c == rule) | near).all()
+    assert (c[np.arange(len(x)), idx] == 0).all()
+    xh = orc.dequantize_blocks("q5_0", d, codes)
+    err = np.abs(x - xh)
+    assert (err <= np.abs(dv) * (1 + 2.0**-20)).all()
+    big = err > np.abs(dv) / 2 * (1 + 2.0**-20)
+    assert (c[big] == 31).all()
+    # one more bit than q4_0 halves the typical error on the same blocks
+    d4, c4 = orc.quantize_blocks("q4_0", xb)
+    e4 = np.abs(x - orc.dequantize_blocks("q4_0", d4, c4))
+    assert 0.4 < err.mean() / e4.mean() < 0.6
+
+
+def test_q5_0_all_zero_and_sign_tie(orc):
+    z = np.zeros((2, 32), dtype=np.float16)
+    z[1] = -0.0
+    d, c = orc.quantize_blocks("q5_0", f16(z))
+    assert (d == 0x8000).all()  # m = +0 -> d = -0
+    assert (c[:, :16] == 0).all() and (c[:, 16:] == 0xFF).all()  # every code is 16: nibble 0, high bit 1
+    assert (orc.dequantize_blocks("q5_0", d, c) == 0).all()
+    x = np.zeros(32)
+    x[4], x[9] = -6.0, 6.0
+    d, _ = orc.quantize_blocks("q5_0", f16(x))
+    assert dval(d)[0] == 0.375  # m = x[4] = -6, the lower index

@@ -1,6 +1,6 @@
 /*
  * kvq.h -- C ABI of libkvq: a KV cache whose keys and values are stored at
- * independently chosen precisions (f16, q8_0, q4_0), with a quantizing
+ * independently chosen precisions (f16, q8_0, q5_0, q4_0), with a quantizing
  * append and flash attention (decode and causal chunked prefill) that reads
  * the quantized blocks directly.  Built for AMD Instinct MI355X (gfx950).
  *
@@ -20,7 +20,10 @@
  *    Silicon when Flash Attention is unavailable ...": the llama_kv_cache
  *    size log lines (K q8_0 / V q4_0 byte totals) and, under "Expected
  *    behavior", the request for a clear early rejection without partial
- *    initialization -- which is this library's error convention.
+ *    initialization -- which is this library's error convention; and, in
+ *    its comment thread, q5_0 named as the working middle ground between
+ *    q8_0 and q4_0 (the format itself is not on the pages: ggml's 5-bit
+ *    block, read the way q4_0 is read below).
  *
  * Conventions for every entry point:
  *  - All tensors live in device memory owned by the caller; the library
@@ -45,8 +48,11 @@
  *  - A 32-element block stores: f16: 32 binary16 values (64 B);
  *    q8_0: 32 int8 codes (32 B) + binary16 scale d, x^ = d*q;
  *    q4_0: 16 bytes, byte i = c_i | c_(i+16) << 4 (4-bit codes) + binary16
- *    scale d, x^ = d*(c-8).  Row code bytes R = 2D, D or D/2; block b of a
- *    row occupies code bytes [b*R/nb, (b+1)*R/nb).
+ *    scale d, x^ = d*(c-8); q5_0: 5-bit codes c, their low 4 bits packed as
+ *    q4_0's, their fifth bits in a 32-bit word (bit i = element i), +
+ *    binary16 scale d, x^ = d*(c-16).  Row code bytes R = 2D, D, D/2 or D/2
+ *    (q5_0: the nibbles); block b of a row occupies code bytes
+ *    [b*R/nb, (b+1)*R/nb).
  *  - K plane ("token-major"): code byte r of token t at
  *        codes + (pair*Tc + t)*R + r;
  *    scale of block b at  scales + 2*((pair*Tc + t)*nb + b).
@@ -56,10 +62,14 @@
  *    value) and 1 byte otherwise, U = R/w units per row, unit u of token t
  *    at  codes + w*((((pair*(Tc/8)) + t/8)*U + u)*8 + t%8);
  *    scale of block b at  scales + 2*(((pair*(Tc/8) + t/8)*nb + b)*8 + t%8).
- *  - Plane bytes: codes S*H*Tc*R, scales S*H*Tc*nb*2 (0 for f16).  With
+ *  - q5_0 high-bit words: in the codes allocation after the S*H*Tc*R bytes
+ *    of rows, one little-endian uint32 per (token, block), at the index of
+ *    that block's scale:  codes + S*H*Tc*R + 4*(scale index).
+ *  - Plane bytes: codes S*H*Tc*R (+ S*H*Tc*nb*4 for q5_0), scales
+ *    S*H*Tc*nb*2 (0 for f16).  With
  *    max_ctx a multiple of 32 nothing is padded: q8_0 costs 34 B and q4_0
  *    18 B per 32 elements, the sizes behind the KVSplit page's 176 / 93.5 /
- *    71.5 / 49.5 MiB and the issue's 816 + 432 MiB.
+ *    71.5 / 49.5 MiB and the issue's 816 + 432 MiB; q5_0 costs 22 B.
  *
  * Quantization (the ggml q8_0 / q4_0 block formats of the cache types named
  * on the llama.cpp pages), bit-exact, in binary32 unless stated:
@@ -69,6 +79,7 @@
  *        d = f16(m/-8); id = d ? 1/d : 0;
  *        c = clamp(trunc((x*id) + 8.5), 0, 15), product and sum rounded
  *        separately (no fused multiply-add).
+ *  q5_0: as q4_0 with d = f16(m/-16) and c = clamp(trunc((x*id) + 16.5), 0, 31).
  *  f16 (the conversion) rounds to nearest even.
  */
 #ifndef KVQ_H
@@ -82,7 +93,7 @@ extern "C" {
 #endif
 
 /* Cache element types (llama.cpp's --cache-type-k / --cache-type-v values). */
-typedef enum kvq_type { KVQ_F16 = 0, KVQ_Q8_0 = 1, KVQ_Q4_0 = 2 } kvq_type;
+typedef enum kvq_type { KVQ_F16 = 0, KVQ_Q8_0 = 1, KVQ_Q4_0 = 2, KVQ_Q5_0 = 3 } kvq_type;
 
 enum {
     KVQ_OK = 0,

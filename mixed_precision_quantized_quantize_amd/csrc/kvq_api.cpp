@@ -16,7 +16,16 @@ using namespace kvq;
 
 namespace {
 
-bool valid_type(int32_t t) { return t == KVQ_F16 || t == KVQ_Q8_0 || t == KVQ_Q4_0; }
+bool valid_type(int32_t t) { return t == KVQ_F16 || t == KVQ_Q8_0 || t == KVQ_Q4_0 || t == KVQ_Q5_0; }
+
+// q5_0's high-bit words follow the nibble rows in the codes allocation.
+uint32_t *high_bits(const kvq_shape &sh, const kvq_plane &p)
+{
+    if (p.type != KVQ_Q5_0)
+        return nullptr;
+    const int64_t rows = (int64_t)sh.n_seqs * sh.n_kv_heads * capacity(sh.max_ctx);
+    return reinterpret_cast<uint32_t *>(static_cast<uint8_t *>(p.codes) + rows * row_code_bytes(p.type, sh.head_dim));
+}
 
 bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 
@@ -162,6 +171,8 @@ int kvq_plane_bytes(const kvq_shape *shape, int32_t type, size_t *codes_bytes, s
         return KVQ_E_TYPE;
     const int64_t rows = (int64_t)shape->n_seqs * shape->n_kv_heads * capacity(shape->max_ctx);
     *codes_bytes = (size_t)(rows * row_code_bytes(type, shape->head_dim));
+    if (type == KVQ_Q5_0)
+        *codes_bytes += (size_t)(rows * (shape->head_dim / 32) * 4);
     *scale_bytes = (type == KVQ_F16) ? 0 : (size_t)(rows * (shape->head_dim / 32) * 2);
     return KVQ_OK;
 }
@@ -198,6 +209,8 @@ int kvq_append(const kvq_cache *cache, int32_t layer, const void *K, const void 
     a.codes[1] = (uint8_t *)cache->v[layer].codes;
     a.scales[0] = (uint16_t *)cache->k[layer].scales;
     a.scales[1] = (uint16_t *)cache->v[layer].scales;
+    a.qh[0] = high_bits(sh, cache->k[layer]);
+    a.qh[1] = high_bits(sh, cache->v[layer]);
     a.H = sh.n_kv_heads;
     a.D = sh.head_dim;
     a.Tc = (int32_t)capacity(sh.max_ctx);
@@ -261,6 +274,8 @@ int attn_decode(const kvq_cache *cache, int32_t layer, const void *K, const void
     a.ks = (const uint16_t *)kp.scales;
     a.vc = (const uint8_t *)vp.codes;
     a.vs = (const uint16_t *)vp.scales;
+    a.kqh = high_bits(sh, kp);
+    a.vqh = high_bits(sh, vp);
     a.q = (const uint16_t *)Q;
     a.knew = (const uint16_t *)K;
     a.vnew = (const uint16_t *)V;
@@ -329,6 +344,8 @@ int kvq_attn_prefill_chunk(const kvq_cache *cache, int32_t layer, const void *Q,
     a.ks = (const uint16_t *)kp.scales;
     a.vc = (const uint8_t *)vp.codes;
     a.vs = (const uint16_t *)vp.scales;
+    a.kqh = high_bits(sh, kp);
+    a.vqh = high_bits(sh, vp);
     a.q = (const uint16_t *)Q;
     a.out = out;
     a.Hq = sh.n_q_heads;

@@ -34,9 +34,9 @@ __global__ __launch_bounds__(256) void append_kernel(const AppendArgs a, int n_q
     const int role = blockIdx.y;
     const uint16_t *blk = a.src[role] + (((int64_t)s * a.n_new + i) * a.H + h) * a.D + 32 * b;
     if (role == 0)
-        quant_store<KT, 0>(blk, q, a.codes[0], a.scales[0], pair, t, b, a.D, a.Tc);
+        quant_store<KT, 0>(blk, q, a.codes[0], a.scales[0], a.qh[0], pair, t, b, a.D, a.Tc);
     else
-        quant_store<VT, 1>(blk, q, a.codes[1], a.scales[1], pair, t, b, a.D, a.Tc);
+        quant_store<VT, 1>(blk, q, a.codes[1], a.scales[1], a.qh[1], pair, t, b, a.D, a.Tc);
 }
 
 template <int KT, int VT>
@@ -53,9 +53,7 @@ hipError_t launch_append(int kt, int vt, const AppendArgs &a, int n_quads, hipSt
 {
 #define KVQ_A(K, V) \
     if (kt == K && vt == V) return launch_t<K, V>(a, n_quads, st);
-    KVQ_A(KVQ_F16, KVQ_F16) KVQ_A(KVQ_F16, KVQ_Q8_0) KVQ_A(KVQ_F16, KVQ_Q4_0)
-    KVQ_A(KVQ_Q8_0, KVQ_F16) KVQ_A(KVQ_Q8_0, KVQ_Q8_0) KVQ_A(KVQ_Q8_0, KVQ_Q4_0)
-    KVQ_A(KVQ_Q4_0, KVQ_F16) KVQ_A(KVQ_Q4_0, KVQ_Q8_0) KVQ_A(KVQ_Q4_0, KVQ_Q4_0)
+    KVQ_FOR_EACH_TYPE_PAIR(KVQ_A)
 #undef KVQ_A
     return hipErrorInvalidValue;
 }

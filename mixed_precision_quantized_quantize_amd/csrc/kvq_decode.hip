@@ -48,9 +48,7 @@ template <int KT, int VT, int D>
 constexpr int decode_nbuf()
 {
     using g = Geo<KT, VT, D>;
-    constexpr int NKS = (KT == KVQ_F16) ? 0 : (g::KS_BYTES == 128 ? 1 : g::KS_BYTES / 256);
-    constexpr int NVS = (VT == KVQ_F16) ? 0 : (g::VS_BYTES == 128 ? 1 : g::VS_BYTES / 256);
-    constexpr int NDMA = g::K_BYTES / 1024 + NKS + g::V_BYTES / 1024 + NVS;
+    constexpr int NDMA = g::NDMA;
     int n = KVQ_DECODE_NBUF;
     while (n > 1 && (n * g::LDS_A > 160 * 1024 || (n - 1) * NDMA >= 64))
         n--;
@@ -116,11 +114,11 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(D <=
             const int role = quad >= NB, b = quad - role * NB;
             const uint16_t *blk = (role ? a.vnew : a.knew) + pair * D + 32 * b;
             if (role == 0)
-                quant::quant_store<KT, 0>(blk, q, const_cast<uint8_t *>(a.kc), const_cast<uint16_t *>(a.ks), pair,
-                                          ctx - 1, b, D, a.Tc);
+                quant::quant_store<KT, 0>(blk, q, const_cast<uint8_t *>(a.kc), const_cast<uint16_t *>(a.ks),
+                                          const_cast<uint32_t *>(a.kqh), pair, ctx - 1, b, D, a.Tc);
             else
-                quant::quant_store<VT, 1>(blk, q, const_cast<uint8_t *>(a.vc), const_cast<uint16_t *>(a.vs), pair,
-                                          ctx - 1, b, D, a.Tc);
+                quant::quant_store<VT, 1>(blk, q, const_cast<uint8_t *>(a.vc), const_cast<uint16_t *>(a.vs),
+                                          const_cast<uint32_t *>(a.vqh), pair, ctx - 1, b, D, a.Tc);
         }
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     }
@@ -132,6 +130,10 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(D <=
         rs.ks = make_rsrc(a.ks + pair * Tc * NB, Tc * NB * 2);
     if (VT != KVQ_F16)
         rs.vs = make_rsrc(a.vs + pair * Tc * NB, Tc * NB * 2);
+    if (KT == KVQ_Q5_0)
+        rs.kh = make_rsrc(a.kqh + pair * Tc * NB, Tc * NB * 4);
+    if (VT == KVQ_Q5_0)
+        rs.vh = make_rsrc(a.vqh + pair * Tc * NB, Tc * NB * 4);
 
     // Q^T operand: lane (n = head, j) holds 8 channels of each block (the
     // channels qk_chan picks: 8j.. for f16/q8_0, 4j.. and 16+4j.. for q4_0);
@@ -140,12 +142,13 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(D <=
     {
         const __amdgpu_buffer_rsrc_t rq =
             make_rsrc(reinterpret_cast<const _Float16 *>(a.q) + ((int64_t)s * a.Hq + (int64_t)h * G) * D, G * D * 2);
-        const int qoff = 2 * (n * D + (KT == KVQ_Q4_0 ? 4 * j : 8 * j));
+        constexpr bool KNIB = KT == KVQ_Q4_0 || KT == KVQ_Q5_0;  // nibble-packed K
+        const int qoff = 2 * (n * D + (KNIB ? 4 * j : 8 * j));
 #pragma unroll
         for (int b = 0; b < NB; b++) {
             qb[b] = half8{};
             if (n < G) {  // lanes past the group keep zeros (their loads are not issued)
-                if (KT == KVQ_Q4_0) {
+                if (KNIB) {
                     const u32x2 lo = __builtin_amdgcn_raw_buffer_load_b64(rq, qoff + 64 * b, 0, 0);
                     const u32x2 hi2 = __builtin_amdgcn_raw_buffer_load_b64(rq, qoff + 64 * b + 32, 0, 0);
                     qb[b] = pack4(lo.x, lo.y, hi2.x, hi2.y);
@@ -168,16 +171,17 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(D <=
         for (int b = 0; b < NB; b++) {
             int c, within;
             if (KT == KVQ_Q8_0) c = 2 * b + (j >> 1), within = 8 * (j & 1);
-            else if (KT == KVQ_Q4_0) c = b, within = 4 * j;
+            else if (KT == KVQ_Q4_0 || KT == KVQ_Q5_0) c = b, within = 4 * j;
             else c = 4 * b + j, within = 0;
             k_rd[T][b] = g::K_OFF + (r * g::CPR + (c ^ kswz<g::CPR>(r))) * 16 + within;
         }
     }
-    constexpr int VL = (VT == KVQ_Q4_0) ? NB : NCT;  // V operand reads per tile
+    constexpr bool VNIB = VT == KVQ_Q4_0 || VT == KVQ_Q5_0;  // nibble-packed V
+    constexpr int VL = VNIB ? NB : NCT;  // V operand reads per tile
     int v_rd[VL];
 #pragma unroll
     for (int i = 0; i < VL; i++) {
-        const int u = 16 * i + n;  // q4_0: byte n of block i; else channel 16i+n
+        const int u = 16 * i + n;  // q4_0 / q5_0: byte n of block i; else channel 16i+n
         const int c = (VT == KVQ_F16) ? u : (u >> 1);
         const int within = (VT == KVQ_F16) ? 0 : 8 * (u & 1);
         v_rd[i] = g::V_OFF + (j * g::CPG + (c ^ vswz<VT, g::CPG>(j))) * 16 + within;
@@ -201,6 +205,8 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(D <=
         uint32_t ks[4 * NB];            // K scales: token r, block b at half r*NB+b
         u32x4 v[VL];                    // V codes per read
         u32x4 vs[NB];                   // V scales: block b, tokens 0..7
+        uint32_t kh[KT == KVQ_Q5_0 ? 2 : 1][KT == KVQ_Q5_0 ? NB : 1];     // q5_0 K high bits
+        uint32_t vh[VT == KVQ_Q5_0 ? NB : 1][VT == KVQ_Q5_0 ? 8 : 1];     // q5_0 V high bits, tokens 0..7
     };
     auto read_ops = [&](const uint8_t *buf, Ops &op) {
 #pragma unroll
@@ -238,6 +244,24 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(D <=
             for (int b = 0; b < NB; b++)
                 op.vs[b] = *reinterpret_cast<const u32x4 *>(buf + g::VS_OFF + (j * NB + b) * 16);
         }
+        if constexpr (KT == KVQ_Q5_0) {
+#pragma unroll
+            for (int T = 0; T < 2; T++) {
+                const int r = 8 * (n >> 2) + 4 * T + (n & 3);
+#pragma unroll
+                for (int b = 0; b < NB; b++)
+                    op.kh[T][b] = *reinterpret_cast<const uint32_t *>(buf + g::KH_OFF + (r * NB + b) * 4);
+            }
+        }
+        if constexpr (VT == KVQ_Q5_0) {
+#pragma unroll
+            for (int b = 0; b < NB; b++) {
+                const u32x4 *p = reinterpret_cast<const u32x4 *>(buf + g::VH_OFF + (j * NB + b) * 32);
+                const u32x4 w0 = p[0], w1 = p[1];
+                op.vh[b][0] = w0.x, op.vh[b][1] = w0.y, op.vh[b][2] = w0.z, op.vh[b][3] = w0.w;
+                op.vh[b][4] = w1.x, op.vh[b][5] = w1.y, op.vh[b][6] = w1.z, op.vh[b][7] = w1.w;
+            }
+        }
     };
 
     // One 32-token tile starting at token tb, from its operands in registers.
@@ -251,14 +275,16 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(D <=
 #pragma unroll
             for (int b = 0; b < NB; b++) {
                 half8 ka;
-                if (KT == KVQ_F16) {
+                if constexpr (KT == KVQ_F16) {
                     const u32x4 w = op.k[T][b];
                     ka = pack4(w.x, w.y, w.z, w.w);
-                } else if (KT == KVQ_Q8_0) {
+                } else if constexpr (KT == KVQ_Q8_0) {
                     ka = deq_q8(op.k[T][b].x, op.k[T][b].y);
-                } else {
+                } else if constexpr (KT == KVQ_Q4_0) {
                     const uint32_t w = op.k[T][b].x;
                     ka = k_operand<KVQ_Q4_0>(&w);
+                } else {
+                    ka = k_operand_q5(op.k[T][b].x, op.kh[T][b] >> (4 * j));
                 }
                 if (KT == KVQ_F16) {
                     sacc[T] = mfma(ka, qb[b], sacc[T]);
@@ -325,7 +351,7 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(D <=
                            h2_bits(bits_h2(p16[2]) * bits_h2(dv.z)) & keep[2],
                            h2_bits(bits_h2(p16[3]) * bits_h2(dv.w)) & keep[3]);
             }
-            if (VT == KVQ_Q4_0) {
+            if constexpr (VT == KVQ_Q4_0) {
                 // bytes of tokens 0..3 (word 0) and 4..7 (word 1); low nibbles feed
                 // channel tile 2b, high nibbles tile 2b+1
                 const u32x4 w = op.v[b];
@@ -336,6 +362,12 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(D <=
                 deq_q4_pair(__builtin_amdgcn_perm(w.y, w.y, 0x0C030C02u), l67, h67);
                 o[2 * b] = mfma(pack4(l01, l23, l45, l67), pb, o[2 * b]);
                 o[2 * b + 1] = mfma(pack4(h01, h23, h45, h67), pb, o[2 * b + 1]);
+            } else if constexpr (VT == KVQ_Q5_0) {
+                // as q4_0, each code's fifth bit from its token's high-bit word
+                half8 va0, va1;
+                v_operand_q5(u32x2{op.v[b].x, op.v[b].y}, op.vh[b], n, va0, va1);
+                o[2 * b] = mfma(va0, pb, o[2 * b]);
+                o[2 * b + 1] = mfma(va1, pb, o[2 * b + 1]);
             } else {
 #pragma unroll
                 for (int hh = 0; hh < 2; hh++) {
@@ -365,9 +397,7 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(D <=
     // in issue order, so "at most n*NDMA outstanding" (NDMA = the count of
     // one tile's copy instructions) means every load issued before the n
     // newer tiles' copies has completed.
-    constexpr int NKS = (KT == KVQ_F16) ? 0 : (g::KS_BYTES == 128 ? 1 : g::KS_BYTES / 256);
-    constexpr int NVS = (VT == KVQ_F16) ? 0 : (g::VS_BYTES == 128 ? 1 : g::VS_BYTES / 256);
-    constexpr int NDMA = g::K_BYTES / 1024 + NKS + g::V_BYTES / 1024 + NVS;
+    constexpr int NDMA = g::NDMA;
     static_assert((NBUF - 1) * NDMA < 64, "vmcnt holds 6 bits");
     constexpr int WAIT_ALL = 0x70 | 0xF00;  // vmcnt(0), expcnt and lgkmcnt untouched
     constexpr int WAIT_1 = (NDMA & 15) | ((NDMA >> 4) << 14) | 0x70 | 0xF00;                    // vmcnt(NDMA)
@@ -517,9 +547,7 @@ hipError_t launch_dec_d(int kt, int vt, const DecodeArgs &a, hipStream_t st)
 {
 #define KVQ_D(K, V) \
     if (kt == K && vt == V) return launch_dec<K, V, D>(a, st);
-    KVQ_D(KVQ_F16, KVQ_F16) KVQ_D(KVQ_F16, KVQ_Q8_0) KVQ_D(KVQ_F16, KVQ_Q4_0)
-    KVQ_D(KVQ_Q8_0, KVQ_F16) KVQ_D(KVQ_Q8_0, KVQ_Q8_0) KVQ_D(KVQ_Q8_0, KVQ_Q4_0)
-    KVQ_D(KVQ_Q4_0, KVQ_F16) KVQ_D(KVQ_Q4_0, KVQ_Q8_0) KVQ_D(KVQ_Q4_0, KVQ_Q4_0)
+    KVQ_FOR_EACH_TYPE_PAIR(KVQ_D)
 #undef KVQ_D
     return hipErrorInvalidValue;
 }

@@ -68,6 +68,73 @@ __device__ inline void deq_q4_pair(uint32_t y, uint32_t &lo, uint32_t &hi)
     hi = h2_bits(__builtin_elementwise_fma(bits_h2(bfi(0x00F000F0u, y, e)), k16, k72));
 }
 
+// q5_0: as deq_q4_pair, with each element's fifth bit supplied in hb_lo (bit
+// 4 / 20: the low-nibble elements of half 0 / 1) and hb_hi (bit 8 / 24: the
+// high-nibble elements) -> binary16 (code - 16), exact:
+// low:  binary16 1024 + c          minus 1040
+// high: binary16 1024 + 16 c       times 1/16 minus 80
+__device__ inline void deq_q5_pair(uint32_t y, uint32_t hb_lo, uint32_t hb_hi, uint32_t &lo, uint32_t &hi)
+{
+    const uint32_t e = 0x64006400u;
+    const half2 k1040 = {(_Float16)1040.0f, (_Float16)1040.0f};
+    const half2 k16 = {(_Float16)0.0625f, (_Float16)0.0625f};
+    const half2 k80 = {(_Float16)-80.0f, (_Float16)-80.0f};
+    lo = h2_bits(bits_h2(bfi(0x000F000Fu, y, e) | hb_lo) - k1040);
+    hi = h2_bits(__builtin_elementwise_fma(bits_h2(bfi(0x00F000F0u, y, e) | hb_hi), k16, k80));
+}
+
+// Fifth bits of an element pair for deq_q5_pair: x holds them in bits 0, 1
+// (the low-nibble elements of half 0, 1) and 16, 17 (the high-nibble ones).
+__device__ inline void q5_pair_bits(uint32_t x, uint32_t &hb_lo, uint32_t &hb_hi)
+{
+    hb_lo = ((x & 1u) << 4) | ((x & 2u) << 19);
+    hb_hi = ((x >> 8) & 0x100u) | ((x << 7) & 0x1000000u);
+}
+
+// Fifth bits of two tokens' element pair (a V operand): bit 0 (low-nibble
+// element) and bit 16 (high-nibble element) of sa (token of half 0) and sb.
+__device__ inline void q5_token_bits(uint32_t sa, uint32_t sb, uint32_t &hb_lo, uint32_t &hb_hi)
+{
+    hb_lo = ((sa & 1u) << 4) | ((sb & 1u) << 20);
+    hb_hi = ((sa >> 8) & 0x100u) | ((sb << 8) & 0x1000000u);
+}
+
+// q5_0 K codes of one block for one lane: w as for q4_0, x = the block's
+// high-bit word shifted right by 4j (bits 0..3: elements 4j..4j+3; bits
+// 16..19: elements 16+4j..16+4j+3).
+__device__ inline half8 k_operand_q5(uint32_t w, uint32_t x)
+{
+    uint32_t l01, h01, l23, h23, a, b;
+    q5_pair_bits(x, a, b);
+    deq_q5_pair(__builtin_amdgcn_perm(w, w, 0x0C010C00u), a, b, l01, h01);
+    q5_pair_bits(x >> 2, a, b);
+    deq_q5_pair(__builtin_amdgcn_perm(w, w, 0x0C030C02u), a, b, l23, h23);
+    return pack4(l01, l23, h01, h23);
+}
+
+// q5_0 V operand of one block: the lane's code byte n (element n low, n+16
+// high) for tokens 0..7 in w (bytes of tokens 0..3 in w.x, 4..7 in w.y) and
+// those tokens' high-bit words h[0..7] -> the two operands (channel tiles
+// of elements n and n+16), binary16 (code - 16).
+__device__ inline void v_operand_q5(u32x2 w, const uint32_t (&h)[8], int n, half8 &va0, half8 &va1)
+{
+    uint32_t s[8];
+#pragma unroll
+    for (int i = 0; i < 8; i++)
+        s[i] = h[i] >> n;
+    uint32_t lo[4], hi[4];
+#pragma unroll
+    for (int p = 0; p < 4; p++) {
+        const uint32_t word = (p < 2) ? w.x : w.y;
+        const uint32_t y = __builtin_amdgcn_perm(word, word, (p & 1) ? 0x0C030C02u : 0x0C010C00u);
+        uint32_t a, b;
+        q5_token_bits(s[2 * p], s[2 * p + 1], a, b);
+        deq_q5_pair(y, a, b, lo[p], hi[p]);
+    }
+    va0 = pack4(lo[0], lo[1], lo[2], lo[3]);
+    va1 = pack4(hi[0], hi[1], hi[2], hi[3]);
+}
+
 // K codes of one block for one lane -> A operand (8 channels of one token).
 template <int KT>
 __device__ inline half8 k_operand(const uint32_t *w)
@@ -88,16 +155,17 @@ __device__ inline half8 k_operand(const uint32_t *w)
 template <int KT>
 __device__ inline int qk_chan(int j, int r)
 {
-    if (KT == KVQ_Q4_0)
+    if (KT == KVQ_Q4_0 || KT == KVQ_Q5_0)
         return (r < 4) ? 4 * j + r : 16 + 4 * j + (r - 4);
     return 8 * j + r;
 }
 
 // ------------------------------------------------------------------ tile geometry
 // One wave stages one 32-token tile in LDS: K codes (token-major rows), K
-// scales, V codes (8-token groups), V scales -- four contiguous ranges of the
-// planes, copied with direct-to-LDS 16-byte loads (every instruction reads one
-// contiguous kilobyte).  16-byte chunks are XOR-swizzled within a K row / V
+// scales, K high bits (q5_0), V codes (8-token groups), V scales, V high bits
+// (q5_0) -- contiguous ranges of the planes, copied with direct-to-LDS
+// 16-byte loads (every instruction reads one contiguous kilobyte) and 4-byte
+// loads for the small ranges.  16-byte chunks are XOR-swizzled within a K row / V
 // group so that the MFMA-operand reads below hit distinct LDS banks.
 template <int KT, int VT, int D>
 struct Geo {
@@ -106,10 +174,20 @@ struct Geo {
     static constexpr int RV = (VT == KVQ_F16) ? 2 * D : (VT == KVQ_Q8_0) ? D : D / 2;  // V row code bytes
     static constexpr int K_BYTES = TILE * RK;
     static constexpr int KS_BYTES = (KT == KVQ_F16) ? 0 : TILE * NB * 2;
+    static constexpr int KH_BYTES = (KT == KVQ_Q5_0) ? TILE * NB * 4 : 0;
     static constexpr int V_BYTES = TILE * RV;
     static constexpr int VS_BYTES = (VT == KVQ_F16) ? 0 : TILE * NB * 2;
-    static constexpr int K_OFF = 0, KS_OFF = K_BYTES, V_OFF = KS_OFF + KS_BYTES, VS_OFF = V_OFF + V_BYTES;
-    static constexpr int BYTES = VS_OFF + VS_BYTES;  // one wave's tile
+    static constexpr int VH_BYTES = (VT == KVQ_Q5_0) ? TILE * NB * 4 : 0;
+    static constexpr int K_OFF = 0, KS_OFF = K_BYTES, KH_OFF = KS_OFF + KS_BYTES, V_OFF = KH_OFF + KH_BYTES;
+    static constexpr int VS_OFF = V_OFF + V_BYTES, VH_OFF = VS_OFF + VS_BYTES;
+    static constexpr int BYTES = VH_OFF + VH_BYTES;  // one wave's tile
+    // copy instructions of one tile: 1 KB each for codes, 256 B each (128 B
+    // on half the lanes) for scales and high bits
+    static constexpr int NK = K_BYTES / 1024, NV = V_BYTES / 1024;
+    static constexpr int NKS = (KT == KVQ_F16) ? 0 : (KS_BYTES == 128 ? 1 : KS_BYTES / 256);
+    static constexpr int NVS = (VT == KVQ_F16) ? 0 : (VS_BYTES == 128 ? 1 : VS_BYTES / 256);
+    static constexpr int NKH = KH_BYTES / 256, NVH = VH_BYTES / 256;
+    static constexpr int NDMA = NK + NKS + NKH + NV + NVS + NVH;
     static constexpr int CPR = RK / 16;              // 16-byte chunks per K row
     static constexpr int CPG = 8 * RV / 16;          // 16-byte chunks per 8-token V group
     static constexpr int LDS_A = WAVES * BYTES;
@@ -182,7 +260,7 @@ struct DmaOffsets {
 
 // Resources over this (sequence, kv head)'s K and V ranges.
 struct PairRsrc {
-    __amdgpu_buffer_rsrc_t kc, ks, vc, vs;
+    __amdgpu_buffer_rsrc_t kc, ks, kh, vc, vs, vh;
 };
 
 // Copies one tile; with nparts > 1 the copy instructions are dealt out
@@ -193,41 +271,57 @@ __device__ inline void issue_tile(uint8_t *buf, int tb, int lane, const DmaOffse
                                   int part = 0, int nparts = 1)
 {
     using g = Geo<KT, VT, D>;
-    constexpr int NK = g::K_BYTES / 1024, NV = g::V_BYTES / 1024;
-    constexpr int NKS = (KT == KVQ_F16) ? 0 : (g::KS_BYTES == 128 ? 1 : g::KS_BYTES / 256);
+    // instruction index: K codes, K scales, K high bits, V codes, V scales,
+    // V high bits
+    constexpr int I_KS = g::NK, I_KH = I_KS + g::NKS, I_V = I_KH + g::NKH, I_VS = I_V + g::NV;
+    constexpr int I_VH = I_VS + g::NVS;
     const int kbase = tb * g::RK;
 #pragma unroll
-    for (int i = 0; i < NK; i++)
+    for (int i = 0; i < g::NK; i++)
         if (i % nparts == part)
             dma<16, CPOL>(r.kc, off.k[i], kbase, buf + g::K_OFF + 1024 * i);
     if (KT != KVQ_F16) {
         const int sbase = tb * g::NB * 2;
         if (g::KS_BYTES == 128) {
-            if (NK % nparts == part && lane < 32)  // 4 bytes on half the lanes (lane l lands at +4 l)
+            if (I_KS % nparts == part && lane < 32)  // 4 bytes on half the lanes (lane l lands at +4 l)
                 dma<4, CPOL>(r.ks, 4 * lane, sbase, buf + g::KS_OFF);
         } else {
 #pragma unroll
-            for (int i = 0; i < g::KS_BYTES / 256; i++)
-                if ((NK + i) % nparts == part)
+            for (int i = 0; i < g::NKS; i++)
+                if ((I_KS + i) % nparts == part)
                     dma<4, CPOL>(r.ks, 256 * i + 4 * lane, sbase, buf + g::KS_OFF + 256 * i);
         }
     }
+    if (KT == KVQ_Q5_0) {  // one word per (token, block), token-major
+        const int hbase = tb * g::NB * 4;
+#pragma unroll
+        for (int i = 0; i < g::NKH; i++)
+            if ((I_KH + i) % nparts == part)
+                dma<4, CPOL>(r.kh, 256 * i + 4 * lane, hbase, buf + g::KH_OFF + 256 * i);
+    }
     const int vbase = (tb >> 3) * 8 * g::RV;
 #pragma unroll
-    for (int i = 0; i < NV; i++)
-        if ((NK + NKS + i) % nparts == part)
+    for (int i = 0; i < g::NV; i++)
+        if ((I_V + i) % nparts == part)
             dma<16, CPOL>(r.vc, off.v[i], vbase, buf + g::V_OFF + 1024 * i);
     if (VT != KVQ_F16) {
         const int sbase = (tb >> 3) * g::NB * 16;
         if (g::VS_BYTES == 128) {
-            if ((NK + NKS + NV) % nparts == part && lane < 32)
+            if (I_VS % nparts == part && lane < 32)
                 dma<4, CPOL>(r.vs, 4 * lane, sbase, buf + g::VS_OFF);
         } else {
 #pragma unroll
-            for (int i = 0; i < g::VS_BYTES / 256; i++)
-                if ((NK + NKS + NV + i) % nparts == part)
+            for (int i = 0; i < g::NVS; i++)
+                if ((I_VS + i) % nparts == part)
                     dma<4, CPOL>(r.vs, 256 * i + 4 * lane, sbase, buf + g::VS_OFF + 256 * i);
         }
+    }
+    if (VT == KVQ_Q5_0) {  // one word per (token, block), 8-token groups
+        const int hbase = (tb >> 3) * g::NB * 32;
+#pragma unroll
+        for (int i = 0; i < g::NVH; i++)
+            if ((I_VH + i) % nparts == part)
+                dma<4, CPOL>(r.vh, 256 * i + 4 * lane, hbase, buf + g::VH_OFF + 256 * i);
     }
 }
 

@@ -16,13 +16,21 @@ __host__ __device__ inline int64_t capacity(int64_t max_ctx) { return (max_ctx +
 
 __host__ __device__ inline int64_t row_code_bytes(int type, int64_t D)
 {
-    return type == KVQ_F16 ? 2 * D : type == KVQ_Q8_0 ? D : D / 2;
+    return type == KVQ_F16 ? 2 * D : type == KVQ_Q8_0 ? D : D / 2;  // q4_0 and the q5_0 nibbles: D/2
 }
+
+// Every (K type, V type) pair, for the kernels' dispatch tables.
+#define KVQ_FOR_EACH_TYPE_PAIR(X)                                                                  \
+    X(KVQ_F16, KVQ_F16) X(KVQ_F16, KVQ_Q8_0) X(KVQ_F16, KVQ_Q4_0) X(KVQ_F16, KVQ_Q5_0)             \
+    X(KVQ_Q8_0, KVQ_F16) X(KVQ_Q8_0, KVQ_Q8_0) X(KVQ_Q8_0, KVQ_Q4_0) X(KVQ_Q8_0, KVQ_Q5_0)         \
+    X(KVQ_Q4_0, KVQ_F16) X(KVQ_Q4_0, KVQ_Q8_0) X(KVQ_Q4_0, KVQ_Q4_0) X(KVQ_Q4_0, KVQ_Q5_0)         \
+    X(KVQ_Q5_0, KVQ_F16) X(KVQ_Q5_0, KVQ_Q8_0) X(KVQ_Q5_0, KVQ_Q4_0) X(KVQ_Q5_0, KVQ_Q5_0)
 
 struct AppendArgs {
     const uint16_t *src[2];  // K, V binary16 [S][n_new][H][D]
     uint8_t *codes[2];       // K plane, V plane
     uint16_t *scales[2];
+    uint32_t *qh[2];         // q5_0 high-bit words (after the nibble rows), else NULL
     int32_t H, D, Tc, n_new, n_seqs;
     int32_t pos[KVQ_MAX_SEQS];
 };
@@ -38,6 +46,7 @@ struct DecodeArgs {
     const uint8_t *vc;
     const uint16_t *vs;
     const uint16_t *q;    // [S][Hq][D]
+    const uint32_t *kqh, *vqh;    // q5_0 high-bit words, else NULL
     const uint16_t *knew, *vnew;  // NULL, or the new row of every sequence, binary16 [S][Hkv][D],
                                   // to quantize into position ctx_len[s] - 1 first
     float *ws;            // partial slots [W][G][D+4]: O (unnormalized), m (base 2), l
@@ -60,6 +69,7 @@ struct PrefillArgs {
     const uint16_t *ks;
     const uint8_t *vc;
     const uint16_t *vs;
+    const uint32_t *kqh, *vqh;  // q5_0 high-bit words, else NULL
     const uint16_t *q;  // [S][n_tok][Hq][D]
     float *out;         // [S][n_tok][Hq][D]
     int32_t Hq, Hkv, G, Tc, n_tok, n_seqs;

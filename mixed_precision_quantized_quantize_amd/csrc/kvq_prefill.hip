@@ -77,7 +77,7 @@ __global__ __launch_bounds__(64 * PW) __attribute__((amdgpu_waves_per_eu(D <= 12
     constexpr int NB = g::NB, NCT = g::NCT;
     constexpr int RB = Rows<D>::RB;
     constexpr int ROWS_G = 16 * RB * PW;
-    constexpr int VL = (VT == KVQ_Q4_0) ? NB : NCT;
+    constexpr int VL = (VT == KVQ_Q4_0 || VT == KVQ_Q5_0) ? NB : NCT;
     constexpr bool KQ = KT != KVQ_F16, VQ = VT != KVQ_F16;
 
     __shared__ __attribute__((aligned(16))) uint8_t lds[2][g::BYTES];
@@ -142,6 +142,10 @@ __global__ __launch_bounds__(64 * PW) __attribute__((amdgpu_waves_per_eu(D <= 12
         rs.ks = make_rsrc(a.ks + pair * Tc * NB, Tc * NB * 2);
     if (VQ)
         rs.vs = make_rsrc(a.vs + pair * Tc * NB, Tc * NB * 2);
+    if (KT == KVQ_Q5_0)
+        rs.kh = make_rsrc(a.kqh + pair * Tc * NB, Tc * NB * 4);
+    if (VT == KVQ_Q5_0)
+        rs.vh = make_rsrc(a.vqh + pair * Tc * NB, Tc * NB * 4);
     DmaOffsets<KT, VT, D> doff;
     doff.init(lane);
 
@@ -155,7 +159,7 @@ __global__ __launch_bounds__(64 * PW) __attribute__((amdgpu_waves_per_eu(D <= 12
         for (int b = 0; b < NB; b++) {
             int c, within;
             if (KT == KVQ_Q8_0) c = 2 * b + (j >> 1), within = 8 * (j & 1);
-            else if (KT == KVQ_Q4_0) c = b, within = 4 * j;
+            else if (KT == KVQ_Q4_0 || KT == KVQ_Q5_0) c = b, within = 4 * j;
             else c = 4 * b + j, within = 0;
             k_rd[T][b] = g::K_OFF + (r * g::CPR + (c ^ kswz<g::CPR>(r))) * 16 + within;
         }
@@ -202,14 +206,18 @@ __global__ __launch_bounds__(64 * PW) __attribute__((amdgpu_waves_per_eu(D <= 12
             if (KQ && job < 2 * NB) {
                 const int T = job / NB, b = job - T * NB;
                 half8 ka;
+                const int r = 8 * (n >> 2) + 4 * T + (n & 3);  // this lane's key in the tile
                 if (KT == KVQ_Q8_0) {
                     const u32x2 w = *reinterpret_cast<const u32x2 *>(buf + k_rd[T][b]);
                     ka = deq_q8(w.x, w.y);
-                } else {
+                } else if (KT == KVQ_Q4_0) {
                     const uint32_t w = *reinterpret_cast<const uint32_t *>(buf + k_rd[T][b]);
                     ka = k_operand<KVQ_Q4_0>(&w);
+                } else {
+                    const uint32_t w = *reinterpret_cast<const uint32_t *>(buf + k_rd[T][b]);
+                    const uint32_t hw = *reinterpret_cast<const uint32_t *>(buf + g::KH_OFF + (r * NB + b) * 4);
+                    ka = k_operand_q5(w, hw >> (4 * j));
                 }
-                const int r = 8 * (n >> 2) + 4 * T + (n & 3);
                 const uint16_t dbits = *reinterpret_cast<const uint16_t *>(buf + g::KS_OFF + (r * NB + b) * 2);
                 const half8 dd = splat8(dbits * 0x00010001u);
                 const half8 hi = ka * dd;
@@ -231,7 +239,13 @@ __global__ __launch_bounds__(64 * PW) __attribute__((amdgpu_waves_per_eu(D <= 12
                     vsc = u32x4{vsc.x & vk[0], vsc.y & vk[1], vsc.z & vk[2], vsc.w & vk[3]};
                 }
                 half8 va[2];
-                if (VT == KVQ_Q4_0) {
+                if (VT == KVQ_Q5_0) {
+                    const u32x2 w = *reinterpret_cast<const u32x2 *>(buf + v_rd[b]);
+                    const u32x4 *hp = reinterpret_cast<const u32x4 *>(buf + g::VH_OFF + (j * NB + b) * 32);
+                    const u32x4 h0 = hp[0], h1 = hp[1];
+                    const uint32_t h[8] = {h0.x, h0.y, h0.z, h0.w, h1.x, h1.y, h1.z, h1.w};
+                    v_operand_q5(w, h, n, va[0], va[1]);
+                } else if (VT == KVQ_Q4_0) {
                     const u32x2 w = *reinterpret_cast<const u32x2 *>(buf + v_rd[b]);
                     uint32_t l01, h01, l23, h23, l45, h45, l67, h67;
                     deq_q4_pair(__builtin_amdgcn_perm(w.x, w.x, 0x0C010C00u), l01, h01);
@@ -419,9 +433,7 @@ hipError_t launch_pf_d(int kt, int vt, const PrefillArgs &a, hipStream_t st)
 {
 #define KVQ_P(K, V) \
     if (kt == K && vt == V) return launch_pf<K, V, D>(a, st);
-    KVQ_P(KVQ_F16, KVQ_F16) KVQ_P(KVQ_F16, KVQ_Q8_0) KVQ_P(KVQ_F16, KVQ_Q4_0)
-    KVQ_P(KVQ_Q8_0, KVQ_F16) KVQ_P(KVQ_Q8_0, KVQ_Q8_0) KVQ_P(KVQ_Q8_0, KVQ_Q4_0)
-    KVQ_P(KVQ_Q4_0, KVQ_F16) KVQ_P(KVQ_Q4_0, KVQ_Q8_0) KVQ_P(KVQ_Q4_0, KVQ_Q4_0)
+    KVQ_FOR_EACH_TYPE_PAIR(KVQ_P)
 #undef KVQ_P
     return hipErrorInvalidValue;
 }

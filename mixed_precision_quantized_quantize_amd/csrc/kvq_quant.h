@@ -1,12 +1,12 @@
 // kvq_quant.h -- the block quantizer of one 32-element block, shared by the
 // append kernel and the decode kernel's fused one-row append.  Four lanes own
-// one block; the block's |x| maximum (q8_0) or signed maximum (q4_0) is
+// one block; the block's |x| maximum (q8_0) or signed maximum (q4_0, q5_0) is
 // reduced across the four lanes with cross-lane shuffles, then every lane
 // writes its own codes.  The arithmetic follows the contract in kvq.h bit for
 // bit: binary32 scale, one rounding to binary16, codes against the stored
-// scale's binary32 reciprocal, q8_0 rounding half away from zero, q4_0
-// product and +8.5 rounded separately (no multiply-add contraction in the
-// functions below).  Internal; not part of the C ABI.
+// scale's binary32 reciprocal, q8_0 rounding half away from zero, q4_0 / q5_0
+// product and +8.5 / +16.5 rounded separately (no multiply-add contraction in
+// the functions below).  Internal; not part of the C ABI.
 #pragma once
 
 #include "kvq_internal.h"
@@ -29,11 +29,12 @@ __device__ inline float round_half_away(float v)
 }
 
 // Element indices held by lane q (0..3) of a block: q8_0 / f16 take 8
-// consecutive elements, q4_0 takes the 4+4 elements that share its 4 bytes.
+// consecutive elements, q4_0 / q5_0 take the 4+4 elements that share its 4
+// nibble bytes.
 template <int T>
 __device__ inline int elem_of(int q, int k)
 {
-    if (T == KVQ_Q4_0)
+    if (T == KVQ_Q4_0 || T == KVQ_Q5_0)
         return (k < 4) ? 4 * q + k : 16 + 4 * q + (k - 4);
     return 8 * q + k;
 }
@@ -41,7 +42,7 @@ __device__ inline int elem_of(int q, int k)
 template <int T>
 __device__ inline void load8(const uint16_t *blk, int q, uint16_t (&x)[8])
 {
-    if (T == KVQ_Q4_0) {
+    if (T == KVQ_Q4_0 || T == KVQ_Q5_0) {
         u32x2 a = *reinterpret_cast<const u32x2 *>(blk + 4 * q);
         u32x2 b = *reinterpret_cast<const u32x2 *>(blk + 16 + 4 * q);
         uint32_t w[4] = {a.x, a.y, b.x, b.y};
@@ -58,9 +59,11 @@ __device__ inline void load8(const uint16_t *blk, int q, uint16_t (&x)[8])
 }
 
 // Quantize one block (this lane's 8 elements) and store codes + scale.
+// qh: q5_0's high-bit words (one per row and block, indexed like the
+// scales), unused for the other types.
 template <int T, int ROLE>
-__device__ inline void quant_store(const uint16_t *blk, int q, uint8_t *codes, uint16_t *scales, int64_t pair,
-                                   int64_t t, int b, int D, int Tc)
+__device__ inline void quant_store(const uint16_t *blk, int q, uint8_t *codes, uint16_t *scales, uint32_t *qh,
+                                   int64_t pair, int64_t t, int b, int D, int Tc)
 {
 #pragma clang fp contract(off)
     const int NB = D / 32;
@@ -129,7 +132,7 @@ __device__ inline void quant_store(const uint16_t *blk, int q, uint8_t *codes, u
         key = key > o ? key : o;
         uint32_t absbits = key >> 6;
         float m = (absbits == 0) ? 0.0f : h2f((uint16_t)(absbits | ((key & 1u) << 15)));
-        float d32 = __fdiv_rn(m, -8.0f);
+        float d32 = __fdiv_rn(m, (T == KVQ_Q5_0) ? -16.0f : -8.0f);
         dbits = f2h_bits(d32);
     }
     d = h2f(dbits);
@@ -155,18 +158,31 @@ __device__ inline void quant_store(const uint16_t *blk, int q, uint8_t *codes, u
                 codes[unit_index(32 * b + 8 * q + k)] = c[k];
         }
     } else {
+        constexpr float HALF_RANGE = (T == KVQ_Q5_0) ? 16.5f : 8.5f;
+        constexpr int TOP = (T == KVQ_Q5_0) ? 31 : 15;
         int c[8];
 #pragma unroll
         for (int k = 0; k < 8; k++) {
-            const float t = x[k] * id;  // rounded product ...
-            const float u = t + 8.5f;   // ... then a separately rounded sum: never one fused op
+            const float t = x[k] * id;       // rounded product ...
+            const float u = t + HALF_RANGE;  // ... then a separately rounded sum: never one fused op
             int ci = (int)__builtin_truncf(u);
-            c[k] = ci < 0 ? 0 : (ci > 15 ? 15 : ci);
+            c[k] = ci < 0 ? 0 : (ci > TOP ? TOP : ci);
         }
         uint8_t by[4];
 #pragma unroll
         for (int k = 0; k < 4; k++)
-            by[k] = (uint8_t)(c[k] | (c[k + 4] << 4));  // element 4q+k low, 16+4q+k high
+            by[k] = (uint8_t)((c[k] & 15) | ((c[k + 4] & 15) << 4));  // element 4q+k low, 16+4q+k high
+        if (T == KVQ_Q5_0) {
+            // the block's 32 high bits: this lane's 8, then OR over the quad
+            uint32_t h = 0;
+#pragma unroll
+            for (int k = 0; k < 4; k++)
+                h |= ((uint32_t)(c[k] >> 4) << (4 * q + k)) | ((uint32_t)(c[k + 4] >> 4) << (16 + 4 * q + k));
+            h |= (uint32_t)__shfl_xor((int)h, 1);
+            h |= (uint32_t)__shfl_xor((int)h, 2);
+            if (q == 0)
+                qh[scale_index()] = h;
+        }
         if (ROLE == 0) {
             *reinterpret_cast<uint32_t *>(codes + unit_index(16 * b + 4 * q)) =
                 by[0] | (by[1] << 8) | (by[2] << 16) | ((uint32_t)by[3] << 24);

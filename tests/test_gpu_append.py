@@ -1,5 +1,5 @@
 """GPU parity of kvq_append: the planes the HIP kernel writes equal the
-oracle's byte for byte (codes and binary16 scales), for all nine K/V type
+oracle's byte for byte (codes, high bits and binary16 scales), for all 16 K/V type
 pairs, every supported head_dim, ragged positions, partial 8-token groups,
 a capacity that is not a multiple of 32, and the degenerate blocks (all
 zero, negative zero, signed-maximum ties, scales in the binary16 subnormal
@@ -15,7 +15,7 @@ from kvq_testutil import assert_planes_equal, bits, zero_cache
 
 pytestmark = pytest.mark.gpu
 
-PAIRS = list(itertools.product(["f16", "q8_0", "q4_0"], repeat=2))
+PAIRS = list(itertools.product(["f16", "q8_0", "q4_0", "q5_0"], repeat=2))
 
 
 def special_rows(x, rng):
@@ -35,6 +35,8 @@ def special_rows(x, rng):
     if n > 5:
         x[-1, 5, 0, :] = 2.5 / 16
         x[-1, 5, 0, 0] = 127 / 16             # q8_0 exact half-way codes
+    if n > 6:
+        x[0, 6, 0, :] = rng.integers(-16, 16, size=D) * 0.125  # q5_0 grid values, halves of q4_0's
     return x
 
 

@@ -1,7 +1,7 @@
 """GPU parity of kvq_attn_decode (split-K flash decode + log-sum-exp merge)
 against the binary64 oracle on the same inputs.
 
-Small shapes cover all nine K/V type pairs, head_dim 64/128/256, GQA group
+Small shapes cover all 16 K/V type pairs (f16, q8_0, q5_0, q4_0), head_dim 64/128/256, GQA group
 sizes 1..16, several tiles with a ragged tail, ragged ctx_len across the
 batch, ctx_len = 1 and several split counts.  The named workloads run at
 their full sizes on one layer, in the launch configuration the benchmark
@@ -18,7 +18,7 @@ from kvq_testutil import assert_attn_close, assert_planes_equal, bits, zero_cach
 
 pytestmark = pytest.mark.gpu
 
-PAIRS = list(itertools.product(["f16", "q8_0", "q4_0"], repeat=2))
+PAIRS = list(itertools.product(["f16", "q8_0", "q4_0", "q5_0"], repeat=2))
 
 
 def small_case(kt, vt, S, Hq, Hkv, D, T, ctx, n_splits_list, seed, kscale=3.0):
@@ -51,7 +51,7 @@ def test_decode_pairs(kt, vt, D):
                seed=zlib.crc32(f"{kt}{vt}{D}".encode()) % 1000)
 
 
-@pytest.mark.parametrize("kt,vt", [("q8_0", "q4_0"), ("f16", "f16"), ("q4_0", "q8_0")])
+@pytest.mark.parametrize("kt,vt", [("q8_0", "q4_0"), ("f16", "f16"), ("q4_0", "q8_0"), ("q5_0", "q5_0"), ("q8_0", "q5_0")])
 def test_decode_head_dim_256(kt, vt):
     print(f"decode parity {kt}/{vt} D=256", flush=True)
     small_case(kt, vt, S=2, Hq=8, Hkv=2, D=256, T=200, ctx=[200, 64], n_splits_list=[0, 2], seed=7)
@@ -192,7 +192,7 @@ def test_decode_graph_replay_matches_eager():
         del junk
 
 
-@pytest.mark.parametrize("kt,vt", [("q8_0", "q4_0"), ("f16", "f16"), ("q4_0", "q8_0")])
+@pytest.mark.parametrize("kt,vt", [("q8_0", "q4_0"), ("f16", "f16"), ("q4_0", "q8_0"), ("q5_0", "q5_0")])
 def test_decode_ignores_garbage_past_context(kt, vt):
     """Cache memory past ctx_len may hold any bits (here NaN patterns in codes
     and scales): the ragged tail tile must not let them into the output."""

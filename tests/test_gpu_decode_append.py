@@ -10,7 +10,7 @@ and checks that
   * the two outputs are equal bit for bit (same quantizer, same work split);
   * the output is within the attention tolerance of the binary64 oracle.
 Position ctx_len-1 holds a different row before the call, so a write that
-went missing or landed elsewhere shows.  Cases cover the nine K/V type pairs,
+went missing or landed elsewhere shows.  Cases cover the 16 K/V type pairs,
 head_dim 64/128/256, ctx_len = 1, tile boundaries (32, 33, 64), ragged
 batches and several split counts (the wave that owns the last tile differs)."""
 import itertools
@@ -24,7 +24,7 @@ from kvq_testutil import assert_attn_close, assert_planes_equal, bits, zero_cach
 
 pytestmark = pytest.mark.gpu
 
-PAIRS = list(itertools.product(["f16", "q8_0", "q4_0"], repeat=2))
+PAIRS = list(itertools.product(["f16", "q8_0", "q4_0", "q5_0"], repeat=2))
 
 
 def fused_case(kt, vt, S, Hq, Hkv, D, T, ctx, splits, seed):
@@ -73,7 +73,7 @@ def test_decode_append_pairs(kt, vt):
 
 
 @pytest.mark.parametrize("D", [64, 256])
-@pytest.mark.parametrize("kt,vt", [("q8_0", "q4_0"), ("f16", "q8_0"), ("q4_0", "f16")])
+@pytest.mark.parametrize("kt,vt", [("q8_0", "q4_0"), ("f16", "q8_0"), ("q4_0", "f16"), ("q5_0", "q5_0")])
 def test_decode_append_head_dims(kt, vt, D):
     fused_case(kt, vt, S=2, Hq=8, Hkv=2, D=D, T=200, ctx=[64, 200], splits=[0, 2, 7], seed=D)
 

@@ -1,7 +1,7 @@
 """GPU parity of kvq_attn_prefill_chunk (causal flash attention of a chunk of
 queries over the quantized cache) against the binary64 oracle.
 
-Small shapes cover all nine K/V type pairs, head_dim 64/128/256, GQA group
+Small shapes cover all 16 K/V type pairs (f16, q8_0, q5_0, q4_0), head_dim 64/128/256, GQA group
 sizes 1..16 (powers of two and not), chunks from 1 query to several
 workgroups with a ragged last one, ragged chunk starts across the batch
 (including a chunk at position 0) and cache memory past the chunk holding
@@ -18,7 +18,7 @@ from kvq_testutil import assert_attn_close, assert_planes_equal, bits, zero_cach
 
 pytestmark = pytest.mark.gpu
 
-PAIRS = list(itertools.product(["f16", "q8_0", "q4_0"], repeat=2))
+PAIRS = list(itertools.product(["f16", "q8_0", "q4_0", "q5_0"], repeat=2))
 
 
 def prefill_case(kt, vt, S, Hq, Hkv, D, T, n_tok, q_pos0, seed, garbage=False, kscale=3.0, scale=None):
@@ -61,7 +61,7 @@ def test_prefill_pairs(kt, vt, D):
                  seed=zlib.crc32(f"p{kt}{vt}{D}".encode()) % 1000)
 
 
-@pytest.mark.parametrize("kt,vt", [("q8_0", "q4_0"), ("f16", "f16"), ("q4_0", "q8_0")])
+@pytest.mark.parametrize("kt,vt", [("q8_0", "q4_0"), ("f16", "f16"), ("q4_0", "q8_0"), ("q5_0", "q5_0"), ("q5_0", "f16")])
 def test_prefill_head_dim_256(kt, vt):
     print(f"prefill parity {kt}/{vt} D=256", flush=True)
     prefill_case(kt, vt, S=2, Hq=8, Hkv=2, D=256, T=200, n_tok=45, q_pos0=[155, 3], seed=8)
@@ -79,7 +79,7 @@ def test_prefill_chunk_shapes(n_tok, q_pos0):
     prefill_case("q8_0", "q4_0", S=2, Hq=32, Hkv=8, D=128, T=300, n_tok=n_tok, q_pos0=q_pos0, seed=n_tok)
 
 
-@pytest.mark.parametrize("kt,vt", [("q8_0", "q4_0"), ("f16", "f16"), ("q4_0", "q8_0"), ("f16", "q4_0")])
+@pytest.mark.parametrize("kt,vt", [("q8_0", "q4_0"), ("f16", "f16"), ("q4_0", "q8_0"), ("f16", "q4_0"), ("q8_0", "q5_0")])
 def test_prefill_ignores_garbage_past_chunk(kt, vt):
     """Positions after the chunk's last query were never written (all bits
     set, NaN as binary16): the diagonal tiles must keep them out."""

@@ -86,13 +86,24 @@ int check_layer(const kvq_cache *c, int32_t layer)
 
 // Decode work split (the kernels describe it): k waves per (sequence, kv
 // head) pair, the same k for the pairs of one sequence.  n_splits > 0 asks
-// for k = n_splits; 0 fills the device (WAVES_PER_CU waves per CU, k about
+// for k = n_splits; 0 fills the device (waves_per_cu waves per CU, k about
 // proportional to each sequence's tiles, at least four tiles per wave).
 // Never more waves for a pair than it has tiles.
 constexpr int AUTO_WAVES_MAX = 4096;
-// One workgroup (four waves, one per SIMD) per CU streams best: more waves
-// per CU measured slower (more concurrent streams, no more bandwidth).
-constexpr int WAVES_PER_CU = 4;
+// Waves per CU of the automatic split.  Where the tile math is heavy for its
+// bytes (K q4_0 or q5_0, or V q5_0: more vector instructions to unpack the
+// codes) two workgroups of four waves share a CU, so that one wave's math
+// overlaps another's copies: measured about 25% faster for q4_0/q4_0 and
+// q5_0/q5_0 at head_dim 128.  Otherwise one workgroup per CU, which streams
+// best (K8V4: 6% faster than two).  One at head_dim 256 either way: its waves
+// need all 512 registers.
+int waves_per_cu(const kvq_shape &sh, int32_t kt, int32_t vt)
+{
+    if (sh.head_dim > 128)
+        return 4;
+    const bool heavy = kt == KVQ_Q4_0 || kt == KVQ_Q5_0 || vt == KVQ_Q5_0;
+    return heavy ? 8 : 4;
+}
 
 int device_cus()
 {
@@ -111,14 +122,13 @@ int device_cus()
 
 // Fills wave_start[0..n_seqs] and returns the wave count W; *k_uniform is
 // the waves per pair when all sequences have the same number, else 0.
-int64_t decode_plan(const kvq_shape &sh, const int32_t *ctx_len, int32_t req, int32_t *wave_start,
-                    int32_t *k_uniform)
+int64_t decode_plan(const kvq_shape &sh, int32_t kt, int32_t vt, const int32_t *ctx_len, int32_t req,
+                    int32_t *wave_start, int32_t *k_uniform)
 {
     int64_t T = 0;
     for (int s = 0; s < sh.n_seqs; s++)
         T += (int64_t)sh.n_kv_heads * ((ctx_len[s] + 31) / 32);
-    const int per_cu = sh.head_dim <= 128 ? WAVES_PER_CU : 4;
-    const int64_t target = std::min<int64_t>((int64_t)device_cus() * per_cu, AUTO_WAVES_MAX);
+    const int64_t target = std::min<int64_t>((int64_t)device_cus() * waves_per_cu(sh, kt, vt), AUTO_WAVES_MAX);
     int64_t W = 0;
     for (int s = 0; s < sh.n_seqs; s++) {
         const int64_t nt = (ctx_len[s] + 31) / 32;
@@ -263,7 +273,8 @@ int attn_decode(const kvq_cache *cache, int32_t layer, const void *K, const void
     for (int s = 0; s < sh.n_seqs; s++)
         if (ctx_len[s] < 1 || ctx_len[s] > sh.max_ctx)
             return KVQ_E_RANGE;
-    const int64_t W = decode_plan(sh, ctx_len, n_splits, a.wave_start, &a.k_uniform);
+    const int64_t W = decode_plan(sh, cache->k[layer].type, cache->v[layer].type, ctx_len, n_splits, a.wave_start,
+                                  &a.k_uniform);
     if (W >= ((int64_t)1 << 31) / 64)
         return KVQ_E_SHAPE;
     if (!workspace || !aligned16(workspace) || workspace_bytes < workspace_need(sh, W))

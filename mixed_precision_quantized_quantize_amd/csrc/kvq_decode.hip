@@ -28,6 +28,7 @@
 // tokens interleaved, so a lane's P.V operand (8 tokens of one channel) is
 // one 8- or 16-byte load.  Online softmax runs in base 2 (scores times
 // scale*log2 e).
+#include <algorithm>
 #include <type_traits>
 
 #include "kvq_device.h"
@@ -462,10 +463,13 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(D <=
 }
 
 // Log-sum-exp merge of the partials of one (sequence, kv head) pair for one
-// query head: workgroup = (pair, head), thread = output channel.  The slot
-// weights 2^(m_j - M) go through LDS in chunks, so that every thread's loads
-// of its channel's partial outputs are independent and issued together.
+// query head: workgroup = (pair, head), P groups of one thread per output
+// channel.  The slot weights 2^(m_j - M) go through LDS in chunks; group p
+// sums slots p, p+P, ... of a chunk, sixteen independent loads at a time, and
+// the groups' sums are added through LDS at the end.  P grows with the
+// slots per pair so that a long merge is not one thread's chain of loads.
 constexpr int MERGE_CHUNK = 512;
+constexpr int MERGE_MAX_THREADS = 1024;
 
 __device__ inline float block_reduce(float v, float *sh, bool is_max)
 {
@@ -486,11 +490,13 @@ __device__ inline float block_reduce(float v, float *sh, bool is_max)
     return r;
 }
 
-__global__ __launch_bounds__(256) void merge_kernel(const MergeArgs a)
+__global__ __launch_bounds__(MERGE_MAX_THREADS) void merge_kernel(const MergeArgs a)
 {
     __shared__ float wts[MERGE_CHUNK];
-    __shared__ float red[4];
+    __shared__ float red[MERGE_MAX_THREADS / 64];
+    __shared__ float part[MERGE_MAX_THREADS];
     const int G = a.G, D = a.D, Dp = a.D + 4;
+    const int P = blockDim.x / D;  // groups; blockDim.x == P * D
     const int pair = blockIdx.x / G, gg = blockIdx.x - pair * G;
     const int s = pair / a.Hkv, h = pair - s * a.Hkv;
     const int k = (a.wave_start[s + 1] - a.wave_start[s]) / a.Hkv;  // the pair's waves = its slots
@@ -498,40 +504,48 @@ __global__ __launch_bounds__(256) void merge_kernel(const MergeArgs a)
     const int nslot = k;
     const int64_t stride = (int64_t)G * Dp;  // floats between consecutive slots
     const float *base = a.ws + ((int64_t)w0 * G + gg) * Dp;
-    const int c = threadIdx.x;  // blockDim.x == D
+    const int t = threadIdx.x, c = t % D, grp = t / D;
 
     float mx = -INFINITY;
-    for (int k = c; k < nslot; k += D)
-        mx = fmaxf(mx, base[k * stride + D]);
+    for (int j = t; j < nslot; j += blockDim.x)
+        mx = fmaxf(mx, base[j * stride + D]);
     const float M = block_reduce(mx, red, true);
 
     float lsum = 0.0f, acc = 0.0f;
     for (int k0 = 0; k0 < nslot; k0 += MERGE_CHUNK) {
         const int chunk = min(MERGE_CHUNK, nslot - k0);
         __syncthreads();  // the previous chunk's weights are no longer read
-        for (int k = c; k < chunk; k += D) {
-            const float *pk = base + (int64_t)(k0 + k) * stride;
+        for (int j = t; j < chunk; j += blockDim.x) {
+            const float *pk = base + (int64_t)(k0 + j) * stride;
             const float w = __builtin_amdgcn_exp2f(pk[D] - M);
-            wts[k] = w;
+            wts[j] = w;
             lsum += pk[D + 1] * w;
         }
         __syncthreads();
         const float *pc = base + (int64_t)k0 * stride + c;
-        int k = 0;
-        for (; k + 8 <= chunk; k += 8) {  // eight independent loads in flight
-            float v[8];
+        int j = grp;
+        for (; j + 15 * P < chunk; j += 16 * P) {  // sixteen independent loads in flight
+            float v[16];
 #pragma unroll
-            for (int u = 0; u < 8; u++)
-                v[u] = pc[(int64_t)(k + u) * stride];
+            for (int u = 0; u < 16; u++)
+                v[u] = pc[(int64_t)(j + u * P) * stride];
 #pragma unroll
-            for (int u = 0; u < 8; u++)
-                acc += v[u] * wts[k + u];
+            for (int u = 0; u < 16; u++)
+                acc += v[u] * wts[j + u * P];
         }
-        for (; k < chunk; k++)
-            acc += pc[(int64_t)k * stride] * wts[k];
+        for (; j < chunk; j += P)
+            acc += pc[(int64_t)j * stride] * wts[j];
     }
     const float L = block_reduce(lsum, red, false);
-    a.out[((int64_t)s * a.Hq + (int64_t)h * G + gg) * D + c] = acc / L;
+    if (P > 1) {
+        part[t] = acc;
+        __syncthreads();
+        if (grp == 0)
+            for (int g2 = 1; g2 < P; g2++)
+                acc += part[g2 * D + c];
+    }
+    if (grp == 0)
+        a.out[((int64_t)s * a.Hq + (int64_t)h * G + gg) * D + c] = acc / L;
 }
 
 template <int KT, int VT, int D>
@@ -565,7 +579,14 @@ hipError_t launch_decode(int kt, int vt, int D, const DecodeArgs &a, const Merge
     }
     if (e != hipSuccess)
         return e;
-    hipLaunchKernelGGL(merge_kernel, dim3(n_pairs * m.G), dim3(m.D), 0, st, m);
+    // merge groups: about 16 slots per group for the longest merge
+    int k_max = 1;
+    for (int q = 0; q < n_pairs / m.Hkv; q++)
+        k_max = std::max(k_max, (m.wave_start[q + 1] - m.wave_start[q]) / m.Hkv);
+    int P = 1;
+    while (P * 2 * m.D <= MERGE_MAX_THREADS && P * 16 < k_max)
+        P *= 2;
+    hipLaunchKernelGGL(merge_kernel, dim3(n_pairs * m.G), dim3(P * m.D), 0, st, m);
     return hipGetLastError();
 }
 

@@ -465,7 +465,7 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(D <=
 // Log-sum-exp merge of the partials of one (sequence, kv head) pair for one
 // query head: workgroup = (pair, head), P groups of one thread per output
 // channel.  The slot weights 2^(m_j - M) go through LDS in chunks; group p
-// sums slots p, p+P, ... of a chunk, sixteen independent loads at a time, and
+// sums slots p, p+P, ... of a chunk, up to sixteen independent loads at a time, and
 // the groups' sums are added through LDS at the end.  P grows with the
 // slots per pair so that a long merge is not one thread's chain of loads.
 constexpr int MERGE_CHUNK = 512;
@@ -524,17 +524,23 @@ __global__ __launch_bounds__(MERGE_MAX_THREADS) void merge_kernel(const MergeArg
         __syncthreads();
         const float *pc = base + (int64_t)k0 * stride + c;
         int j = grp;
-        for (; j + 15 * P < chunk; j += 16 * P) {  // sixteen independent loads in flight
-            float v[16];
+        // batches of U independent loads in flight, U = 16, then 8, 4, 1
+        auto batch = [&](auto u_c) {
+            constexpr int U = decltype(u_c)::value;
+            for (; j + (U - 1) * P < chunk; j += U * P) {
+                float v[U];
 #pragma unroll
-            for (int u = 0; u < 16; u++)
-                v[u] = pc[(int64_t)(j + u * P) * stride];
+                for (int u = 0; u < U; u++)
+                    v[u] = pc[(int64_t)(j + u * P) * stride];
 #pragma unroll
-            for (int u = 0; u < 16; u++)
-                acc += v[u] * wts[j + u * P];
-        }
-        for (; j < chunk; j += P)
-            acc += pc[(int64_t)j * stride] * wts[j];
+                for (int u = 0; u < U; u++)
+                    acc += v[u] * wts[j + u * P];
+            }
+        };
+        batch(std::integral_constant<int, 16>());
+        batch(std::integral_constant<int, 8>());
+        batch(std::integral_constant<int, 4>());
+        batch(std::integral_constant<int, 1>());
     }
     const float L = block_reduce(lsum, red, false);
     if (P > 1) {

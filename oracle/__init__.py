@@ -23,11 +23,12 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "kvq_oracle.c")
 _LIB = os.path.join(_HERE, "libkvq_oracle.so")
 
-F16, Q8_0, Q4_0, Q5_0 = 0, 1, 2, 3
-TYPES = {"f16": F16, "q8_0": Q8_0, "q4_0": Q4_0, "q5_0": Q5_0}
+F16, Q8_0, Q4_0, Q5_0, TURBO3 = 0, 1, 2, 3, 4
+TYPES = {"f16": F16, "q8_0": Q8_0, "q4_0": Q4_0, "q5_0": Q5_0, "turbo3": TURBO3}
 ROLE_K, ROLE_V = 0, 1
-# q5_0 blocks: 16 nibble bytes, then the 32 high bits as 4 little-endian bytes
-BLOCK_CODE_BYTES = {F16: 64, Q8_0: 32, Q4_0: 16, Q5_0: 20}
+# q5_0 blocks: 16 nibble bytes, then the 32 high bits as 4 little-endian bytes;
+# turbo3: 8 bytes of 2-bit planes, then the 32 third bits
+BLOCK_CODE_BYTES = {F16: 64, Q8_0: 32, Q4_0: 16, Q5_0: 20, TURBO3: 12}
 
 _lock = threading.Lock()
 _lib = None
@@ -70,6 +71,7 @@ def lib():
             L.kvqo_f16_to_f32_n.argtypes = [vp, vp, i64]
             L.kvqo_quantize_blocks.argtypes = [i32, vp, i64, vp, vp]
             L.kvqo_dequantize_blocks.argtypes = [i32, vp, vp, i64, vp]
+            L.kvqo_wht32.argtypes = [vp, vp]
             L.kvqo_capacity.argtypes = [i64]
             L.kvqo_capacity.restype = i64
             L.kvqo_row_code_bytes.argtypes = [i32, i64]
@@ -128,9 +130,17 @@ def quantize_blocks(t, x_bits) -> tuple[np.ndarray, np.ndarray]:
     return d, codes
 
 
+def wht32(x) -> np.ndarray:
+    """H x for the 32-point Sylvester Hadamard matrix (turbo3's rotation), binary64."""
+    x = np.ascontiguousarray(x, dtype=np.float64).reshape(32)
+    y = np.empty(32, dtype=np.float64)
+    lib().kvqo_wht32(_ptr(x), _ptr(y))
+    return y
+
+
 def dequantize_blocks(t, d_bits, codes) -> np.ndarray:
     """Dequantized values [n, 32] in float64: d*q (q8_0), d*(c-8) (q4_0),
-    d*(c-16) (q5_0)."""
+    d*(c-16) (q5_0); turbo3 undoes the rotation of d*L[c]."""
     t = _type_id(t)
     d = np.ascontiguousarray(d_bits, dtype=np.uint16).reshape(-1)
     c = np.ascontiguousarray(codes, dtype=np.uint8).reshape(d.size, BLOCK_CODE_BYTES[t])
@@ -162,6 +172,7 @@ class OracleLayer:
 
     def __init__(self, k_type, v_type, n_seqs, n_q_heads, n_kv_heads, head_dim, max_ctx):
         self.k_type, self.v_type = _type_id(k_type), _type_id(v_type)
+        assert self.k_type != TURBO3, "turbo3 is a values-only type"
         self.shape = Shape(n_seqs, n_q_heads, n_kv_heads, head_dim, max_ctx)
         kc, ks = plane_bytes(self.k_type, n_seqs, n_kv_heads, head_dim, max_ctx)
         vc, vs = plane_bytes(self.v_type, n_seqs, n_kv_heads, head_dim, max_ctx)

@@ -49,6 +49,25 @@
  *     code = clamp(trunc(x*id + 16.5), 0, 31), value d*(code - 16); 22 bytes
  *     per 32 elements (16 bytes of low nibbles in q4_0's order, 32 high bits,
  *     the binary16 scale).  Parity with llama.cpp's own q5_0 is unpinned.
+ *   - turbo3 (values only): the page "Benchmark TurboQuant en Apple
+ *     Silicon" (section "Que es TurboQuant?") names a random rotation by the
+ *     Walsh-Hadamard transform to make the data Gaussian, an optimal scalar
+ *     quantizer, 3 bits per value, keys kept at q8_0.  Nothing more of the
+ *     format is on the page; the reading taken, per 32-element block:
+ *       y = H * (s . x), H the 32x32 Sylvester Hadamard matrix
+ *         (H[k][i] = (-1)^popcount(k & i)), s_i = -1 where bit i of
+ *         TQ3_SIGNS is set; computed in binary64, which is exact here
+ *         (binary16 inputs: every partial sum is a multiple of 2^-24 below
+ *         2^21);
+ *       codebook: the 8 Lloyd-Max levels of N(0,1), rounded to binary16;
+ *       d = f16(f32(max_k |y_k|) / L_7) (the block maximum lands on the
+ *         outermost level), id = d ? 1/d : 0;
+ *       code_k = number of midpoints (L_j + L_j+1)/2 that f32(y_k) * id
+ *         reaches (>=), so the nearest level, 0..7;
+ *       value: x^ = (1/32) * s . (H * (d * L[code])).
+ *     Stored as a 2-bit plane (byte j of a block: elements j, j+8, j+16,
+ *     j+24 at bits 0, 2, 4, 6) and a 32-bit word of the codes' third bits
+ *     (bit i = element i): 14 bytes per 32 elements with the scale.
  *   - Attention: flash attention is exactly standard softmax attention
  *     ([Tokios] Flash Attention: mathematically equivalent, no
  *     approximation), so decode is textbook softmax attention over the
@@ -67,6 +86,8 @@
  *       U = R/w units per row, unit u of token t at unit index
  *       (((s*H + h)*(Tc/8) + t/8)*U + u)*8 + t%8;
  *       scale of block b at (((s*H + h)*(Tc/8) + t/8)*nb + b)*8 + t%8.
+ *   turbo3: row code bytes R = D/4 (the 2-bit planes), then the third-bit
+ *   words exactly as q5_0's high-bit words below.
  *   q5_0: the code stream holds the nibble rows exactly as q4_0 does, then,
  *   from byte S*H*Tc*R on, one little-endian 32-bit word of high bits per
  *   (token, block), indexed like that block's scale (bit i = bit 4 of the
@@ -83,6 +104,12 @@
 #define KVQO_Q8_0 1
 #define KVQO_Q4_0 2
 #define KVQO_Q5_0 3
+#define KVQO_TQ3 4
+
+/* turbo3: rotation signs and the binary16 bits of the Lloyd-Max levels of
+ * N(0,1) for 8 levels (+-0.2451, +-0.7560, +-1.3439, +-2.1519 rounded). */
+#define TQ3_SIGNS 0x9E3779B9u
+static const uint16_t TQ3_LEVELS[8] = {0xC04E, 0xBD60, 0xBA0C, 0xB3D8, 0x33D8, 0x3A0C, 0x3D60, 0x404E};
 #define KVQO_ROLE_K 0
 #define KVQO_ROLE_V 1
 
@@ -246,6 +273,62 @@ void kvqo_quantize_q5_0(const uint16_t *x16, uint16_t *d_out, uint8_t *packed, u
     *d_out = d16;
 }
 
+/* The 32-point Walsh-Hadamard transform in Sylvester order, in place,
+ * butterflies of span 1, 2, 4, 8, 16 (binary64). */
+static void wht32(double *v)
+{
+    for (int len = 1; len < 32; len <<= 1)
+        for (int i = 0; i < 32; i += 2 * len)
+            for (int k = i; k < i + len; k++) {
+                double a = v[k], b = v[k + len];
+                v[k] = a + b;
+                v[k + len] = a - b;
+            }
+}
+
+/* exported for the tests: out = H * in (binary64) */
+void kvqo_wht32(const double *in, double *out)
+{
+    memcpy(out, in, 32 * sizeof(double));
+    wht32(out);
+}
+
+/* turbo3 block: 8 bytes of 2-bit planes + 4 bytes (little-endian) of third bits. */
+void kvqo_quantize_tq3(const uint16_t *x16, uint16_t *d_out, uint8_t *packed)
+{
+    double y[32];
+    for (int i = 0; i < 32; i++) {
+        double x = (double)kvqo_f16_to_f32(x16[i]);
+        y[i] = ((TQ3_SIGNS >> i) & 1u) ? -x : x;
+    }
+    wht32(y);
+    double m = 0.0;
+    for (int k = 0; k < 32; k++)
+        if (fabs(y[k]) > m)
+            m = fabs(y[k]);
+    float lmax = kvqo_f16_to_f32(TQ3_LEVELS[7]);
+    float d32 = (float)m / lmax;
+    uint16_t d16 = kvqo_f32_to_f16(d32);
+    float d = kvqo_f16_to_f32(d16);
+    float id = (d != 0.0f) ? 1.0f / d : 0.0f;
+    float mid[7];
+    for (int j = 0; j < 7; j++)
+        mid[j] = (kvqo_f16_to_f32(TQ3_LEVELS[j]) + kvqo_f16_to_f32(TQ3_LEVELS[j + 1])) * 0.5f; /* exact */
+    memset(packed, 0, 12);
+    uint32_t hi = 0;
+    for (int k = 0; k < 32; k++) {
+        float t = (float)y[k] * id;
+        int c = 0;
+        for (int j = 0; j < 7; j++)
+            c += (t >= mid[j]);
+        packed[k % 8] |= (uint8_t)((c & 3) << (2 * (k / 8)));
+        hi |= (uint32_t)(c >> 2) << k;
+    }
+    for (int b = 0; b < 4; b++)
+        packed[8 + b] = (uint8_t)(hi >> (8 * b));
+    *d_out = d16;
+}
+
 /* f16 "quantizer": the block is stored as is. */
 static void store_f16_block(const uint16_t *x16, uint8_t *codes)
 {
@@ -254,8 +337,10 @@ static void store_f16_block(const uint16_t *x16, uint8_t *codes)
 
 int kvqo_block_code_bytes(int type)
 {
-    /* q5_0: 16 nibble bytes, then the 32 high bits as 4 little-endian bytes */
-    return type == KVQO_F16 ? 64 : type == KVQO_Q8_0 ? 32 : type == KVQO_Q4_0 ? 16 : type == KVQO_Q5_0 ? 20 : -1;
+    /* q5_0: 16 nibble bytes, then the 32 high bits as 4 little-endian bytes;
+     * turbo3: 8 bytes of 2-bit planes, then the 32 third bits */
+    return type == KVQO_F16 ? 64 : type == KVQO_Q8_0 ? 32 : type == KVQO_Q4_0 ? 16 : type == KVQO_Q5_0 ? 20
+         : type == KVQO_TQ3 ? 12 : -1;
 }
 
 /* Contiguous blocks: x [n][32] -> codes [n][block_code_bytes], d [n]. */
@@ -272,6 +357,8 @@ void kvqo_quantize_blocks(int type, const uint16_t *x, int64_t n, uint16_t *d, u
             kvqo_quantize_q5_0(x + 32 * i, d + i, codes + cb * i, &qh);
             for (int k = 0; k < 4; k++)
                 codes[cb * i + 16 + k] = (uint8_t)(qh >> (8 * k));
+        } else if (type == KVQO_TQ3) {
+            kvqo_quantize_tq3(x + 32 * i, d + i, codes + cb * i);
         } else {
             store_f16_block(x + 32 * i, codes + cb * i);
             d[i] = 0;
@@ -297,12 +384,36 @@ static double dequant_elem(int type, uint16_t d16, const uint8_t *bc, int e)
     return d * (double)(c - 16);
 }
 
+/* turbo3: the whole block (the rotation mixes its elements), binary64. */
+static void dequant_tq3(uint16_t d16, const uint8_t *bc, double *out)
+{
+    double d = (double)kvqo_f16_to_f32(d16);
+    uint32_t hi = (uint32_t)bc[8] | ((uint32_t)bc[9] << 8) | ((uint32_t)bc[10] << 16) | ((uint32_t)bc[11] << 24);
+    double y[32];
+    for (int k = 0; k < 32; k++) {
+        int c = ((bc[k % 8] >> (2 * (k / 8))) & 3) | (int)(((hi >> k) & 1u) << 2);
+        y[k] = d * (double)kvqo_f16_to_f32(TQ3_LEVELS[c]);
+    }
+    wht32(y); /* H is symmetric and H*H = 32 I */
+    for (int i = 0; i < 32; i++)
+        out[i] = (((TQ3_SIGNS >> i) & 1u) ? -y[i] : y[i]) / 32.0;
+}
+
+static void dequant_block(int type, uint16_t d16, const uint8_t *bc, double *out)
+{
+    if (type == KVQO_TQ3) {
+        dequant_tq3(d16, bc, out);
+        return;
+    }
+    for (int e = 0; e < 32; e++)
+        out[e] = dequant_elem(type, d16, bc, e);
+}
+
 void kvqo_dequantize_blocks(int type, const uint16_t *d, const uint8_t *codes, int64_t n, double *out)
 {
     int cb = kvqo_block_code_bytes(type);
     for (int64_t i = 0; i < n; i++)
-        for (int e = 0; e < 32; e++)
-            out[32 * i + e] = dequant_elem(type, d[i], codes + cb * i, e);
+        dequant_block(type, d[i], codes + cb * i, out + 32 * i);
 }
 
 /* ------------------------------------------------------------------ */
@@ -324,15 +435,19 @@ int64_t kvqo_capacity(int64_t max_ctx) { return (max_ctx + 31) / 32 * 32; }
 
 int64_t kvqo_row_code_bytes(int type, int64_t D)
 {
-    return type == KVQO_F16 ? 2 * D : type == KVQO_Q8_0 ? D : D / 2; /* q5_0: nibble rows */
+    /* q5_0: nibble rows; turbo3: 2-bit plane rows */
+    return type == KVQO_F16 ? 2 * D : type == KVQO_Q8_0 ? D : type == KVQO_TQ3 ? D / 4 : D / 2;
 }
+
+/* Types whose code stream continues with one 32-bit word per (row, block). */
+static int has_bit_words(int type) { return type == KVQO_Q5_0 || type == KVQO_TQ3; }
 
 void kvqo_plane_bytes(int type, int64_t n_seqs, int64_t n_kv_heads, int64_t head_dim, int64_t max_ctx,
                       int64_t *codes_bytes, int64_t *scale_bytes)
 {
     int64_t rows = n_seqs * n_kv_heads * kvqo_capacity(max_ctx);
     *codes_bytes = rows * kvqo_row_code_bytes(type, head_dim);
-    if (type == KVQO_Q5_0)
+    if (has_bit_words(type))
         *codes_bytes += rows * (head_dim / 32) * 4; /* the high-bit words */
     *scale_bytes = (type == KVQO_F16) ? 0 : rows * (head_dim / 32) * 2;
 }
@@ -386,12 +501,12 @@ void kvqo_append(const kvqo_plane *p, const kvqo_shape *sh, const uint16_t *x, i
                     uint8_t bc[64];
                     uint16_t d16 = 0;
                     kvqo_quantize_blocks(p->type, row + 32 * b, 1, &d16, bc);
-                    int nib = (p->type == KVQO_Q5_0) ? 16 : cb; /* bytes that live in the rows */
+                    int nib = has_bit_words(p->type) ? cb - 4 : cb; /* bytes that live in the rows */
                     for (int r = 0; r < nib; r++)
                         p->codes[code_byte_addr(p, sh, s, h, t, (int64_t)b * nib + r)] = bc[r];
-                    if (p->type == KVQO_Q5_0)
+                    if (has_bit_words(p->type))
                         for (int k = 0; k < 4; k++)
-                            p->codes[qh_byte_addr(p, sh, s, h, t, b) + k] = bc[16 + k];
+                            p->codes[qh_byte_addr(p, sh, s, h, t, b) + k] = bc[nib + k];
                     if (p->type != KVQO_F16)
                         p->scales[scale_index(p, sh, s, h, t, b)] = d16;
                 }
@@ -408,15 +523,14 @@ void kvqo_read_rows(const kvqo_plane *p, const kvqo_shape *sh, int s, int h, int
         int64_t t = t0 + k;
         for (int b = 0; b < nb; b++) {
             uint8_t bc[64];
-            int nib = (p->type == KVQO_Q5_0) ? 16 : cb;
+            int nib = has_bit_words(p->type) ? cb - 4 : cb;
             for (int r = 0; r < nib; r++)
                 bc[r] = p->codes[code_byte_addr(p, sh, s, h, t, (int64_t)b * nib + r)];
-            if (p->type == KVQO_Q5_0)
+            if (has_bit_words(p->type))
                 for (int k = 0; k < 4; k++)
-                    bc[16 + k] = p->codes[qh_byte_addr(p, sh, s, h, t, b) + k];
+                    bc[nib + k] = p->codes[qh_byte_addr(p, sh, s, h, t, b) + k];
             uint16_t d16 = (p->type == KVQO_F16) ? 0 : p->scales[scale_index(p, sh, s, h, t, b)];
-            for (int e = 0; e < 32; e++)
-                out[k * D + 32 * b + e] = dequant_elem(p->type, d16, bc, e);
+            dequant_block(p->type, d16, bc, out + k * D + 32 * b);
         }
     }
 }

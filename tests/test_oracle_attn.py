@@ -19,6 +19,8 @@ import pytest
 import torch
 
 PAIRS = list(itertools.product(["f16", "q8_0", "q4_0", "q5_0"], repeat=2))
+# turbo3 is a values-only type
+PAIRS += [(k, "turbo3") for k in ["f16", "q8_0", "q4_0", "q5_0"]]
 
 
 def rand_f16(rng, shape, scale=1.0):
@@ -78,14 +80,14 @@ def test_quantized_decode_equals_sdpa_over_dequantized(orc, kt, vt):
         np.testing.assert_allclose(out[s], sdpa_ref(q, Kd, Vd, ctx[s], 0.125, Hq // Hkv), rtol=1e-12, atol=1e-12)
 
 
-@pytest.mark.parametrize("t", ["K", "V"])
-@pytest.mark.parametrize("typ", ["f16", "q8_0", "q4_0", "q5_0"])
+@pytest.mark.parametrize("t,typ", [(t, typ) for t in ("K", "V") for typ in ("f16", "q8_0", "q4_0", "q5_0")]
+                         + [("V", "turbo3")])
 def test_rows_read_back_as_their_blocks(orc, t, typ):
     """append writes each row's blocks; read_rows returns their dequantized
     values (block quantizer applied row by row, independent of layout)."""
     rng = np.random.default_rng(2)
     S, Hkv, D, T = 2, 3, 64, 40
-    lay, K, V = build(orc, typ, typ, S, 3, Hkv, D, T, rng)
+    lay, K, V = build(orc, "q8_0" if typ == "turbo3" else typ, typ, S, 3, Hkv, D, T, rng)
     X = K if t == "K" else V
     for s in range(S):
         for h in range(Hkv):
@@ -98,9 +100,9 @@ def numpy_read_plane(codes, scales, typ, role, S, H, D, max_ctx):
     """Loop-free numpy reading of a plane from the header's layout formula."""
     Tc = (max_ctx + 31) // 32 * 32
     nb = D // 32
-    R = {"f16": 2 * D, "q8_0": D, "q4_0": D // 2, "q5_0": D // 2}[typ]
+    R = {"f16": 2 * D, "q8_0": D, "q4_0": D // 2, "q5_0": D // 2, "turbo3": D // 4}[typ]
     qh = None
-    if typ == "q5_0":
+    if typ in ("q5_0", "turbo3"):
         # the nibble rows, then one 32-bit high-bit word per (row, block),
         # indexed like the scales
         n_rows = S * H * Tc
@@ -128,6 +130,16 @@ def numpy_read_plane(codes, scales, typ, role, S, H, D, max_ctx):
         q = blk.view(np.int8).astype(np.float64)
     elif typ == "q4_0":
         q = np.concatenate([(blk & 0xF), (blk >> 4)], axis=-1).astype(np.float64) - 8
+    elif typ == "turbo3":
+        # element k: 2 bits at (byte k%8, bits 2*(k//8)), third bit k of the word
+        lo = np.stack([(blk[..., k % 8] >> (2 * (k // 8))) & 3 for k in range(32)], axis=-1).astype(np.int64)
+        hi = (qh[..., None].astype(np.int64) >> np.arange(32)) & 1
+        levels = np.array([-2.152, -1.344, -0.756, -0.2451, 0.2451, 0.756, 1.344, 2.152], np.float16)
+        yh = levels.astype(np.float64)[lo | (hi << 2)] * d[..., None]
+        k = np.arange(32)
+        Hm = (-1.0) ** np.array([[bin(a & b).count("1") for b in k] for a in k])  # Sylvester Hadamard
+        sg = np.array([-1.0 if (0x9E3779B9 >> i) & 1 else 1.0 for i in range(32)])  # rotation signs
+        return ((yh @ Hm.T) * sg / 32).reshape(S, H, Tc, D)
     else:
         lo = np.concatenate([(blk & 0xF), (blk >> 4)], axis=-1).astype(np.int64)
         hi = (qh[..., None].astype(np.int64) >> np.arange(32)) & 1

@@ -17,6 +17,7 @@ import oracle
 from mixed_precision_quantized_quantize_amd import synth
 
 TYPES = ["f16", "q8_0", "q5_0", "q4_0"]
+V_TYPES = TYPES + ["turbo3"]  # turbo3 stores values only
 
 
 def rel_errors(wname, n_tok, n_seqs):
@@ -26,7 +27,7 @@ def rel_errors(wname, n_tok, n_seqs):
     Kb, Vb, Qb = synth.as_bits(K), synth.as_bits(V), synth.as_bits(Q)
     ctx = np.full(n_seqs, n_tok, np.int32)
     outs = {}
-    for kt, vt in itertools.product(TYPES, repeat=2):
+    for kt, vt in itertools.product(TYPES, V_TYPES):
         orc = oracle.OracleLayer(kt, vt, n_seqs, w.n_q_heads, w.n_kv_heads, w.head_dim, n_tok)
         orc.append(Kb, Vb, np.zeros(n_seqs, np.int32))
         outs[(kt, vt)] = orc.attn_decode(Qb, ctx, w.scale)
@@ -35,8 +36,8 @@ def rel_errors(wname, n_tok, n_seqs):
 
 
 def check_ordering(err, what):
-    rows = "\n".join(f"  K {kt:5s} V {vt:5s}  rel. RMS error {err[(kt, vt)]:.3e}"
-                     for kt, vt in itertools.product(TYPES, repeat=2))
+    rows = "\n".join(f"  K {kt:5s} V {vt:6s}  rel. RMS error {err[(kt, vt)]:.3e}"
+                     for kt, vt in itertools.product(TYPES, V_TYPES))
     print(f"\n{what}\n{rows}")
     assert err[("f16", "f16")] == 0.0
     # keys are the sensitive half: the same bits spent on K lose less
@@ -49,6 +50,9 @@ def check_ordering(err, what):
     # q5_0, the middle ground the llama.cpp issue's thread reports, sits between
     assert err[("q8_0", "q8_0")] < err[("q5_0", "q5_0")] < err[("q4_0", "q4_0")], what
     assert err[("q8_0", "q4_0")] < err[("q5_0", "q4_0")] < err[("q4_0", "q4_0")], what
+    # turbo3 values (3.5 bits) lose more than q4_0 values, yet K8 + turbo3 V
+    # still beats 4-bit keys with 8-bit values: the page's keys-first point
+    assert err[("q8_0", "q4_0")] < err[("q8_0", "turbo3")] < err[("q4_0", "q8_0")], what
 
 
 def test_keys_more_sensitive_outlier_channels():

@@ -1,6 +1,7 @@
 /*
  * kvq.h -- C ABI of libkvq: a KV cache whose keys and values are stored at
- * independently chosen precisions (f16, q8_0, q5_0, q4_0), with a quantizing
+ * independently chosen precisions (f16, q8_0, q5_0, q4_0; turbo3 for
+ * values), with a quantizing
  * append and flash attention (decode and causal chunked prefill) that reads
  * the quantized blocks directly.  Built for AMD Instinct MI355X (gfx950).
  *
@@ -24,6 +25,10 @@
  *    its comment thread, q5_0 named as the working middle ground between
  *    q8_0 and q4_0 (the format itself is not on the pages: ggml's 5-bit
  *    block, read the way q4_0 is read below).
+ *  - "Benchmark TurboQuant en Apple Silicon" (asiai.dev), section "Que es
+ *    TurboQuant?": values compressed to 3 bits after a random Walsh-Hadamard
+ *    rotation and an optimal scalar quantizer, keys kept at q8_0 -- the
+ *    values-only type turbo3 below (the format itself is a reading).
  *
  * Conventions for every entry point:
  *  - All tensors live in device memory owned by the caller; the library
@@ -50,9 +55,12 @@
  *    q4_0: 16 bytes, byte i = c_i | c_(i+16) << 4 (4-bit codes) + binary16
  *    scale d, x^ = d*(c-8); q5_0: 5-bit codes c, their low 4 bits packed as
  *    q4_0's, their fifth bits in a 32-bit word (bit i = element i), +
- *    binary16 scale d, x^ = d*(c-16).  Row code bytes R = 2D, D, D/2 or D/2
- *    (q5_0: the nibbles); block b of a row occupies code bytes
- *    [b*R/nb, (b+1)*R/nb).
+ *    binary16 scale d, x^ = d*(c-16); turbo3 (V planes only): 3-bit codes of
+ *    the rotated block, their low 2 bits in 8 bytes (byte j: elements j,
+ *    j+8, j+16, j+24 at bits 0, 2, 4, 6), their third bits in a 32-bit word
+ *    (bit i = element i), + binary16 scale d (see Quantization).  Row code
+ *    bytes R = 2D, D, D/2, D/2 (q5_0: the nibbles) or D/4 (turbo3: the
+ *    2-bit planes); block b of a row occupies code bytes [b*R/nb, (b+1)*R/nb).
  *  - K plane ("token-major"): code byte r of token t at
  *        codes + (pair*Tc + t)*R + r;
  *    scale of block b at  scales + 2*((pair*Tc + t)*nb + b).
@@ -62,14 +70,16 @@
  *    value) and 1 byte otherwise, U = R/w units per row, unit u of token t
  *    at  codes + w*((((pair*(Tc/8)) + t/8)*U + u)*8 + t%8);
  *    scale of block b at  scales + 2*(((pair*(Tc/8) + t/8)*nb + b)*8 + t%8).
- *  - q5_0 high-bit words: in the codes allocation after the S*H*Tc*R bytes
+ *  - q5_0 high-bit words and turbo3 third-bit words: in the codes allocation after the S*H*Tc*R bytes
  *    of rows, one little-endian uint32 per (token, block), at the index of
  *    that block's scale:  codes + S*H*Tc*R + 4*(scale index).
- *  - Plane bytes: codes S*H*Tc*R (+ S*H*Tc*nb*4 for q5_0), scales
+ *  - Plane bytes: codes S*H*Tc*R (+ S*H*Tc*nb*4 for q5_0 and turbo3), scales
  *    S*H*Tc*nb*2 (0 for f16).  With
  *    max_ctx a multiple of 32 nothing is padded: q8_0 costs 34 B and q4_0
  *    18 B per 32 elements, the sizes behind the KVSplit page's 176 / 93.5 /
- *    71.5 / 49.5 MiB and the issue's 816 + 432 MiB; q5_0 costs 22 B.
+ *    71.5 / 49.5 MiB and the issue's 816 + 432 MiB; q5_0 costs 22 B and
+ *    turbo3 14 B (the TurboQuant page's ~4 GB KV at 32K tokens for a 70B
+ *    model with q8_0 keys).
  *
  * Quantization (the ggml q8_0 / q4_0 block formats of the cache types named
  * on the llama.cpp pages), bit-exact, in binary32 unless stated:
@@ -80,6 +90,14 @@
  *        c = clamp(trunc((x*id) + 8.5), 0, 15), product and sum rounded
  *        separately (no fused multiply-add).
  *  q5_0: as q4_0 with d = f16(m/-16) and c = clamp(trunc((x*id) + 16.5), 0, 31).
+ *  turbo3: y = H*(s.x) for the 32x32 Sylvester Hadamard matrix H
+ *        (H[k][i] = (-1)^popcount(k&i)) and s_i = -1 where bit i of
+ *        0x9E3779B9 is set, exact (binary64 arithmetic); levels L = the
+ *        8-level Lloyd-Max quantizer of N(0,1) in binary16 (+-0.2451,
+ *        +-0.756, +-1.344, +-2.152); d = f16(f32(max|y|)/L[7]);
+ *        id = d ? 1/d : 0; code = #{j : f32(y)*id >= (L[j]+L[j+1])/2};
+ *        x^ = s.(H*(d*L[code]))/32.  Attention accumulates P.V in the
+ *        rotated basis and rotates each output block back once.
  *  f16 (the conversion) rounds to nearest even.
  */
 #ifndef KVQ_H
@@ -93,12 +111,13 @@ extern "C" {
 #endif
 
 /* Cache element types (llama.cpp's --cache-type-k / --cache-type-v values). */
-typedef enum kvq_type { KVQ_F16 = 0, KVQ_Q8_0 = 1, KVQ_Q4_0 = 2, KVQ_Q5_0 = 3 } kvq_type;
+typedef enum kvq_type { KVQ_F16 = 0, KVQ_Q8_0 = 1, KVQ_Q4_0 = 2, KVQ_Q5_0 = 3, KVQ_TURBO3 = 4 } kvq_type;
 
 enum {
     KVQ_OK = 0,
     KVQ_E_ARG = -1,       /* NULL or misaligned pointer, malformed argument   */
-    KVQ_E_TYPE = -2,      /* unknown type, or type differs from the plane's   */
+    KVQ_E_TYPE = -2,      /* unknown type, type differs from the plane's, or
+                             turbo3 on a K plane                              */
     KVQ_E_SHAPE = -3,     /* unsupported head_dim / head grouping / counts    */
     KVQ_E_RANGE = -4,     /* layer, position or context length out of range   */
     KVQ_E_WORKSPACE = -5, /* workspace NULL or smaller than required          */

@@ -17,8 +17,8 @@ import threading
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libkvq.so")
 
-F16, Q8_0, Q4_0, Q5_0 = 0, 1, 2, 3
-TYPES = {"f16": F16, "q8_0": Q8_0, "q4_0": Q4_0, "q5_0": Q5_0}
+F16, Q8_0, Q4_0, Q5_0, TURBO3 = 0, 1, 2, 3, 4
+TYPES = {"f16": F16, "q8_0": Q8_0, "q4_0": Q4_0, "q5_0": Q5_0, "turbo3": TURBO3}  # turbo3: values only
 TYPE_NAMES = {v: k for k, v in TYPES.items()}
 
 KVQ_OK, KVQ_E_ARG, KVQ_E_TYPE, KVQ_E_SHAPE, KVQ_E_RANGE, KVQ_E_WORKSPACE, KVQ_E_HIP = 0, -1, -2, -3, -4, -5, -6

@@ -16,12 +16,15 @@ using namespace kvq;
 
 namespace {
 
-bool valid_type(int32_t t) { return t == KVQ_F16 || t == KVQ_Q8_0 || t == KVQ_Q4_0 || t == KVQ_Q5_0; }
+bool valid_type(int32_t t)
+{
+    return t == KVQ_F16 || t == KVQ_Q8_0 || t == KVQ_Q4_0 || t == KVQ_Q5_0 || t == KVQ_TURBO3;
+}
 
 // q5_0's high-bit words follow the nibble rows in the codes allocation.
 uint32_t *high_bits(const kvq_shape &sh, const kvq_plane &p)
 {
-    if (p.type != KVQ_Q5_0)
+    if (!has_bit_words(p.type))
         return nullptr;
     const int64_t rows = (int64_t)sh.n_seqs * sh.n_kv_heads * capacity(sh.max_ctx);
     return reinterpret_cast<uint32_t *>(static_cast<uint8_t *>(p.codes) + rows * row_code_bytes(p.type, sh.head_dim));
@@ -70,6 +73,8 @@ int check_cache(const kvq_cache *c)
     for (int l = 0; l < c->shape.n_layers; l++) {
         if ((rc = check_plane(&c->k[l])) || (rc = check_plane(&c->v[l])))
             return rc;
+        if (c->k[l].type == KVQ_TURBO3)  // a values-only type
+            return KVQ_E_TYPE;
     }
     return KVQ_OK;
 }
@@ -181,7 +186,7 @@ int kvq_plane_bytes(const kvq_shape *shape, int32_t type, size_t *codes_bytes, s
         return KVQ_E_TYPE;
     const int64_t rows = (int64_t)shape->n_seqs * shape->n_kv_heads * capacity(shape->max_ctx);
     *codes_bytes = (size_t)(rows * row_code_bytes(type, shape->head_dim));
-    if (type == KVQ_Q5_0)
+    if (has_bit_words(type))
         *codes_bytes += (size_t)(rows * (shape->head_dim / 32) * 4);
     *scale_bytes = (type == KVQ_F16) ? 0 : (size_t)(rows * (shape->head_dim / 32) * 2);
     return KVQ_OK;
@@ -306,6 +311,7 @@ int attn_decode(const kvq_cache *cache, int32_t layer, const void *K, const void
     m.Hkv = a.Hkv;
     m.G = a.G;
     m.D = sh.head_dim;
+    m.v_rotated = vp.type == KVQ_TURBO3;
     memcpy(m.wave_start, a.wave_start, sizeof(int32_t) * (sh.n_seqs + 1));
     hipError_t e = launch_decode(kp.type, vp.type, sh.head_dim, a, m, sh.n_seqs * sh.n_kv_heads, (hipStream_t)stream);
     return e == hipSuccess ? KVQ_OK : KVQ_E_HIP;

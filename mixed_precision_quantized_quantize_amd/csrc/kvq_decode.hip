@@ -133,7 +133,7 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(D <=
         rs.vs = make_rsrc(a.vs + pair * Tc * NB, Tc * NB * 2);
     if (KT == KVQ_Q5_0)
         rs.kh = make_rsrc(a.kqh + pair * Tc * NB, Tc * NB * 4);
-    if (VT == KVQ_Q5_0)
+    if (has_bit_words(VT))
         rs.vh = make_rsrc(a.vqh + pair * Tc * NB, Tc * NB * 4);
 
     // Q^T operand: lane (n = head, j) holds 8 channels of each block (the
@@ -178,11 +178,12 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(D <=
         }
     }
     constexpr bool VNIB = VT == KVQ_Q4_0 || VT == KVQ_Q5_0;  // nibble-packed V
-    constexpr int VL = VNIB ? NB : NCT;  // V operand reads per tile
+    constexpr int VL = (VNIB || VT == KVQ_TURBO3) ? NB : NCT;  // V operand reads per tile
     int v_rd[VL];
 #pragma unroll
     for (int i = 0; i < VL; i++) {
-        const int u = 16 * i + n;  // q4_0 / q5_0: byte n of block i; else channel 16i+n
+        // q4_0 / q5_0: byte n of block i; turbo3: byte n&7 of block i; else channel 16i+n
+        const int u = (VT == KVQ_TURBO3) ? 8 * i + (n & 7) : 16 * i + n;
         const int c = (VT == KVQ_F16) ? u : (u >> 1);
         const int within = (VT == KVQ_F16) ? 0 : 8 * (u & 1);
         v_rd[i] = g::V_OFF + (j * g::CPG + (c ^ vswz<VT, g::CPG>(j))) * 16 + within;
@@ -207,7 +208,7 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(D <=
         u32x4 v[VL];                    // V codes per read
         u32x4 vs[NB];                   // V scales: block b, tokens 0..7
         uint32_t kh[KT == KVQ_Q5_0 ? 2 : 1][KT == KVQ_Q5_0 ? NB : 1];     // q5_0 K high bits
-        uint32_t vh[VT == KVQ_Q5_0 ? NB : 1][VT == KVQ_Q5_0 ? 8 : 1];     // q5_0 V high bits, tokens 0..7
+        uint32_t vh[has_bit_words(VT) ? NB : 1][has_bit_words(VT) ? 8 : 1];  // V high / third bits, tokens 0..7
     };
     auto read_ops = [&](const uint8_t *buf, Ops &op) {
 #pragma unroll
@@ -254,7 +255,7 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(D <=
                     op.kh[T][b] = *reinterpret_cast<const uint32_t *>(buf + g::KH_OFF + (r * NB + b) * 4);
             }
         }
-        if constexpr (VT == KVQ_Q5_0) {
+        if constexpr (has_bit_words(VT)) {
 #pragma unroll
             for (int b = 0; b < NB; b++) {
                 const u32x4 *p = reinterpret_cast<const u32x4 *>(buf + g::VH_OFF + (j * NB + b) * 32);
@@ -367,6 +368,13 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(D <=
                 // as q4_0, each code's fifth bit from its token's high-bit word
                 half8 va0, va1;
                 v_operand_q5(u32x2{op.v[b].x, op.v[b].y}, op.vh[b], n, va0, va1);
+                o[2 * b] = mfma(va0, pb, o[2 * b]);
+                o[2 * b + 1] = mfma(va1, pb, o[2 * b + 1]);
+            } else if constexpr (VT == KVQ_TURBO3) {
+                // codebook levels of the rotated values: O accumulates in the
+                // rotated basis, the merge rotates it back
+                half8 va0, va1;
+                v_operand_tq3(u32x2{op.v[b].x, op.v[b].y}, op.vh[b], n, va0, va1);
                 o[2 * b] = mfma(va0, pb, o[2 * b]);
                 o[2 * b + 1] = mfma(va1, pb, o[2 * b + 1]);
             } else {
@@ -550,8 +558,20 @@ __global__ __launch_bounds__(MERGE_MAX_THREADS) void merge_kernel(const MergeArg
             for (int g2 = 1; g2 < P; g2++)
                 acc += part[g2 * D + c];
     }
+    float r = acc / L;
+    if (a.v_rotated && grp == 0) {
+        // turbo3 values: rotate each 32-channel block back, x = s.(H y)/32 --
+        // butterflies of span 1..16 across the 32 threads of the block
+        // (whole waves take this branch: D is a multiple of 64)
+#pragma unroll
+        for (int span = 1; span < 32; span <<= 1) {
+            const float o = __shfl_xor(r, span);
+            r = (c & span) ? o - r : r + o;
+        }
+        r = ((TQ3_SIGNS >> (c & 31)) & 1u) ? -r * 0.03125f : r * 0.03125f;
+    }
     if (grp == 0)
-        a.out[((int64_t)s * a.Hq + (int64_t)h * G + gg) * D + c] = acc / L;
+        a.out[((int64_t)s * a.Hq + (int64_t)h * G + gg) * D + c] = r;
 }
 
 template <int KT, int VT, int D>

@@ -135,6 +135,51 @@ __device__ inline void v_operand_q5(u32x2 w, const uint32_t (&h)[8], int n, half
     va1 = pack4(hi[0], hi[1], hi[2], hi[3]);
 }
 
+// turbo3 codebook: the 8 Lloyd-Max levels of N(0,1) in binary16 (-2.152,
+// -1.344, -0.756, -0.2451, 0.2451, 0.756, 1.344, 2.152), two per word with
+// the even entry in the low half.
+constexpr uint32_t TQ3_L01 = 0xBD60C04Eu, TQ3_L23 = 0xB3D8BA0Cu, TQ3_L45 = 0x3A0C33D8u, TQ3_L67 = 0x404E3D60u;
+
+// Two levels as one binary16 pair: z holds 2-bit codes in its bytes, pick is
+// the perm selector that repeats the pair's two bytes as [a, a, b, b], and
+// bit 0 of t0 / t1 is the third bit of the first / second code.
+__device__ inline uint32_t tq3_pair(uint32_t z, uint32_t pick, uint32_t t0, uint32_t t1)
+{
+    // byte selector of entry e: bytes 2e, 2e+1 of the 8-byte table half
+    const uint32_t sel = (__builtin_amdgcn_perm(z, z, pick) << 1) + 0x01000100u;
+    const uint32_t lo = __builtin_amdgcn_perm(TQ3_L23, TQ3_L01, sel);  // entries 0..3
+    const uint32_t hi = __builtin_amdgcn_perm(TQ3_L67, TQ3_L45, sel);  // entries 4..7
+    const uint32_t mask = ((t0 & 1u) ? 0x0000FFFFu : 0u) | ((t1 & 1u) ? 0xFFFF0000u : 0u);
+    return bfi(mask, hi, lo);
+}
+
+// turbo3 V operand of one block: the lane's code byte n&7 for tokens 0..7
+// in w (2-bit codes of elements n&7, +8, +16, +24 at bits 0, 2, 4, 6; tokens
+// 0..3 in w.x, 4..7 in w.y) and the tokens' third-bit words h[0..7] -> the
+// two operands (channel tiles of elements n and n+16) as binary16 levels.
+__device__ inline void v_operand_tq3(u32x2 w, const uint32_t (&h)[8], int n, half8 &va0, half8 &va1)
+{
+    const int sh0 = 2 * (n >> 3), sh1 = sh0 + 4;  // bit offsets of elements n and n+16
+    const uint32_t z0[2] = {(w.x >> sh0) & 0x03030303u, (w.y >> sh0) & 0x03030303u};
+    const uint32_t z1[2] = {(w.x >> sh1) & 0x03030303u, (w.y >> sh1) & 0x03030303u};
+    uint32_t s[8];
+#pragma unroll
+    for (int i = 0; i < 8; i++)
+        s[i] = h[i] >> n;  // bit 0: element n's third bit, bit 16: element n+16's
+    uint32_t r0[4], r1[4];
+#pragma unroll
+    for (int p = 0; p < 4; p++) {
+        const uint32_t pick = (p & 1) ? 0x03030202u : 0x01010000u;
+        r0[p] = tq3_pair(z0[p >> 1], pick, s[2 * p], s[2 * p + 1]);
+        r1[p] = tq3_pair(z1[p >> 1], pick, s[2 * p] >> 16, s[2 * p + 1] >> 16);
+    }
+    va0 = pack4(r0[0], r0[1], r0[2], r0[3]);
+    va1 = pack4(r1[0], r1[1], r1[2], r1[3]);
+}
+
+// turbo3's rotation signs: element i of a block is negated where bit i is set.
+constexpr uint32_t TQ3_SIGNS = 0x9E3779B9u;
+
 // K codes of one block for one lane -> A operand (8 channels of one token).
 template <int KT>
 __device__ inline half8 k_operand(const uint32_t *w)
@@ -170,20 +215,21 @@ __device__ inline int qk_chan(int j, int r)
 template <int KT, int VT, int D>
 struct Geo {
     static constexpr int NB = D / 32, NCT = D / 16;
-    static constexpr int RK = (KT == KVQ_F16) ? 2 * D : (KT == KVQ_Q8_0) ? D : D / 2;  // K row code bytes
-    static constexpr int RV = (VT == KVQ_F16) ? 2 * D : (VT == KVQ_Q8_0) ? D : D / 2;  // V row code bytes
+    static constexpr int RK = row_code_bytes(KT, D);  // K row code bytes
+    static constexpr int RV = row_code_bytes(VT, D);  // V row code bytes
     static constexpr int K_BYTES = TILE * RK;
     static constexpr int KS_BYTES = (KT == KVQ_F16) ? 0 : TILE * NB * 2;
     static constexpr int KH_BYTES = (KT == KVQ_Q5_0) ? TILE * NB * 4 : 0;
     static constexpr int V_BYTES = TILE * RV;
     static constexpr int VS_BYTES = (VT == KVQ_F16) ? 0 : TILE * NB * 2;
-    static constexpr int VH_BYTES = (VT == KVQ_Q5_0) ? TILE * NB * 4 : 0;
+    static constexpr int VH_BYTES = has_bit_words(VT) ? TILE * NB * 4 : 0;
     static constexpr int K_OFF = 0, KS_OFF = K_BYTES, KH_OFF = KS_OFF + KS_BYTES, V_OFF = KH_OFF + KH_BYTES;
     static constexpr int VS_OFF = V_OFF + V_BYTES, VH_OFF = VS_OFF + VS_BYTES;
     static constexpr int BYTES = VH_OFF + VH_BYTES;  // one wave's tile
     // copy instructions of one tile: 1 KB each for codes, 256 B each (128 B
     // on half the lanes) for scales and high bits
-    static constexpr int NK = K_BYTES / 1024, NV = V_BYTES / 1024;
+    // (turbo3 V at head_dim 64 is half a kilobyte: one instruction on half the lanes)
+    static constexpr int NK = K_BYTES / 1024, NV = (V_BYTES + 1023) / 1024;
     static constexpr int NKS = (KT == KVQ_F16) ? 0 : (KS_BYTES == 128 ? 1 : KS_BYTES / 256);
     static constexpr int NVS = (VT == KVQ_F16) ? 0 : (VS_BYTES == 128 ? 1 : VS_BYTES / 256);
     static constexpr int NKH = KH_BYTES / 256, NVH = VH_BYTES / 256;
@@ -242,7 +288,7 @@ template <int KT, int VT, int D>
 struct DmaOffsets {
     using g = Geo<KT, VT, D>;
     int k[g::K_BYTES / 1024];
-    int v[g::V_BYTES / 1024];
+    int v[g::NV];
     __device__ void init(int lane)
     {
 #pragma unroll
@@ -251,7 +297,7 @@ struct DmaOffsets {
             k[i] = r * g::RK + 16 * c;
         }
 #pragma unroll
-        for (int i = 0; i < g::V_BYTES / 1024; i++) {
+        for (int i = 0; i < g::NV; i++) {
             const int sl = 64 * i + lane, grp = sl / g::CPG, c = (sl % g::CPG) ^ vswz<VT, g::CPG>(grp);
             v[i] = grp * (8 * g::RV) + 16 * c;
         }
@@ -302,7 +348,7 @@ __device__ inline void issue_tile(uint8_t *buf, int tb, int lane, const DmaOffse
     const int vbase = (tb >> 3) * 8 * g::RV;
 #pragma unroll
     for (int i = 0; i < g::NV; i++)
-        if ((I_V + i) % nparts == part)
+        if ((I_V + i) % nparts == part && (g::V_BYTES % 1024 == 0 || 1024 * i + 16 * lane < g::V_BYTES))
             dma<16, CPOL>(r.vc, off.v[i], vbase, buf + g::V_OFF + 1024 * i);
     if (VT != KVQ_F16) {
         const int sbase = (tb >> 3) * g::NB * 16;
@@ -316,7 +362,7 @@ __device__ inline void issue_tile(uint8_t *buf, int tb, int lane, const DmaOffse
                     dma<4, CPOL>(r.vs, 256 * i + 4 * lane, sbase, buf + g::VS_OFF + 256 * i);
         }
     }
-    if (VT == KVQ_Q5_0) {  // one word per (token, block), 8-token groups
+    if (has_bit_words(VT)) {  // one word per (token, block), 8-token groups
         const int hbase = (tb >> 3) * g::NB * 32;
 #pragma unroll
         for (int i = 0; i < g::NVH; i++)

@@ -14,23 +14,29 @@ namespace kvq {
 // kernel reading a full tile never leaves the plane.
 __host__ __device__ inline int64_t capacity(int64_t max_ctx) { return (max_ctx + 31) / 32 * 32; }
 
-__host__ __device__ inline int64_t row_code_bytes(int type, int64_t D)
+__host__ __device__ constexpr int64_t row_code_bytes(int type, int64_t D)
 {
-    return type == KVQ_F16 ? 2 * D : type == KVQ_Q8_0 ? D : D / 2;  // q4_0 and the q5_0 nibbles: D/2
+    // q4_0 and the q5_0 nibbles: D/2; turbo3's 2-bit planes: D/4
+    return type == KVQ_F16 ? 2 * D : type == KVQ_Q8_0 ? D : type == KVQ_TURBO3 ? D / 4 : D / 2;
 }
 
+// Types whose code allocation continues with one 32-bit word per (row, block).
+__host__ __device__ constexpr bool has_bit_words(int type) { return type == KVQ_Q5_0 || type == KVQ_TURBO3; }
+
 // Every (K type, V type) pair, for the kernels' dispatch tables.
+// (turbo3 is a values-only type.)
 #define KVQ_FOR_EACH_TYPE_PAIR(X)                                                                  \
     X(KVQ_F16, KVQ_F16) X(KVQ_F16, KVQ_Q8_0) X(KVQ_F16, KVQ_Q4_0) X(KVQ_F16, KVQ_Q5_0)             \
     X(KVQ_Q8_0, KVQ_F16) X(KVQ_Q8_0, KVQ_Q8_0) X(KVQ_Q8_0, KVQ_Q4_0) X(KVQ_Q8_0, KVQ_Q5_0)         \
     X(KVQ_Q4_0, KVQ_F16) X(KVQ_Q4_0, KVQ_Q8_0) X(KVQ_Q4_0, KVQ_Q4_0) X(KVQ_Q4_0, KVQ_Q5_0)         \
-    X(KVQ_Q5_0, KVQ_F16) X(KVQ_Q5_0, KVQ_Q8_0) X(KVQ_Q5_0, KVQ_Q4_0) X(KVQ_Q5_0, KVQ_Q5_0)
+    X(KVQ_Q5_0, KVQ_F16) X(KVQ_Q5_0, KVQ_Q8_0) X(KVQ_Q5_0, KVQ_Q4_0) X(KVQ_Q5_0, KVQ_Q5_0)         \
+    X(KVQ_F16, KVQ_TURBO3) X(KVQ_Q8_0, KVQ_TURBO3) X(KVQ_Q4_0, KVQ_TURBO3) X(KVQ_Q5_0, KVQ_TURBO3)
 
 struct AppendArgs {
     const uint16_t *src[2];  // K, V binary16 [S][n_new][H][D]
     uint8_t *codes[2];       // K plane, V plane
     uint16_t *scales[2];
-    uint32_t *qh[2];         // q5_0 high-bit words (after the nibble rows), else NULL
+    uint32_t *qh[2];         // q5_0 high-bit / turbo3 third-bit words (after the rows), else NULL
     int32_t H, D, Tc, n_new, n_seqs;
     int32_t pos[KVQ_MAX_SEQS];
 };
@@ -61,6 +67,7 @@ struct MergeArgs {
     const float *ws;
     float *out;  // [S][Hq][D]
     int32_t Hq, Hkv, G, D;
+    int32_t v_rotated;  // turbo3 values: rotate every 32-channel block of the output back
     int32_t wave_start[KVQ_MAX_SEQS + 1];
 };
 

@@ -77,7 +77,7 @@ __global__ __launch_bounds__(64 * PW) __attribute__((amdgpu_waves_per_eu(D <= 12
     constexpr int NB = g::NB, NCT = g::NCT;
     constexpr int RB = Rows<D>::RB;
     constexpr int ROWS_G = 16 * RB * PW;
-    constexpr int VL = (VT == KVQ_Q4_0 || VT == KVQ_Q5_0) ? NB : NCT;
+    constexpr int VL = (VT == KVQ_Q4_0 || VT == KVQ_Q5_0 || VT == KVQ_TURBO3) ? NB : NCT;
     constexpr bool KQ = KT != KVQ_F16, VQ = VT != KVQ_F16;
 
     __shared__ __attribute__((aligned(16))) uint8_t lds[2][g::BYTES];
@@ -144,7 +144,7 @@ __global__ __launch_bounds__(64 * PW) __attribute__((amdgpu_waves_per_eu(D <= 12
         rs.vs = make_rsrc(a.vs + pair * Tc * NB, Tc * NB * 2);
     if (KT == KVQ_Q5_0)
         rs.kh = make_rsrc(a.kqh + pair * Tc * NB, Tc * NB * 4);
-    if (VT == KVQ_Q5_0)
+    if (has_bit_words(VT))
         rs.vh = make_rsrc(a.vqh + pair * Tc * NB, Tc * NB * 4);
     DmaOffsets<KT, VT, D> doff;
     doff.init(lane);
@@ -167,7 +167,7 @@ __global__ __launch_bounds__(64 * PW) __attribute__((amdgpu_waves_per_eu(D <= 12
     int v_rd[VL];
 #pragma unroll
     for (int i = 0; i < VL; i++) {
-        const int u = 16 * i + n;
+        const int u = (VT == KVQ_TURBO3) ? 8 * i + (n & 7) : 16 * i + n;
         const int c = (VT == KVQ_F16) ? u : (u >> 1);
         const int within = (VT == KVQ_F16) ? 0 : 8 * (u & 1);
         v_rd[i] = g::V_OFF + (j * g::CPG + (c ^ vswz<VT, g::CPG>(j))) * 16 + within;
@@ -239,7 +239,13 @@ __global__ __launch_bounds__(64 * PW) __attribute__((amdgpu_waves_per_eu(D <= 12
                     vsc = u32x4{vsc.x & vk[0], vsc.y & vk[1], vsc.z & vk[2], vsc.w & vk[3]};
                 }
                 half8 va[2];
-                if (VT == KVQ_Q5_0) {
+                if (VT == KVQ_TURBO3) {
+                    const u32x2 w = *reinterpret_cast<const u32x2 *>(buf + v_rd[b]);
+                    const u32x4 *hp = reinterpret_cast<const u32x4 *>(buf + g::VH_OFF + (j * NB + b) * 32);
+                    const u32x4 h0 = hp[0], h1 = hp[1];
+                    const uint32_t h[8] = {h0.x, h0.y, h0.z, h0.w, h1.x, h1.y, h1.z, h1.w};
+                    v_operand_tq3(w, h, n, va[0], va[1]);  // levels of the rotated values
+                } else if (VT == KVQ_Q5_0) {
                     const u32x2 w = *reinterpret_cast<const u32x2 *>(buf + v_rd[b]);
                     const u32x4 *hp = reinterpret_cast<const u32x4 *>(buf + g::VH_OFF + (j * NB + b) * 32);
                     const u32x4 h0 = hp[0], h1 = hp[1];
@@ -403,6 +409,44 @@ __global__ __launch_bounds__(64 * PW) __attribute__((amdgpu_waves_per_eu(D <= 12
         step(std::integral_constant<bool, false>(), t);
     for (int t = t_d; t < ntile; t++)
         step(std::integral_constant<bool, true>(), t);
+
+    // ---- turbo3 values: O was accumulated in the rotated basis; rotate each
+    // 32-channel block back, x = s.(H y)/32.  Channel 32b + e of this lane's
+    // row sits at e = 16(ct - 2b) + 4j + i: butterflies of span 1, 2 over i,
+    // 4, 8 over the lane groups j (lanes 16 and 32 apart), 16 over ct.
+    if constexpr (VT == KVQ_TURBO3) {
+#pragma unroll
+        for (int rb = 0; rb < RB; rb++) {
+#pragma unroll
+            for (int ct = 0; ct < NCT; ct++) {
+                floatx4 &v = o[rb][ct];
+                const float a0 = v[0] + v[1], a1 = v[0] - v[1], a2 = v[2] + v[3], a3 = v[2] - v[3];
+                v = floatx4{a0 + a2, a1 + a3, a0 - a2, a1 - a3};
+#pragma unroll
+                for (int lm = 16; lm <= 32; lm <<= 1) {
+                    const bool upper = (lane & lm) != 0;
+#pragma unroll
+                    for (int i = 0; i < 4; i++) {
+                        const float other = __shfl_xor(v[i], lm);
+                        v[i] = upper ? other - v[i] : v[i] + other;
+                    }
+                }
+            }
+#pragma unroll
+            for (int b = 0; b < NB; b++) {
+                const floatx4 lo = o[rb][2 * b], hi = o[rb][2 * b + 1];
+                o[rb][2 * b] = lo + hi;
+                o[rb][2 * b + 1] = lo - hi;
+            }
+#pragma unroll
+            for (int ct = 0; ct < NCT; ct++)
+#pragma unroll
+                for (int i = 0; i < 4; i++) {
+                    const int e = 16 * (ct & 1) + 4 * j + i;
+                    o[rb][ct][i] *= ((TQ3_SIGNS >> e) & 1u) ? -0.03125f : 0.03125f;
+                }
+        }
+    }
 
     // ---- normalize and write this lane's rows: channels 16ct + 4j + i
 #pragma unroll

@@ -59,6 +59,107 @@ __device__ inline void load8(const uint16_t *blk, int q, uint16_t (&x)[8])
 }
 
 // Quantize one block (this lane's 8 elements) and store codes + scale.
+// turbo3 (values only): the rotated block y = H (s . x) in binary64 -- exact,
+// since every partial sum of binary16 inputs is a multiple of 2^-24 below
+// 2^21 -- butterflies within the lane's 8 elements and then across the quad;
+// scale from max |y|, codes = the nearest of the 8 binary16 Lloyd-Max levels
+// of the scaled value (binary32), stored as a 2-bit plane byte per element
+// group and a third-bit word.  Lane q holds elements 8q..8q+7.
+template <int ROLE>
+__device__ inline void quant_store_tq3(const uint16_t *blk, int q, uint8_t *codes, uint16_t *scales, uint32_t *qh,
+                                       int64_t pair, int64_t t, int b, int D, int Tc)
+{
+#pragma clang fp contract(off)
+    constexpr uint32_t SIGNS = 0x9E3779B9u;
+    // the level midpoints (binary32, exact): between -2.152 -1.344 -0.756
+    // -0.2451 0.2451 0.756 1.344 2.152 (binary16 values)
+    constexpr float LV[8] = {-2.15234375f, -1.34375f, -0.755859375f, -0.2451171875f,
+                             0.2451171875f, 0.755859375f, 1.34375f, 2.15234375f};
+    uint16_t xb[8];
+    load8<KVQ_F16>(blk, q, xb);
+    double y[8];
+#pragma unroll
+    for (int k = 0; k < 8; k++) {
+        const double x = (double)h2f(xb[k]);
+        y[k] = ((SIGNS >> (8 * q + k)) & 1u) ? -x : x;
+    }
+#pragma unroll
+    for (int len = 1; len < 8; len <<= 1)
+#pragma unroll
+        for (int i = 0; i < 8; i += 2 * len)
+#pragma unroll
+            for (int k = i; k < i + len; k++) {
+                const double a0 = y[k], b0 = y[k + len];
+                y[k] = a0 + b0;
+                y[k + len] = a0 - b0;
+            }
+#pragma unroll
+    for (int lm = 1; lm <= 2; lm <<= 1) {  // spans 8 and 16: lane bits 0 and 1
+        const bool upper = (q & lm) != 0;
+#pragma unroll
+        for (int k = 0; k < 8; k++) {
+            const double o = __shfl_xor(y[k], lm);
+            y[k] = upper ? o - y[k] : y[k] + o;
+        }
+    }
+    double m = 0.0;
+#pragma unroll
+    for (int k = 0; k < 8; k++)
+        m = fmax(m, __builtin_fabs(y[k]));
+    m = fmax(m, __shfl_xor(m, 1));
+    m = fmax(m, __shfl_xor(m, 2));
+    const float d32 = __fdiv_rn((float)m, LV[7]);
+    const uint16_t dbits = f2h_bits(d32);
+    const float d = h2f(dbits);
+    const float id = (d != 0.0f) ? __fdiv_rn(1.0f, d) : 0.0f;
+    uint32_t plane = 0, third = 0;  // this lane's bits of the 2-bit plane bytes 0..7 (two words), third bits
+    uint32_t plane_hi = 0;
+#pragma unroll
+    for (int k = 0; k < 8; k++) {
+        const float tv = (float)y[k] * id;
+        int c = 0;
+#pragma unroll
+        for (int jj = 0; jj < 7; jj++)
+            c += (tv >= (LV[jj] + LV[jj + 1]) * 0.5f) ? 1 : 0;
+        const uint32_t bits = (uint32_t)(c & 3) << (8 * (k & 3) + 2 * q);  // byte k, bits 2q
+        if (k < 4)
+            plane |= bits;
+        else
+            plane_hi |= bits;
+        third |= (uint32_t)(c >> 2) << (8 * q + k);
+    }
+    plane |= (uint32_t)__shfl_xor((int)plane, 1);
+    plane |= (uint32_t)__shfl_xor((int)plane, 2);
+    plane_hi |= (uint32_t)__shfl_xor((int)plane_hi, 1);
+    plane_hi |= (uint32_t)__shfl_xor((int)plane_hi, 2);
+    third |= (uint32_t)__shfl_xor((int)third, 1);
+    third |= (uint32_t)__shfl_xor((int)third, 2);
+
+    const int64_t R = row_code_bytes(KVQ_TURBO3, D);
+    const int NB = D / 32;
+    if (ROLE == 0) {
+        if (q == 0)
+            *reinterpret_cast<u32x2 *>(codes + (pair * Tc + t) * R + 8 * b) = u32x2{plane, plane_hi};
+        if (q == 1) {
+            qh[(pair * Tc + t) * NB + b] = third;
+            scales[(pair * Tc + t) * NB + b] = dbits;
+        }
+    } else {
+        // 8-token groups: byte u of token t at ((pair*(Tc/8) + t/8)*R + u)*8 + t%8
+        const uint32_t w = (q < 2) ? plane : plane_hi;
+#pragma unroll
+        for (int k = 0; k < 2; k++) {
+            const int u = 2 * q + k;  // bytes 2q, 2q+1 of the block's 8
+            codes[((pair * (Tc / 8) + t / 8) * R + 8 * b + u) * 8 + (t & 7)] = (uint8_t)(w >> (8 * (u & 3)));
+        }
+        if (q == 0) {
+            const int64_t si = ((pair * (Tc / 8) + t / 8) * NB + b) * 8 + (t & 7);
+            qh[si] = third;
+            scales[si] = dbits;
+        }
+    }
+}
+
 // qh: q5_0's high-bit words (one per row and block, indexed like the
 // scales), unused for the other types.
 template <int T, int ROLE>
@@ -66,6 +167,10 @@ __device__ inline void quant_store(const uint16_t *blk, int q, uint8_t *codes, u
                                    int64_t pair, int64_t t, int b, int D, int Tc)
 {
 #pragma clang fp contract(off)
+    if constexpr (T == KVQ_TURBO3) {
+        quant_store_tq3<ROLE>(blk, q, codes, scales, qh, pair, t, b, D, Tc);
+        return;
+    }
     const int NB = D / 32;
     const int64_t R = row_code_bytes(T, D);
     uint16_t xb[8];

@@ -77,12 +77,12 @@ def test_plane_bytes_equal_the_oracles_for_every_type(L, orc):
     of the layout contract), q5_0 included: 22 B per 32 elements."""
     for D in (64, 128, 256):
         sh = shape(n_layers=1, n_seqs=3, n_q_heads=8, n_kv_heads=2, head_dim=D, max_ctx=1000)
-        for t in ("f16", "q8_0", "q4_0", "q5_0"):
+        for t in ("f16", "q8_0", "q4_0", "q5_0", "turbo3"):
             assert kvq.kvq_plane_bytes(sh, t) == orc.plane_bytes(t, 3, 2, D, 1000), (t, D)
     sh = shape(n_layers=1, n_seqs=1, n_q_heads=8, n_kv_heads=1, head_dim=128, max_ctx=1024)
     assert sum(kvq.kvq_plane_bytes(sh, "q5_0")) * 32 == 22 * 1024 * 128
     a = ctypes.c_size_t()
-    assert L.kvq_plane_bytes(ctypes.byref(sh), 4, ctypes.byref(a), ctypes.byref(a)) == kvq.KVQ_E_TYPE
+    assert L.kvq_plane_bytes(ctypes.byref(sh), 5, ctypes.byref(a), ctypes.byref(a)) == kvq.KVQ_E_TYPE
 
 
 def make_cache(sh, kt=1, vt=2, codes=FAKE, scales=FAKE + 4096):
@@ -115,7 +115,9 @@ def test_shape_rejections(L, kw, code):
 def test_plane_rejections(L):
     sh = shape()
     assert kvq.kvq_cache_check(make_cache(sh)) == kvq.KVQ_OK
-    assert kvq.kvq_cache_check(make_cache(sh, kt=4)) == kvq.KVQ_E_TYPE
+    assert kvq.kvq_cache_check(make_cache(sh, kt=5)) == kvq.KVQ_E_TYPE
+    assert kvq.kvq_cache_check(make_cache(sh, kt=4)) == kvq.KVQ_E_TYPE  # turbo3 keys: values only
+    assert kvq.kvq_cache_check(make_cache(sh, kt=1, vt=4)) == kvq.KVQ_OK
     assert kvq.kvq_cache_check(make_cache(sh, codes=None)) == kvq.KVQ_E_ARG
     assert kvq.kvq_cache_check(make_cache(sh, codes=FAKE + 8)) == kvq.KVQ_E_ARG  # misaligned
     assert kvq.kvq_cache_check(make_cache(sh, scales=None)) == kvq.KVQ_E_ARG  # quantized needs scales

@@ -16,6 +16,7 @@ from kvq_testutil import assert_planes_equal, bits, zero_cache
 pytestmark = pytest.mark.gpu
 
 PAIRS = list(itertools.product(["f16", "q8_0", "q4_0", "q5_0"], repeat=2))
+PAIRS += [(k, "turbo3") for k in ["f16", "q8_0", "q4_0", "q5_0"]]  # turbo3 stores values only
 
 
 def special_rows(x, rng):

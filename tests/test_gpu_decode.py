@@ -19,6 +19,7 @@ from kvq_testutil import assert_attn_close, assert_planes_equal, bits, zero_cach
 pytestmark = pytest.mark.gpu
 
 PAIRS = list(itertools.product(["f16", "q8_0", "q4_0", "q5_0"], repeat=2))
+PAIRS += [(k, "turbo3") for k in ["f16", "q8_0", "q4_0", "q5_0"]]  # turbo3 stores values only
 
 
 def small_case(kt, vt, S, Hq, Hkv, D, T, ctx, n_splits_list, seed, kscale=3.0):
@@ -51,7 +52,7 @@ def test_decode_pairs(kt, vt, D):
                seed=zlib.crc32(f"{kt}{vt}{D}".encode()) % 1000)
 
 
-@pytest.mark.parametrize("kt,vt", [("q8_0", "q4_0"), ("f16", "f16"), ("q4_0", "q8_0"), ("q5_0", "q5_0"), ("q8_0", "q5_0")])
+@pytest.mark.parametrize("kt,vt", [("q8_0", "q4_0"), ("f16", "f16"), ("q4_0", "q8_0"), ("q5_0", "q5_0"), ("q8_0", "q5_0"), ("q8_0", "turbo3")])
 def test_decode_head_dim_256(kt, vt):
     print(f"decode parity {kt}/{vt} D=256", flush=True)
     small_case(kt, vt, S=2, Hq=8, Hkv=2, D=256, T=200, ctx=[200, 64], n_splits_list=[0, 2], seed=7)
@@ -192,7 +193,8 @@ def test_decode_graph_replay_matches_eager():
         del junk
 
 
-@pytest.mark.parametrize("kt,vt", [("q8_0", "q4_0"), ("f16", "f16"), ("q4_0", "q8_0"), ("q5_0", "q5_0")])
+@pytest.mark.parametrize("kt,vt", [("q8_0", "q4_0"), ("f16", "f16"), ("q4_0", "q8_0"), ("q5_0", "q5_0"),
+                                   ("q8_0", "turbo3")])
 def test_decode_ignores_garbage_past_context(kt, vt):
     """Cache memory past ctx_len may hold any bits (here NaN patterns in codes
     and scales): the ragged tail tile must not let them into the output."""

@@ -25,6 +25,7 @@ from kvq_testutil import assert_attn_close, assert_planes_equal, bits, zero_cach
 pytestmark = pytest.mark.gpu
 
 PAIRS = list(itertools.product(["f16", "q8_0", "q4_0", "q5_0"], repeat=2))
+PAIRS += [(k, "turbo3") for k in ["f16", "q8_0", "q4_0", "q5_0"]]  # turbo3 stores values only
 
 
 def fused_case(kt, vt, S, Hq, Hkv, D, T, ctx, splits, seed):
@@ -73,7 +74,7 @@ def test_decode_append_pairs(kt, vt):
 
 
 @pytest.mark.parametrize("D", [64, 256])
-@pytest.mark.parametrize("kt,vt", [("q8_0", "q4_0"), ("f16", "q8_0"), ("q4_0", "f16"), ("q5_0", "q5_0")])
+@pytest.mark.parametrize("kt,vt", [("q8_0", "q4_0"), ("f16", "q8_0"), ("q4_0", "f16"), ("q5_0", "q5_0"), ("q8_0", "turbo3")])
 def test_decode_append_head_dims(kt, vt, D):
     fused_case(kt, vt, S=2, Hq=8, Hkv=2, D=D, T=200, ctx=[64, 200], splits=[0, 2, 7], seed=D)
 

@@ -22,7 +22,8 @@ def test_per_layer_type_mix():
     import mixed_precision_quantized_quantize_amd as kvq
 
     print("per-layer type mix", flush=True)
-    types = [("q8_0", "q4_0"), ("f16", "f16"), ("q4_0", "q4_0"), ("q8_0", "q8_0"), ("q4_0", "f16")]
+    types = [("q8_0", "q4_0"), ("f16", "f16"), ("q4_0", "q4_0"), ("q8_0", "q8_0"), ("q4_0", "f16"), ("q5_0", "q5_0"),
+             ("q8_0", "turbo3")]
     S, Hq, Hkv, D, T = 2, 16, 2, 128, 300
     ctx = [300, 133]
     cache = kvq.KVCache(len(types), S, Hq, Hkv, D, T, types)

@@ -19,6 +19,7 @@ from kvq_testutil import assert_attn_close, assert_planes_equal, bits, zero_cach
 pytestmark = pytest.mark.gpu
 
 PAIRS = list(itertools.product(["f16", "q8_0", "q4_0", "q5_0"], repeat=2))
+PAIRS += [(k, "turbo3") for k in ["f16", "q8_0", "q4_0", "q5_0"]]  # turbo3 stores values only
 
 
 def prefill_case(kt, vt, S, Hq, Hkv, D, T, n_tok, q_pos0, seed, garbage=False, kscale=3.0, scale=None):
@@ -61,7 +62,7 @@ def test_prefill_pairs(kt, vt, D):
                  seed=zlib.crc32(f"p{kt}{vt}{D}".encode()) % 1000)
 
 
-@pytest.mark.parametrize("kt,vt", [("q8_0", "q4_0"), ("f16", "f16"), ("q4_0", "q8_0"), ("q5_0", "q5_0"), ("q5_0", "f16")])
+@pytest.mark.parametrize("kt,vt", [("q8_0", "q4_0"), ("f16", "f16"), ("q4_0", "q8_0"), ("q5_0", "q5_0"), ("q5_0", "f16"), ("q8_0", "turbo3")])
 def test_prefill_head_dim_256(kt, vt):
     print(f"prefill parity {kt}/{vt} D=256", flush=True)
     prefill_case(kt, vt, S=2, Hq=8, Hkv=2, D=256, T=200, n_tok=45, q_pos0=[155, 3], seed=8)
@@ -79,7 +80,7 @@ def test_prefill_chunk_shapes(n_tok, q_pos0):
     prefill_case("q8_0", "q4_0", S=2, Hq=32, Hkv=8, D=128, T=300, n_tok=n_tok, q_pos0=q_pos0, seed=n_tok)
 
 
-@pytest.mark.parametrize("kt,vt", [("q8_0", "q4_0"), ("f16", "f16"), ("q4_0", "q8_0"), ("f16", "q4_0"), ("q8_0", "q5_0")])
+@pytest.mark.parametrize("kt,vt", [("q8_0", "q4_0"), ("f16", "f16"), ("q4_0", "q8_0"), ("f16", "q4_0"), ("q8_0", "q5_0"), ("q8_0", "turbo3")])
 def test_prefill_ignores_garbage_past_chunk(kt, vt):
     """Positions after the chunk's last query were never written (all bits
     set, NaN as binary16): the diagonal tiles must keep them out."""

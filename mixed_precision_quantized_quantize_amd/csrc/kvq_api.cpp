@@ -96,17 +96,17 @@ int check_layer(const kvq_cache *c, int32_t layer)
 // Never more waves for a pair than it has tiles.
 constexpr int AUTO_WAVES_MAX = 4096;
 // Waves per CU of the automatic split.  Where the tile math is heavy for its
-// bytes (K q4_0 or q5_0, or V q5_0: more vector instructions to unpack the
-// codes) two workgroups of four waves share a CU, so that one wave's math
-// overlaps another's copies: measured about 25% faster for q4_0/q4_0 and
-// q5_0/q5_0 at head_dim 128.  Otherwise one workgroup per CU, which streams
+// bytes (K q4_0 or q5_0, or V q5_0 or turbo3: more vector instructions to
+// unpack the codes) two workgroups of four waves share a CU, so that one
+// wave's math overlaps another's copies: measured about 25% faster for
+// q4_0/q4_0, q5_0/q5_0 and q8_0/turbo3 at head_dim 128.  Otherwise one workgroup per CU, which streams
 // best (K8V4: 6% faster than two).  One at head_dim 256 either way: its waves
 // need all 512 registers.
 int waves_per_cu(const kvq_shape &sh, int32_t kt, int32_t vt)
 {
     if (sh.head_dim > 128)
         return 4;
-    const bool heavy = kt == KVQ_Q4_0 || kt == KVQ_Q5_0 || vt == KVQ_Q5_0;
+    const bool heavy = kt == KVQ_Q4_0 || kt == KVQ_Q5_0 || vt == KVQ_Q5_0 || vt == KVQ_TURBO3;
     return heavy ? 8 : 4;
 }
 

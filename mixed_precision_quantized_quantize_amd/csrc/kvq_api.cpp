@@ -312,6 +312,8 @@ int attn_decode(const kvq_cache *cache, int32_t layer, const void *K, const void
     m.G = a.G;
     m.D = sh.head_dim;
     m.v_rotated = vp.type == KVQ_TURBO3;
+    m.n_seqs = sh.n_seqs;
+    m.k_uniform = a.k_uniform;
     memcpy(m.wave_start, a.wave_start, sizeof(int32_t) * (sh.n_seqs + 1));
     hipError_t e = launch_decode(kp.type, vp.type, sh.head_dim, a, m, sh.n_seqs * sh.n_kv_heads, (hipStream_t)stream);
     return e == hipSuccess ? KVQ_OK : KVQ_E_HIP;

@@ -79,13 +79,22 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(D <=
     const int G = a.G, Hkv = a.Hkv;
     const int64_t Tc = a.Tc;
 
-    // this wave's pair (s, h), its index r among the pair's k waves: a
-    // division when every sequence has k waves per pair, else a binary
-    // search of the sequences' first waves (dependent scalar loads)
-    int s = 0, k = a.k_uniform, local;
+    // this wave's pair (s, h) and its index r among the pair's k waves.
+    // The pairs are interleaved over the grid (wave gw serves pair
+    // gw mod pairs), so that every pair gets waves from early- and
+    // late-dispatched workgroups alike: with two workgroups per CU the first
+    // one on a CU runs well ahead of the second, and pairs served by only one
+    // of them would finish far apart.  When every sequence has k waves per
+    // pair this is a division; else the sequences' first waves are binary
+    // searched (dependent scalar loads) and the heads of one sequence are
+    // interleaved.
+    int s = 0, k = a.k_uniform, h, r;
     if (k > 0) {
-        s = gw / (k * Hkv);
-        local = gw - s * k * Hkv;
+        const int n_pairs = a.n_seqs * Hkv;
+        r = gw / n_pairs;
+        const int pg = gw - r * n_pairs;
+        s = pg / Hkv;
+        h = pg - s * Hkv;
     } else {
         int hi = a.n_seqs;  // wave_start[s] <= gw < wave_start[hi]
         while (hi - s > 1) {
@@ -96,9 +105,10 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(D <=
                 hi = mid;
         }
         k = (a.wave_start[s + 1] - a.wave_start[s]) / Hkv;
-        local = gw - a.wave_start[s];
+        const int local = gw - a.wave_start[s];
+        r = local / Hkv;
+        h = local - r * Hkv;
     }
-    const int h = local / k, r = local - h * k;
     const int ctx = a.ctx_len[s];
     const int nt = (ctx + TILE - 1) / TILE;
     const int n_mine = (nt - r + k - 1) / k;  // tiles r, r+k, ... below nt (>= 1)
@@ -508,9 +518,12 @@ __global__ __launch_bounds__(MERGE_MAX_THREADS) void merge_kernel(const MergeArg
     const int pair = blockIdx.x / G, gg = blockIdx.x - pair * G;
     const int s = pair / a.Hkv, h = pair - s * a.Hkv;
     const int k = (a.wave_start[s + 1] - a.wave_start[s]) / a.Hkv;  // the pair's waves = its slots
-    const int w0 = a.wave_start[s] + h * k;
+    // slot of wave r of the pair (the decode kernel's interleave): r*pairs + pair
+    // when every sequence has k waves per pair, else first(s) + r*Hkv + h
+    const int w0 = a.k_uniform > 0 ? pair : a.wave_start[s] + h;
+    const int slot_step = a.k_uniform > 0 ? a.n_seqs * a.Hkv : a.Hkv;
     const int nslot = k;
-    const int64_t stride = (int64_t)G * Dp;  // floats between consecutive slots
+    const int64_t stride = (int64_t)slot_step * G * Dp;  // floats between the pair's consecutive slots
     const float *base = a.ws + ((int64_t)w0 * G + gg) * Dp;
     const int t = threadIdx.x, c = t % D, grp = t / D;
 

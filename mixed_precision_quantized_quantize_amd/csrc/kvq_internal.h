@@ -43,9 +43,11 @@ struct AppendArgs {
 
 // Decode work split: every (sequence, kv head) pair of sequence s gets k_s
 // waves; wave r of a pair streams its tiles r, r + k_s, ... and writes one
-// partial into slot (its global wave index).  wave_start[s] = first wave of
-// sequence s (n_kv_heads * the k of every earlier sequence); wave_start[n_seqs]
-// = W, the number of waves.
+// partial into slot (its global wave index).  The pairs are interleaved over
+// the waves: with one k for all sequences (k_uniform) wave r of pair p is
+// wave r*pairs + p; otherwise wave wave_start[s] + r*n_kv_heads + h.
+// wave_start[s] = first wave of sequence s (n_kv_heads * the k of every
+// earlier sequence); wave_start[n_seqs] = W, the number of waves.
 struct DecodeArgs {
     const uint8_t *kc;
     const uint16_t *ks;
@@ -66,7 +68,8 @@ struct DecodeArgs {
 struct MergeArgs {
     const float *ws;
     float *out;  // [S][Hq][D]
-    int32_t Hq, Hkv, G, D;
+    int32_t Hq, Hkv, G, D, n_seqs;
+    int32_t k_uniform;  // as in DecodeArgs (selects the slot interleave)
     int32_t v_rotated;  // turbo3 values: rotate every 32-channel block of the output back
     int32_t wave_start[KVQ_MAX_SEQS + 1];
 };

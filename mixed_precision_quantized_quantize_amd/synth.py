@@ -61,8 +61,8 @@ WORKLOADS = {
                  notes="TinyLlama-shaped cache, 22 layers x 256-wide KV"),
         Workload("llama3_8b_32k", 32, 32, 8, 128, 32768, 16, (("q8_0", "q4_0"),), "student_t", 3000,
                  notes="Llama-3-8B-shaped decode, K8V4"),
-        Workload("llama31_70b_32k", 80, 64, 8, 128, 32768, 1, (("q8_0", "q4_0"),), "student_t", 4000,
-                 notes="Llama-3.1-70B-shaped decode, K8V4"),
+        Workload("llama31_70b_32k", 80, 64, 8, 128, 32768, 1, (("q8_0", "q4_0"), ("q8_0", "turbo3")), "student_t",
+                 4000, notes="Llama-3.1-70B-shaped decode, K8V4; also K q8_0 / V turbo3 (the TurboQuant page's setup)"),
         Workload("llama3_8b_128k_prefill", 32, 32, 8, 128, 131072, 4, (("q4_0", "q4_0"),), "student_t", 5000,
                  prefill=512, notes="long context, K4V4 decode plus a 512-query causal chunk"),
     ]

@@ -123,6 +123,12 @@ def test_llama31_70b_32k_full_size_sampled():
     workload_layer("llama31_70b_32k", 0, [0], [0, 9, 63])
 
 
+def test_llama31_70b_32k_turbo3_full_size_sampled():
+    """The TurboQuant page's configuration: Llama-3.1-70B shape at 32K tokens,
+    keys q8_0, values turbo3."""
+    workload_layer("llama31_70b_32k", 0, [0], [0, 9, 63], pair=("q8_0", "turbo3"))
+
+
 def test_llama3_8b_128k_decode_full_size_sampled():
     workload_layer("llama3_8b_128k_prefill", 0, [3], [0, 17])
 

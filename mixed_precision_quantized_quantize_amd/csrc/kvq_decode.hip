@@ -508,6 +508,50 @@ __device__ inline float block_reduce(float v, float *sh, bool is_max)
     return r;
 }
 
+// turbo3 values: rotate each 32-channel block of the output back,
+// x = s.(H y)/32 -- butterflies of span 1..16 across the 32 threads (lanes)
+// of the block, thread c holding channel c
+__device__ inline float rotate_back(float r, const int c)
+{
+#pragma unroll
+    for (int span = 1; span < 32; span <<= 1) {
+        const float o = __shfl_xor(r, span);
+        r = (c & span) ? o - r : r + o;
+    }
+    return ((TQ3_SIGNS >> (c & 31)) & 1u) ? -r * 0.03125f : r * 0.03125f;
+}
+
+// Channel c of one query head from its k <= KF partials (slot j at
+// base + j*stride): all 3*KF loads issued together (slots past k repeat the
+// last one and weigh nothing), then sum_j O_j[c] 2^(m_j - M) / sum_j l_j 2^(m_j - M)
+// in slot order.
+template <int KF>
+__device__ inline float merge_few(const float *base, const int64_t stride, const int k, const int c, const int D)
+{
+    float mj[KF], lj[KF], oj[KF];
+#pragma unroll
+    for (int j = 0; j < KF; j++) {
+        const float *pk = base + (int64_t)min(j, k - 1) * stride;
+        mj[j] = pk[D];
+        lj[j] = pk[D + 1];
+        oj[j] = pk[c];
+    }
+    float M = mj[0];
+#pragma unroll
+    for (int j = 1; j < KF; j++)
+        if (j < k)
+            M = fmaxf(M, mj[j]);
+    float L = 0.0f, acc = 0.0f;
+#pragma unroll
+    for (int j = 0; j < KF; j++)
+        if (j < k) {
+            const float w = __builtin_amdgcn_exp2f(mj[j] - M);
+            L += lj[j] * w;
+            acc += oj[j] * w;
+        }
+    return acc / L;
+}
+
 __global__ __launch_bounds__(MERGE_MAX_THREADS) void merge_kernel(const MergeArgs a)
 {
     __shared__ float wts[MERGE_CHUNK];
@@ -526,6 +570,17 @@ __global__ __launch_bounds__(MERGE_MAX_THREADS) void merge_kernel(const MergeArg
     const int64_t stride = (int64_t)slot_step * G * Dp;  // floats between the pair's consecutive slots
     const float *base = a.ws + ((int64_t)w0 * G + gg) * Dp;
     const int t = threadIdx.x, c = t % D, grp = t / D;
+    float *const dst = a.out + ((int64_t)s * a.Hq + (int64_t)h * G + gg) * D + c;
+
+    if (nslot <= 16) {
+        // few slots (the usual case): one thread per channel loads the (m, l)
+        // and O of every slot at once -- one round trip, no barriers
+        if (grp > 0)
+            return;  // whole waves: D is a multiple of 64
+        const float r = nslot <= 8 ? merge_few<8>(base, stride, nslot, c, D) : merge_few<16>(base, stride, nslot, c, D);
+        *dst = a.v_rotated ? rotate_back(r, c) : r;
+        return;
+    }
 
     float mx = -INFINITY;
     for (int j = t; j < nslot; j += blockDim.x)
@@ -572,19 +627,10 @@ __global__ __launch_bounds__(MERGE_MAX_THREADS) void merge_kernel(const MergeArg
                 acc += part[g2 * D + c];
     }
     float r = acc / L;
-    if (a.v_rotated && grp == 0) {
-        // turbo3 values: rotate each 32-channel block back, x = s.(H y)/32 --
-        // butterflies of span 1..16 across the 32 threads of the block
-        // (whole waves take this branch: D is a multiple of 64)
-#pragma unroll
-        for (int span = 1; span < 32; span <<= 1) {
-            const float o = __shfl_xor(r, span);
-            r = (c & span) ? o - r : r + o;
-        }
-        r = ((TQ3_SIGNS >> (c & 31)) & 1u) ? -r * 0.03125f : r * 0.03125f;
-    }
+    if (a.v_rotated && grp == 0)  // whole waves take this branch
+        r = rotate_back(r, c);
     if (grp == 0)
-        a.out[((int64_t)s * a.Hq + (int64_t)h * G + gg) * D + c] = r;
+        *dst = r;
 }
 
 template <int KT, int VT, int D>

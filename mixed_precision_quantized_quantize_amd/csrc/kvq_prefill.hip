@@ -12,7 +12,9 @@
 // copied once into LDS (the four waves deal out the copy instructions), its
 // quantized blocks are turned into MFMA operands once for the workgroup (the
 // four waves deal out those jobs too and write the operands back to LDS), and
-// all four waves read them.  Per wave and tile both contractions run on
+// all four waves read them.  The operands of tile t+1 are built while tile t
+// is computed, one barrier per tile, so that each wave's dequantization runs
+// between its MFMAs.  Per wave and tile both contractions run on
 // v_mfma_f32_16x16x32_f16, and every operand is shared by the wave's RB row
 // blocks:
 //   S^T[key][row]  = K[key][c] . Q^T[c][row]
@@ -80,14 +82,21 @@ __global__ __launch_bounds__(64 * PW) __attribute__((amdgpu_waves_per_eu(D <= 12
     constexpr int VL = (VT == KVQ_Q4_0 || VT == KVQ_Q5_0 || VT == KVQ_TURBO3) ? NB : NCT;
     constexpr bool KQ = KT != KVQ_F16, VQ = VT != KVQ_F16;
 
-    __shared__ __attribute__((aligned(16))) uint8_t lds[2][g::BYTES];
+    // raw tiles: tile t in lds[t % NRAW] (t+1 being dequantized and t+2 in
+    // flight while t is computed)
+    constexpr int NRAW = 3;
+    __shared__ __attribute__((aligned(16))) uint8_t lds[NRAW][g::BYTES];
     // Dequantized operands of the current tile, built once per workgroup:
     // K hi and lo per (score tile T, block b), V (times scale) per (block b,
     // half hh); each set is one MFMA operand, 16 bytes per lane, lane-major.
     constexpr int NKSET = KQ ? 2 * NB : 0, NVSET = VQ ? 2 * NB : 0;
     constexpr int DQ_KHI = 0, DQ_KLO = DQ_KHI + NKSET * 1024, DQ_V = DQ_KLO + NKSET * 1024;
     constexpr int DQ_BYTES = DQ_V + NVSET * 1024;
-    __shared__ __attribute__((aligned(16))) uint8_t dq[DQ_BYTES > 0 ? DQ_BYTES : 16];
+    // tile t's in dq0 (t even) or dq1 (t odd): two arrays, so that the
+    // compiler sees that building one tile's operands does not touch the
+    // other's, and may interleave the two
+    __shared__ __attribute__((aligned(16))) uint8_t dq0[DQ_BYTES > 0 ? DQ_BYTES : 16];
+    __shared__ __attribute__((aligned(16))) uint8_t dq1[DQ_BYTES > 0 ? DQ_BYTES : 16];
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -186,35 +195,36 @@ __global__ __launch_bounds__(64 * PW) __attribute__((amdgpu_waves_per_eu(D <= 12
     }
 
     const int ntile = (key_end + TILE - 1) / TILE;
-    issue_tile<KT, VT, D>(lds[0], 0, lane, doff, rs, wave, PW);
-    // One tile; DG: the tile may hold keys past a row's position (masking).
-    auto step = [&](auto diag_c, const int t) {
-        constexpr bool DG = decltype(diag_c)::value;
-        const uint8_t *buf = lds[t & 1];
-        const int tb = t * TILE;
-        // every wave's share of this tile has landed before anyone reads it
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        __syncthreads();
 
-        // ---- the wave's share of the tile's dequantization (jobs dealt
-        // round-robin over the waves: K sets (T, b) then V blocks b)
-        constexpr int NJOB = (KQ ? 2 * NB : 0) + (VQ ? NB : 0);
+    // ---- dequantization of tile t (raw copy in lds[t % NRAW]) into
+    // dq[t & 1].  The tile's jobs are K sets (T, b), then V blocks b; this
+    // wave takes jobs wave, wave + PW, ...  As 2*NB is a multiple of PW, the
+    // i-th job of every wave is of the same kind: straight-line code with
+    // wave-uniform offsets.  MASK: the tile may reach past key_end.
+    static_assert(!KQ || (2 * NB) % PW == 0, "K jobs are dealt evenly");
+    auto dequant = [&](auto mask_c, const int t, uint8_t *const dqt) {
+        constexpr bool MASK = decltype(mask_c)::value;
+        const uint8_t *buf = lds[t % NRAW];
+        const int tb = t * TILE;
+        constexpr int NKJ = KQ ? 2 * NB : 0, NJOB = NKJ + (VQ ? NB : 0);
 #pragma unroll
-        for (int job = 0; job < NJOB; job++) {
-            if (job % PW != wave)
-                continue;
-            if (KQ && job < 2 * NB) {
+        for (int i = 0; i < (NJOB + PW - 1) / PW; i++) {
+            const int job = wave + PW * i;
+            if (PW * i < NKJ) {
                 const int T = job / NB, b = job - T * NB;
-                half8 ka;
                 const int r = 8 * (n >> 2) + 4 * T + (n & 3);  // this lane's key in the tile
+                const int c = (KT == KVQ_Q8_0) ? 2 * b + (j >> 1) : b;
+                const int within = (KT == KVQ_Q8_0) ? 8 * (j & 1) : 4 * j;
+                const int krd = g::K_OFF + (r * g::CPR + (c ^ kswz<g::CPR>(r))) * 16 + within;
+                half8 ka;
                 if (KT == KVQ_Q8_0) {
-                    const u32x2 w = *reinterpret_cast<const u32x2 *>(buf + k_rd[T][b]);
+                    const u32x2 w = *reinterpret_cast<const u32x2 *>(buf + krd);
                     ka = deq_q8(w.x, w.y);
                 } else if (KT == KVQ_Q4_0) {
-                    const uint32_t w = *reinterpret_cast<const uint32_t *>(buf + k_rd[T][b]);
+                    const uint32_t w = *reinterpret_cast<const uint32_t *>(buf + krd);
                     ka = k_operand<KVQ_Q4_0>(&w);
                 } else {
-                    const uint32_t w = *reinterpret_cast<const uint32_t *>(buf + k_rd[T][b]);
+                    const uint32_t w = *reinterpret_cast<const uint32_t *>(buf + krd);
                     const uint32_t hw = *reinterpret_cast<const uint32_t *>(buf + g::KH_OFF + (r * NB + b) * 4);
                     ka = k_operand_q5(w, hw >> (4 * j));
                 }
@@ -222,37 +232,42 @@ __global__ __launch_bounds__(64 * PW) __attribute__((amdgpu_waves_per_eu(D <= 12
                 const half8 dd = splat8(dbits * 0x00010001u);
                 const half8 hi = ka * dd;
                 const half8 lo = __builtin_elementwise_fma(ka, dd, -hi);
-                *reinterpret_cast<half8 *>(dq + DQ_KHI + (job * 64 + lane) * 16) = hi;
-                *reinterpret_cast<half8 *>(dq + DQ_KLO + (job * 64 + lane) * 16) = lo;
-            } else if (VQ) {
-                const int b = job - (KQ ? 2 * NB : 0);
+                *reinterpret_cast<half8 *>(dqt + DQ_KHI + (job * 64 + lane) * 16) = hi;
+                *reinterpret_cast<half8 *>(dqt + DQ_KLO + (job * 64 + lane) * 16) = lo;
+            } else if (VQ && (NJOB % PW == 0 || job < NJOB)) {  // waves < PW: only a ragged last round checks
+                const int b = job - NKJ;
+                // LDS offset of the codes a lane reads for operand u (as v_rd)
+                auto vrd = [&](const int u_i) {
+                    const int u = (VT == KVQ_TURBO3) ? 8 * u_i + (n & 7) : 16 * u_i + n;
+                    return g::V_OFF + (j * g::CPG + ((u >> 1) ^ vswz<VT, g::CPG>(j))) * 16 + 8 * (u & 1);
+                };
                 u32x4 vsc = *reinterpret_cast<const u32x4 *>(buf + g::VS_OFF + (j * NB + b) * 16);
                 // keys at or past key_end were never written for this chunk:
                 // their scale bits may be anything, even NaN -> force zero
-                if (DG && tb + TILE > key_end) {
+                if (MASK && tb + TILE > key_end) {
                     uint32_t vk[4];
 #pragma unroll
-                    for (int i = 0; i < 4; i++) {
-                        const int k0 = tb + 8 * j + 2 * i;
-                        vk[i] = (k0 < key_end ? 0x0000FFFFu : 0u) | (k0 + 1 < key_end ? 0xFFFF0000u : 0u);
+                    for (int q = 0; q < 4; q++) {
+                        const int k0 = tb + 8 * j + 2 * q;
+                        vk[q] = (k0 < key_end ? 0x0000FFFFu : 0u) | (k0 + 1 < key_end ? 0xFFFF0000u : 0u);
                     }
                     vsc = u32x4{vsc.x & vk[0], vsc.y & vk[1], vsc.z & vk[2], vsc.w & vk[3]};
                 }
                 half8 va[2];
                 if (VT == KVQ_TURBO3) {
-                    const u32x2 w = *reinterpret_cast<const u32x2 *>(buf + v_rd[b]);
+                    const u32x2 w = *reinterpret_cast<const u32x2 *>(buf + vrd(b));
                     const u32x4 *hp = reinterpret_cast<const u32x4 *>(buf + g::VH_OFF + (j * NB + b) * 32);
                     const u32x4 h0 = hp[0], h1 = hp[1];
                     const uint32_t h[8] = {h0.x, h0.y, h0.z, h0.w, h1.x, h1.y, h1.z, h1.w};
                     v_operand_tq3(w, h, n, va[0], va[1]);  // levels of the rotated values
                 } else if (VT == KVQ_Q5_0) {
-                    const u32x2 w = *reinterpret_cast<const u32x2 *>(buf + v_rd[b]);
+                    const u32x2 w = *reinterpret_cast<const u32x2 *>(buf + vrd(b));
                     const u32x4 *hp = reinterpret_cast<const u32x4 *>(buf + g::VH_OFF + (j * NB + b) * 32);
                     const u32x4 h0 = hp[0], h1 = hp[1];
                     const uint32_t h[8] = {h0.x, h0.y, h0.z, h0.w, h1.x, h1.y, h1.z, h1.w};
                     v_operand_q5(w, h, n, va[0], va[1]);
                 } else if (VT == KVQ_Q4_0) {
-                    const u32x2 w = *reinterpret_cast<const u32x2 *>(buf + v_rd[b]);
+                    const u32x2 w = *reinterpret_cast<const u32x2 *>(buf + vrd(b));
                     uint32_t l01, h01, l23, h23, l45, h45, l67, h67;
                     deq_q4_pair(__builtin_amdgcn_perm(w.x, w.x, 0x0C010C00u), l01, h01);
                     deq_q4_pair(__builtin_amdgcn_perm(w.x, w.x, 0x0C030C02u), l23, h23);
@@ -263,16 +278,25 @@ __global__ __launch_bounds__(64 * PW) __attribute__((amdgpu_waves_per_eu(D <= 12
                 } else {
 #pragma unroll
                     for (int hh = 0; hh < 2; hh++) {
-                        const u32x2 w = *reinterpret_cast<const u32x2 *>(buf + v_rd[2 * b + hh]);
+                        const u32x2 w = *reinterpret_cast<const u32x2 *>(buf + vrd(2 * b + hh));
                         va[hh] = deq_q8(w.x, w.y);
                     }
                 }
                 const half8 dv = pack4(vsc.x, vsc.y, vsc.z, vsc.w);  // scales of keys 0..7
 #pragma unroll
                 for (int hh = 0; hh < 2; hh++)
-                    *reinterpret_cast<half8 *>(dq + DQ_V + ((2 * b + hh) * 64 + lane) * 16) = va[hh] * dv;
+                    *reinterpret_cast<half8 *>(dqt + DQ_V + ((2 * b + hh) * 64 + lane) * 16) = va[hh] * dv;
             }
         }
+    };
+
+    // ---- one tile's attention from its operands (dq[t & 1], and the raw
+    // tile for binary16 planes); DG: the tile may hold keys past a row's
+    // position (masking)
+    auto compute = [&](auto diag_c, const int t, const uint8_t *const dqt) {
+        constexpr bool DG = decltype(diag_c)::value;
+        const uint8_t *buf = lds[t % NRAW];
+        const int tb = t * TILE;
         // raw f16 operands (no dequantization) stay in the raw tile
         u32x4 kop[2][NB];
         u32x4 vop[VL];
@@ -299,14 +323,6 @@ __global__ __launch_bounds__(64 * PW) __attribute__((amdgpu_waves_per_eu(D <= 12
                     vop[i] = u32x4{vop[i].x & vk[0], vop[i].y & vk[1], vop[i].z & vk[2], vop[i].w & vk[3]};
             }
         }
-        // the shared operands are complete before anyone reads them
-        if (KQ || VQ)
-            __syncthreads();
-        // start the next tile's copy into the other buffer (its last readers
-        // finished before this iteration's first barrier)
-        if (t + 1 < ntile)
-            issue_tile<KT, VT, D>(lds[(t + 1) & 1], tb + TILE, lane, doff, rs, wave, PW);
-
         // ---- scores
         floatx4 sacc[RB][2];
 #pragma unroll
@@ -323,8 +339,8 @@ __global__ __launch_bounds__(64 * PW) __attribute__((amdgpu_waves_per_eu(D <= 12
                         sacc[rb][T] = mfma(ka, qb[rb][b], sacc[rb][T]);
                 } else {
                     const int set = T * NB + b;
-                    const half8 hi = *reinterpret_cast<const half8 *>(dq + DQ_KHI + (set * 64 + lane) * 16);
-                    const half8 lo = *reinterpret_cast<const half8 *>(dq + DQ_KLO + (set * 64 + lane) * 16);
+                    const half8 hi = *reinterpret_cast<const half8 *>(dqt + DQ_KHI + (set * 64 + lane) * 16);
+                    const half8 lo = *reinterpret_cast<const half8 *>(dqt + DQ_KLO + (set * 64 + lane) * 16);
 #pragma unroll
                     for (int rb = 0; rb < RB; rb++) {
                         sacc[rb][T] = mfma(hi, qb[rb][b], sacc[rb][T]);
@@ -383,7 +399,7 @@ __global__ __launch_bounds__(64 * PW) __attribute__((amdgpu_waves_per_eu(D <= 12
             if (VQ) {
 #pragma unroll
                 for (int hh = 0; hh < 2; hh++)
-                    va[hh] = *reinterpret_cast<const half8 *>(dq + DQ_V + ((2 * b + hh) * 64 + lane) * 16);
+                    va[hh] = *reinterpret_cast<const half8 *>(dqt + DQ_V + ((2 * b + hh) * 64 + lane) * 16);
             } else {
 #pragma unroll
                 for (int hh = 0; hh < 2; hh++) {
@@ -401,14 +417,73 @@ __global__ __launch_bounds__(64 * PW) __attribute__((amdgpu_waves_per_eu(D <= 12
         for (int rb = 0; rb < RB; rb++)
             lacc[rb] = mfma(ones, pb[rb], lacc[rb]);
     };
+
+    // ---- the tile loop: one barrier per tile.  At the barrier of tile t,
+    // tile t+1's copy has landed (each wave waited for its share), tile t's
+    // operands are complete, and every wave is done with tile t-1's operands
+    // and with the raw buffer of tile t-1.  Then: start the copy of tile
+    // t+2 into that buffer, build tile t+1's operands, and compute tile t --
+    // the dequantization's vector instructions run beside the MFMAs.
+    // dqw, dqr: the operand buffers of tiles t+1 and t.  In the loops they
+    // are the arrays themselves (pairs of tiles per round), so that the
+    // compiler may move tile t's operand reads and MFMAs in between tile
+    // t+1's dequantization.
+    auto body = [&](auto diag_c, auto last2_c, const int t, uint8_t *const dqw, const uint8_t *const dqr) {
+        constexpr bool LAST2 = decltype(last2_c)::value;  // t = ntile-2: no copy to start, dequant with mask
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+        if (!LAST2)
+            issue_tile<KT, VT, D>(lds[(t + 2) % NRAW], (t + 2) * TILE, lane, doff, rs, wave, PW);
+        if (KQ || VQ)
+            dequant(std::integral_constant<bool, LAST2>(), t + 1, dqw);
+        compute(diag_c, t, dqr);
+    };
+    using F = std::integral_constant<bool, false>;
+    using Tr = std::integral_constant<bool, true>;
+    issue_tile<KT, VT, D>(lds[0], 0, lane, doff, rs, wave, PW);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (ntile > 1)
+        issue_tile<KT, VT, D>(lds[1], TILE, lane, doff, rs, wave, PW);
+    if (KQ || VQ) {
+        if (ntile > 1)
+            dequant(F(), 0, dq0);
+        else
+            dequant(Tr(), 0, dq0);
+    }
     // Tiles before t_d lie entirely at or below every row position of this
     // wave and run without mask code.  Every wave still meets the same
     // barriers, those of ntile tiles.
     const int t_d = min(ntile, (wave_first + 1) / TILE);
-    for (int t = 0; t < t_d; t++)
-        step(std::integral_constant<bool, false>(), t);
-    for (int t = t_d; t < ntile; t++)
-        step(std::integral_constant<bool, true>(), t);
+    const int t_a = min(t_d, ntile - 2);
+    int t = 0;
+    for (; t + 2 <= t_a; t += 2) {
+        body(F(), F(), t, dq1, dq0);
+        body(F(), F(), t + 1, dq0, dq1);
+    }
+    if (t < t_a) {  // t even
+        body(F(), F(), t, dq1, dq0);
+        t++;
+    }
+    if (t < ntile - 2 && (t & 1)) {
+        body(Tr(), F(), t, dq0, dq1);
+        t++;
+    }
+    for (; t + 2 <= ntile - 2; t += 2) {
+        body(Tr(), F(), t, dq1, dq0);
+        body(Tr(), F(), t + 1, dq0, dq1);
+    }
+    if (t < ntile - 2) {  // t even
+        body(Tr(), F(), t, dq1, dq0);
+        t++;
+    }
+    // the last two tiles (with the mask code, which checks at run time
+    // whether a tile needs it)
+    if (ntile >= 2)
+        body(Tr(), Tr(), ntile - 2, (ntile & 1) ? dq0 : dq1, (ntile & 1) ? dq1 : dq0);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    compute(Tr(), ntile - 1, (ntile & 1) ? dq0 : dq1);
 
     // ---- turbo3 values: O was accumulated in the rotated basis; rotate each
     // 32-channel block back, x = s.(H y)/32.  Channel 32b + e of this lane's

@@ -202,7 +202,7 @@ __global__ __launch_bounds__(64 * PW) __attribute__((amdgpu_waves_per_eu(D <= 12
     // i-th job of every wave is of the same kind: straight-line code with
     // wave-uniform offsets.  MASK: the tile may reach past key_end.
     static_assert(!KQ || (2 * NB) % PW == 0, "K jobs are dealt evenly");
-    auto dequant = [&](auto mask_c, const int t, uint8_t *const dqt) {
+    auto dequant = [&](auto mask_c, const int t, uint8_t *const dqt) __attribute__((always_inline)) {
         constexpr bool MASK = decltype(mask_c)::value;
         const uint8_t *buf = lds[t % NRAW];
         const int tb = t * TILE;
@@ -293,7 +293,7 @@ __global__ __launch_bounds__(64 * PW) __attribute__((amdgpu_waves_per_eu(D <= 12
     // ---- one tile's attention from its operands (dq[t & 1], and the raw
     // tile for binary16 planes); DG: the tile may hold keys past a row's
     // position (masking)
-    auto compute = [&](auto diag_c, const int t, const uint8_t *const dqt) {
+    auto compute = [&](auto diag_c, const int t, const uint8_t *const dqt) __attribute__((always_inline)) {
         constexpr bool DG = decltype(diag_c)::value;
         const uint8_t *buf = lds[t % NRAW];
         const int tb = t * TILE;
@@ -428,7 +428,7 @@ __global__ __launch_bounds__(64 * PW) __attribute__((amdgpu_waves_per_eu(D <= 12
     // are the arrays themselves (pairs of tiles per round), so that the
     // compiler may move tile t's operand reads and MFMAs in between tile
     // t+1's dequantization.
-    auto body = [&](auto diag_c, auto last2_c, const int t, uint8_t *const dqw, const uint8_t *const dqr) {
+    auto body = [&](auto diag_c, auto last2_c, const int t, uint8_t *const dqw, const uint8_t *const dqr) __attribute__((always_inline)) {
         constexpr bool LAST2 = decltype(last2_c)::value;  // t = ntile-2: no copy to start, dequant with mask
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();

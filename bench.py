@@ -50,6 +50,7 @@ def parse():
                    help="append with kvq_append, then decode with kvq_attn_decode (two calls per layer)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-prefill", action="store_true", help="skip the prefill measurement")
+    p.add_argument("--no-stream-ceiling", action="store_true", help="skip the streaming-read ceiling measurement")
     p.add_argument("--prefill-only", action="store_true",
                    help="measure only the chunked prefill (prints a JSON line with the `prefill` object)")
     p.add_argument("--cpu-seconds", type=float, default=10.0)
@@ -92,6 +93,35 @@ def traffic_from_profile(src_hash, workload):
 
 
 MFMA_F16_PEAK_TFLOPS = 2500.0  # dense binary16 matrix peak
+
+
+def stream_ceiling(dev, nbytes: int, achieved: float) -> dict:
+    """The practical read-bandwidth ceiling: kvq_stream_read over a buffer of
+    one decode call's KV size, outside the timed region."""
+    import torch
+
+    import mixed_precision_quantized_quantize_amd as kvq
+
+    n = nbytes // 16 * 16
+    buf = torch.empty(n, dtype=torch.uint8, device=dev)
+    buf.fill_(1)
+    sink = torch.zeros(1, dtype=torch.int32, device=dev)
+    for _ in range(3):
+        kvq.stream_read(buf, 0x7FFFFFFF, sink)
+    torch.cuda.synchronize()
+    reps = 20
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        kvq.stream_read(buf, 0x7FFFFFFF, sink)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    gbs = n / (ms * 1e-3) / 1e9
+    del buf
+    return {"value": round(gbs, 1), "unit": "GB/s", "bytes_per_launch": n, "us_per_launch": round(ms * 1e3, 2),
+            "kernel": "kvq_stream_read: non-temporal 16-byte loads, 8 in flight per lane, 8 workgroups of 256 per CU",
+            "frac_of_peak": round(gbs / HBM_PEAK_GBPS, 4), "decode_frac_of_ceiling": round(achieved / gbs, 4)}
 
 
 def prefill_measure(dev, calls=5):
@@ -345,6 +375,10 @@ def main():
     }
     log(f"step {ms_step:.3f} ms, {value:.1f} GB/s ({100 * value / HBM_PEAK_GBPS:.1f}% of peak), "
         f"decode call {dec_avg_ms * 1e3:.1f} us -> {achieved:.1f} GB/s")
+
+    if not args.no_stream_ceiling:
+        result["stream_read_ceiling"] = stream_ceiling(dev, kv_layer, achieved)
+        log(f"streaming-read ceiling {result['stream_read_ceiling']['value']:.1f} GB/s")
 
     if args.calib_copy:
         x = torch.empty(1 << 28, dtype=torch.float32, device=dev)

@@ -232,6 +232,18 @@ int kvq_attn_decode_append(const kvq_cache *cache, int32_t layer, const void *K,
 int kvq_attn_prefill_chunk(const kvq_cache *cache, int32_t layer, const void *Q, int32_t n_tok,
                            const int32_t *q_pos0, float scale, float *out, void *stream);
 
+/* ---- measurement support (not part of the attention path) ----
+ *
+ * Streams `bytes` of device memory at `src` through non-temporal vector loads
+ * and discards them: the practical read-bandwidth ceiling that decode
+ * figures are compared with.  `src` device, 16-byte aligned, bytes a
+ * multiple of 16; `sink` device, one uint32 that is written only if the XOR
+ * of everything a lane read equals `key` (pick a key that no lane's fold
+ * takes, or ignore the sink).  blocks: workgroups of 256 threads, 0 = eight
+ * per compute unit.  KVQ_E_ARG on a null pointer, misalignment or a size
+ * that is not a multiple of 16; KVQ_E_HIP if the launch fails. */
+int kvq_stream_read(const void *src, size_t bytes, uint32_t key, uint32_t *sink, int32_t blocks, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -25,7 +25,7 @@ KVQ_OK, KVQ_E_ARG, KVQ_E_TYPE, KVQ_E_SHAPE, KVQ_E_RANGE, KVQ_E_WORKSPACE, KVQ_E_
 KVQ_MAX_SEQS, KVQ_MAX_GROUP, KVQ_MAX_SPLITS = 256, 16, 256
 
 EXPORTS = ["kvq_strerror", "kvq_plane_bytes", "kvq_cache_check", "kvq_append", "kvq_decode_workspace_bytes",
-           "kvq_attn_decode", "kvq_attn_decode_append", "kvq_attn_prefill_chunk"]
+           "kvq_attn_decode", "kvq_attn_decode_append", "kvq_attn_prefill_chunk", "kvq_stream_read"]
 
 
 class KvqLibraryMissing(RuntimeError):
@@ -78,6 +78,7 @@ def lib():
                                                  vp, vp, sz, i32, vp]
             L.kvq_attn_prefill_chunk.argtypes = [P(kvq_cache), i32, vp, i32, P(ctypes.c_int32), ctypes.c_float,
                                                  vp, vp]
+            L.kvq_stream_read.argtypes = [vp, sz, ctypes.c_uint32, vp, i32, vp]
             for name in EXPORTS:
                 if name != "kvq_strerror":
                     getattr(L, name).restype = ctypes.c_int
@@ -144,6 +145,20 @@ def kvq_attn_prefill_chunk(cache: kvq_cache, layer: int, Q_ptr: int, n_tok: int,
                            out_ptr: int, stream: int) -> int:
     return lib().kvq_attn_prefill_chunk(ctypes.byref(cache), int(layer), Q_ptr, int(n_tok), _i32_array(q_pos0),
                                         float(scale), out_ptr, stream)
+
+
+def kvq_stream_read(src_ptr: int, nbytes: int, key: int, sink_ptr: int, blocks: int, stream: int) -> int:
+    return lib().kvq_stream_read(src_ptr, int(nbytes), ctypes.c_uint32(key), sink_ptr, int(blocks), stream)
+
+
+def stream_read(buf, key: int, sink, blocks: int = 0) -> None:
+    """Streams the device tensor `buf` (contiguous, 16-byte aligned, size a
+    multiple of 16 bytes) through the read-bandwidth probe on the current
+    stream; `sink` is a device uint32 / int32 tensor of at least one element."""
+    import torch
+
+    _check(kvq_stream_read(buf.data_ptr(), buf.numel() * buf.element_size(), key, sink.data_ptr(), blocks,
+                           torch.cuda.current_stream(buf.device).cuda_stream), "kvq_stream_read")
 
 
 # ------------------------------------------------------------------ torch plumbing

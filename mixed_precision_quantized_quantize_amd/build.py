@@ -18,7 +18,7 @@ OUT = os.path.join(PKG, "libkvq.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
 ARCH = "gfx950"
 
-SOURCES = ["kvq_api.cpp", "kvq_append.hip", "kvq_decode.hip", "kvq_prefill.hip"]
+SOURCES = ["kvq_api.cpp", "kvq_append.hip", "kvq_decode.hip", "kvq_prefill.hip", "kvq_probe.hip"]
 
 # Packed-fp32 instructions stay disabled (the host pass warns that it does not
 # know the feature; that is harmless).  No fast-math: the quantizer relies on

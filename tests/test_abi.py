@@ -203,3 +203,15 @@ def test_prefill_rejections(L):
     assert call(p0=(-3, 0)) == kvq.KVQ_E_RANGE
     assert call(n_tok=0) == kvq.KVQ_E_RANGE
     assert call(Q=None) == kvq.KVQ_E_ARG
+
+
+def test_stream_read_rejections(L):
+    """The read-bandwidth probe rejects bad arguments on the host; an empty
+    read is a no-op (nothing is launched)."""
+    E_ARG = -1
+    assert kvq.kvq_stream_read(0, 1024, 0, FAKE, 0, 0) == E_ARG  # null source
+    assert kvq.kvq_stream_read(FAKE, 1024, 0, 0, 0, 0) == E_ARG  # null sink
+    assert kvq.kvq_stream_read(FAKE + 8, 1024, 0, FAKE, 0, 0) == E_ARG  # misaligned
+    assert kvq.kvq_stream_read(FAKE, 1000, 0, FAKE, 0, 0) == E_ARG  # not a multiple of 16 bytes
+    assert kvq.kvq_stream_read(FAKE, 1024, 0, FAKE, -1, 0) == E_ARG  # negative grid
+    assert kvq.kvq_stream_read(FAKE, 0, 0, FAKE, 0, 0) == 0

@@ -99,15 +99,18 @@ constexpr int AUTO_WAVES_MAX = 4096;
 // bytes (K q4_0 or q5_0, or V q5_0 or turbo3: more vector instructions to
 // unpack the codes) two workgroups of four waves share a CU, so that one
 // wave's math overlaps another's copies: measured about 25% faster for
-// q4_0/q4_0, q5_0/q5_0 and q8_0/turbo3 at head_dim 128.  Otherwise one workgroup per CU, which streams
-// best (K8V4: 6% faster than two).  One at head_dim 256 either way: its waves
-// need all 512 registers.
-int waves_per_cu(const kvq_shape &sh, int32_t kt, int32_t vt)
+// q4_0/q4_0, q5_0/q5_0 and q8_0/turbo3 at head_dim 128 -- as long as each
+// wave still gets at least 16 tiles (a one-sequence 70B-shaped layer with
+// turbo3 values, 4 tiles per wave at eight waves per CU: 30 us against 26.5
+// with four).  Otherwise one workgroup per CU, which streams best (K8V4: 6%
+// faster than two).  One at head_dim 256 either way: its waves need all 512
+// registers.  `tiles`: the call's (kv head, tile) units.
+int waves_per_cu(const kvq_shape &sh, int32_t kt, int32_t vt, int64_t tiles, int cus)
 {
     if (sh.head_dim > 128)
         return 4;
     const bool heavy = kt == KVQ_Q4_0 || kt == KVQ_Q5_0 || vt == KVQ_Q5_0 || vt == KVQ_TURBO3;
-    return heavy ? 8 : 4;
+    return heavy && tiles >= (int64_t)16 * 8 * cus ? 8 : 4;
 }
 
 int device_cus()
@@ -133,7 +136,8 @@ int64_t decode_plan(const kvq_shape &sh, int32_t kt, int32_t vt, const int32_t *
     int64_t T = 0;
     for (int s = 0; s < sh.n_seqs; s++)
         T += (int64_t)sh.n_kv_heads * ((ctx_len[s] + 31) / 32);
-    const int64_t target = std::min<int64_t>((int64_t)device_cus() * waves_per_cu(sh, kt, vt), AUTO_WAVES_MAX);
+    const int cus = device_cus();
+    const int64_t target = std::min<int64_t>((int64_t)cus * waves_per_cu(sh, kt, vt, T, cus), AUTO_WAVES_MAX);
     int64_t W = 0;
     for (int s = 0; s < sh.n_seqs; s++) {
         const int64_t nt = (ctx_len[s] + 31) / 32;

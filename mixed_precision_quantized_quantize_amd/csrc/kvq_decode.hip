@@ -582,6 +582,45 @@ __global__ __launch_bounds__(MERGE_MAX_THREADS) void merge_kernel(const MergeArg
         return;
     }
 
+    if (nslot <= 16 * P && nslot <= (int)blockDim.x) {
+        // up to 16 slots per group: thread t loads slot t's (m, l), and each
+        // thread the O values of its group's slots grp, grp+P, ... -- all
+        // loads issued together, one round trip; then the maximum, the
+        // weights (through LDS) and the sums
+        float mt = -INFINITY, lt = 0.0f;
+        if (t < nslot) {
+            mt = base[(int64_t)t * stride + D];
+            lt = base[(int64_t)t * stride + D + 1];
+        }
+        float ov[16];
+#pragma unroll
+        for (int u = 0; u < 16; u++)
+            ov[u] = base[(int64_t)min(grp + u * P, nslot - 1) * stride + c];
+        const float M = block_reduce(mt, red, true);
+        const float w = t < nslot ? __builtin_amdgcn_exp2f(mt - M) : 0.0f;
+        if (t < nslot)
+            wts[t] = w;
+        const float L = block_reduce(lt * w, red, false);  // its barriers also publish wts
+        float acc = 0.0f;
+#pragma unroll
+        for (int u = 0; u < 16; u++)
+            if (grp + u * P < nslot)
+                acc += ov[u] * wts[grp + u * P];
+        if (P > 1) {
+            part[t] = acc;
+            __syncthreads();
+            if (grp == 0)
+                for (int g2 = 1; g2 < P; g2++)
+                    acc += part[g2 * D + c];
+        }
+        float r = acc / L;
+        if (a.v_rotated && grp == 0)  // whole waves take this branch
+            r = rotate_back(r, c);
+        if (grp == 0)
+            *dst = r;
+        return;
+    }
+
     float mx = -INFINITY;
     for (int j = t; j < nslot; j += blockDim.x)
         mx = fmaxf(mx, base[j * stride + D]);

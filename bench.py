@@ -169,6 +169,16 @@ def prefill_measure(dev, calls=5):
     }
 
 
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(w, kt, vt, layer_kv, q_bits, seconds):
     """The oracle, as it stands, on layer 0 of the workload: append the new
     row and decode all query heads of every sequence, repeated for about
@@ -197,6 +207,7 @@ def cpu_baseline(w, kt, vt, layer_kv, q_bits, seconds):
         "value": round(kvb / dt / 1e9, 3),
         "unit": "GB/s",
         "cores": threads,
+        "cpu_model": cpu_model(),
         "kind": "oracle",
         "sample": f"layer 0 of {w.name}: append 1 row + decode all {S} sequences x {w.n_q_heads} query heads "
                   f"over {w.ctx} tokens, binary64, {reps} repetition(s), {dt:.3f} s each "
@@ -306,6 +317,19 @@ def main():
     ms_total = start.elapsed_time(end)
     ms_step = ms_total / args.steps
 
+    # per-step durations in a second pass after the timed region (events
+    # between steps only), for the median and spread
+    step_ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(args.steps)]
+    for e0, e1 in step_ev:
+        e0.record(stream)
+        run()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    per_step = sorted(e0.elapsed_time(e1) for e0, e1 in step_ev)
+    ms_median = per_step[len(per_step) // 2] if len(per_step) % 2 else \
+        0.5 * (per_step[len(per_step) // 2 - 1] + per_step[len(per_step) // 2])
+
     if args.unfused:
         # the step also holds append launches: bracket each decode call with
         # events in one extra step after the timed region
@@ -341,6 +365,9 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms_step, 4),
+        "ms_per_step_median": round(ms_median, 4),
+        "ms_per_step_min_max": [round(per_step[0], 4), round(per_step[-1], 4)],
+        "ms_per_step_median_note": "a second pass of the same number of steps, each bracketed by events",
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,

@@ -32,7 +32,8 @@
  *
  * Conventions for every entry point:
  *  - All tensors live in device memory owned by the caller; the library
- *    allocates nothing, keeps no global state and is re-entrant.
+ *    allocates nothing and is re-entrant (its only global state is a
+ *    per-device cache of the compute-unit count, read once).
  *  - Per-sequence integer arrays (pos, ctx_len, q_pos0) are HOST arrays of
  *    n_seqs entries; they are validated on the host and passed to the
  *    kernels by value.
@@ -228,7 +229,11 @@ int kvq_attn_decode_append(const kvq_cache *cache, int32_t layer, const void *K,
  *   Q      : device binary16 [n_seqs][n_tok][n_q_heads][head_dim]
  *   q_pos0 : host int32 [n_seqs], 0 <= q_pos0[s], q_pos0[s]+n_tok <= max_ctx
  *   out    : device float32 [n_seqs][n_tok][n_q_heads][head_dim]
- * Query i of sequence s attends to positions 0 .. q_pos0[s]+i. */
+ * Query i of sequence s attends to positions 0 .. q_pos0[s]+i; cache bytes
+ * past q_pos0[s]+n_tok-1 may hold anything.  One launch on `stream`.
+ * Errors: the cache checks of kvq_cache_check, KVQ_E_RANGE (layer, n_tok < 1
+ * or a chunk past max_ctx), KVQ_E_ARG (NULL or misaligned Q / out / q_pos0,
+ * non-finite scale). */
 int kvq_attn_prefill_chunk(const kvq_cache *cache, int32_t layer, const void *Q, int32_t n_tok,
                            const int32_t *q_pos0, float scale, float *out, void *stream);
 

@@ -124,7 +124,7 @@ def stream_ceiling(dev, nbytes: int, achieved: float) -> dict:
             "frac_of_peak": round(gbs / HBM_PEAK_GBPS, 4), "decode_frac_of_ceiling": round(achieved / gbs, 4)}
 
 
-def prefill_measure(dev, calls=5):
+def prefill_measure(dev, calls=5, cpu=False):
     """Causal chunked prefill on one layer of the long-context workload: the
     last 512-query chunk of each of 4 sequences over 131072 K4V4 positions.
     Algorithmic flop = 4 * head_dim * n_q_heads * (visible keys summed over
@@ -159,14 +159,47 @@ def prefill_measure(dev, calls=5):
     keys = sum(T - n_tok + i + 1 for i in range(n_tok))
     flop = 4.0 * w.head_dim * w.n_q_heads * keys * S
     tflops = flop / (ms * 1e-3) / 1e12
-    del cache, Q, out
+    del cache, out
     torch.cuda.empty_cache()
-    return {
+    res = {
         "workload": w.name, "layer": 0, "batch": S, "n_tok": n_tok, "q_pos0": T - n_tok, "ctx": T,
         "k_type": kt, "v_type": vt, "ms_per_call": round(ms, 4), "alg_flop_per_call": flop,
         "roofline": {"bound": "mfma", "kernel": "prefill_kernel, one layer", "achieved": round(tflops, 1),
                      "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(tflops / MFMA_F16_PEAK_TFLOPS, 4)},
+        "cpu_baseline": None,
     }
+    if cpu:
+        res["cpu_baseline"] = prefill_cpu_baseline(w, Q)
+    return res
+
+
+def prefill_cpu_baseline(w, Q, n_q=64):
+    """The oracle's causal prefill on a bounded sample of the same call:
+    sequence 0, the first and the last n_q queries of the chunk, all heads."""
+    import numpy as np
+
+    import oracle
+    from mixed_precision_quantized_quantize_amd import synth
+
+    kt, vt = w.type_pairs[0]
+    n_tok, T = w.prefill, w.ctx
+    orc = oracle.OracleLayer(kt, vt, 1, w.n_q_heads, w.n_kv_heads, w.head_dim, T)
+    for c0 in range(0, T, synth.CHUNK):
+        K, V = synth.kv_batch(w, 0, c0, min(synth.CHUNK, T - c0), device=Q.device, seqs=[0])
+        orc.append(synth.as_bits(K), synth.as_bits(V), np.array([c0], np.int32))
+        del K, V
+    qb = synth.as_bits(Q[:1])
+    flop, dt = 0.0, 0.0
+    for first in (0, n_tok - n_q):
+        p0 = T - n_tok + first
+        t0 = time.perf_counter()
+        orc.attn_prefill(qb[:, first:first + n_q], np.array([p0], np.int32), w.scale)
+        dt += time.perf_counter() - t0
+        flop += 4.0 * w.head_dim * w.n_q_heads * sum(p0 + i + 1 for i in range(n_q))
+    return {"value": round(flop / dt / 1e12, 5), "unit": "TFLOP/s", "cores": oracle.max_threads(),
+            "cpu_model": cpu_model(), "kind": "oracle",
+            "sample": f"layer 0, sequence 0 of {w.name}: the first and the last {n_q} queries of the "
+                      f"{n_tok}-query chunk, all {w.n_q_heads} query heads, binary64 ({dt:.2f} s)"}
 
 
 def cpu_model() -> str:
@@ -420,7 +453,7 @@ def main():
         torch.cuda.empty_cache()
     if not args.no_prefill:
         log("timing the chunked prefill ...")
-        result["prefill"] = prefill_measure(dev)
+        result["prefill"] = prefill_measure(dev, cpu=not args.no_cpu_baseline)
     if not args.no_cpu_baseline and layer0 is not None:
         from mixed_precision_quantized_quantize_amd.synth import as_bits
 

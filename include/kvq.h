@@ -137,7 +137,10 @@ typedef struct kvq_shape {
     int32_t n_q_heads;  /* multiple of n_kv_heads                */
     int32_t n_kv_heads; /* >= 1, n_q_heads/n_kv_heads <= 16      */
     int32_t head_dim;   /* 64, 128 or 256                        */
-    int32_t max_ctx;    /* cache capacity in tokens, >= 1        */
+    int32_t max_ctx;    /* cache capacity in tokens, >= 1, with
+                           max_ctx (rounded up to 32) * 2 * head_dim
+                           < 2^31: one (sequence, kv head)'s range of
+                           a stream is addressed with 32-bit offsets */
 } kvq_shape;
 
 /* One plane (the K or the V half of one layer). */

@@ -47,6 +47,11 @@ int check_shape(const kvq_shape *sh)
     // grid dimensions in their hardware limits
     if ((int64_t)sh->n_seqs * sh->n_kv_heads * capacity(sh->max_ctx) > ((int64_t)1 << 40))
         return KVQ_E_SHAPE;
+    // the kernels address one (sequence, kv head)'s range of a stream with
+    // 32-bit offsets: its largest stream (binary16 rows, 2*head_dim bytes a
+    // token) must stay below 2^31 bytes
+    if (capacity(sh->max_ctx) * 2 * sh->head_dim >= ((int64_t)1 << 31))
+        return KVQ_E_SHAPE;
     return KVQ_OK;
 }
 

@@ -103,6 +103,10 @@ def make_cache(sh, kt=1, vt=2, codes=FAKE, scales=FAKE + 4096):
     (dict(n_seqs=0), kvq.KVQ_E_SHAPE),
     (dict(max_ctx=0), kvq.KVQ_E_SHAPE),
     (dict(n_layers=0), kvq.KVQ_E_SHAPE),
+    # one (sequence, kv head) range of binary16 rows must stay below 2^31 bytes
+    (dict(n_seqs=1, n_q_heads=2, n_kv_heads=1, head_dim=256, max_ctx=1 << 22), kvq.KVQ_E_SHAPE),
+    (dict(n_seqs=1, n_q_heads=2, n_kv_heads=1, head_dim=64, max_ctx=(1 << 24) - 31), kvq.KVQ_E_SHAPE),
+    (dict(n_seqs=1, n_q_heads=2, n_kv_heads=1, head_dim=256, max_ctx=(1 << 22) - 32), kvq.KVQ_OK),
 ])
 def test_shape_rejections(L, kw, code):
     sh = shape(**kw)

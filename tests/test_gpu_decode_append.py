@@ -127,3 +127,55 @@ def test_decode_append_llama3_8b_32k_full_size():
         orc.append(bits(Kn)[s:s + 1], bits(Vn)[s:s + 1], np.array([T - 1], np.int32))
         ref = orc.attn_decode(bits(Q)[s:s + 1], np.array([T], np.int32), w.scale)
         print(assert_attn_close(got[s:s + 1], ref, f"{w.name} seq {s}"), flush=True)
+
+
+def test_decode_append_and_prefill_graph_replay():
+    """The fused decode step and a prefill chunk captured in one HIP graph:
+    every replay (with eager work and synchronizations between replays)
+    equals the eager result bit for bit, and the planes stay as the eager
+    calls left them (the fused append rewrites the same row each time)."""
+    import torch
+
+    import mixed_precision_quantized_quantize_amd as kvq
+
+    print("decode_append + prefill graph replay", flush=True)
+    rng = np.random.default_rng(12)
+    S, Hq, Hkv, D, T = 3, 16, 4, 128, 700
+    cache = kvq.KVCache(1, S, Hq, Hkv, D, T, ("q8_0", "q4_0"))
+    zero_cache(cache)
+    K = torch.from_numpy((rng.standard_t(4, (S, T, Hkv, D)) * 3).astype(np.float16)).cuda()
+    V = torch.from_numpy(rng.standard_normal((S, T, Hkv, D)).astype(np.float16)).cuda()
+    cache.append(0, K, V, [0] * S)
+    Kn = torch.from_numpy((rng.standard_t(4, (S, Hkv, D)) * 3).astype(np.float16)).cuda()
+    Vn = torch.from_numpy(rng.standard_normal((S, Hkv, D)).astype(np.float16)).cuda()
+    Q = torch.from_numpy(rng.standard_normal((S, Hq, D)).astype(np.float16)).cuda()
+    Qp = torch.from_numpy(rng.standard_normal((S, 40, Hq, D)).astype(np.float16)).cuda()
+    ctx, p0 = [700, 333, 64], [100, 0, 600]
+    eager_d = cache.decode_append(0, Kn, Vn, Q, ctx, 0.0883883).clone()
+    eager_p = cache.prefill(0, Qp, p0, 0.0883883).clone()
+    planes = [p.clone() for p in cache.plane_tensors(0) if p is not None]
+    out_d = torch.empty_like(eager_d)
+    out_p = torch.empty_like(eager_p)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        cache.decode_append(0, Kn, Vn, Q, ctx, 0.0883883, out=out_d)
+        cache.prefill(0, Qp, p0, 0.0883883, out=out_p)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        cache.decode_append(0, Kn, Vn, Q, ctx, 0.0883883, out=out_d)
+        cache.prefill(0, Qp, p0, 0.0883883, out=out_p)
+    for i in range(5):
+        out_d.zero_()
+        out_p.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out_d, eager_d), f"replay {i}: decode_append"
+        assert torch.equal(out_p, eager_p), f"replay {i}: prefill"
+        junk = cache.decode(0, Q, [50] * S, 0.0883883, n_splits=3)  # eager work between replays
+        torch.cuda.synchronize()
+        del junk
+    for a, b in zip([p for p in cache.plane_tensors(0) if p is not None], planes):
+        assert torch.equal(a, b)

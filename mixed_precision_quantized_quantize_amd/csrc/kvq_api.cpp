@@ -241,6 +241,14 @@ int kvq_append(const kvq_cache *cache, int32_t layer, const void *K, const void 
     a.n_new = n_new;
     a.n_seqs = sh.n_seqs;
     memcpy(a.pos, pos, sizeof(int32_t) * sh.n_seqs);
+    // the V plane is written in 8-token groups: the most groups any
+    // sequence's range [pos, pos + n_new) touches
+    int64_t ng = 1;
+    for (int s = 0; s < sh.n_seqs; s++)
+        ng = std::max<int64_t>(ng, (pos[s] % 8 + (int64_t)n_new + 7) / 8);
+    if ((int64_t)sh.n_seqs * sh.n_kv_heads * ng > ((int64_t)1 << 31) - 64)
+        return KVQ_E_SHAPE;
+    a.ng = (int32_t)ng;
     hipError_t e = launch_append(k_type, v_type, a, (int)n_quads, (hipStream_t)stream);
     return e == hipSuccess ? KVQ_OK : KVQ_E_HIP;
 }

@@ -38,6 +38,7 @@ struct AppendArgs {
     uint16_t *scales[2];
     uint32_t *qh[2];         // q5_0 high-bit / turbo3 third-bit words (after the rows), else NULL
     int32_t H, D, Tc, n_new, n_seqs;
+    int32_t ng;  // 8-token groups per sequence the V plane's launch covers (the most any sequence spans)
     int32_t pos[KVQ_MAX_SEQS];
 };
 

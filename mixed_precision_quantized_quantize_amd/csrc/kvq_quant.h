@@ -58,16 +58,26 @@ __device__ inline void load8(const uint16_t *blk, int q, uint16_t (&x)[8])
     }
 }
 
-// Quantize one block (this lane's 8 elements) and store codes + scale.
+// One lane's share of a quantized block: its code units in unit order and
+// the block's scale and bit word (the same in all four lanes).  Units are the
+// bytes of a row's codes (binary16 values for f16); lane q holds NU units
+// starting at NU*q within the block.
+struct LaneCodes {
+    uint16_t dbits;  // binary16 scale (f16: unused)
+    uint32_t bits;   // q5_0 high-bit word / turbo3 third-bit word of the block, else 0
+    uint32_t w[4];   // the lane's units, little-endian: f16 8 x 2 B, q8_0 8 B, q4_0 / q5_0 4 B, turbo3 2 B
+};
+template <int T>
+constexpr int lane_units() { return (T == KVQ_Q4_0 || T == KVQ_Q5_0) ? 4 : (T == KVQ_TURBO3 ? 2 : 8); }
+
 // turbo3 (values only): the rotated block y = H (s . x) in binary64 -- exact,
 // since every partial sum of binary16 inputs is a multiple of 2^-24 below
 // 2^21 -- butterflies within the lane's 8 elements and then across the quad;
 // scale from max |y|, codes = the nearest of the 8 binary16 Lloyd-Max levels
-// of the scaled value (binary32), stored as a 2-bit plane byte per element
-// group and a third-bit word.  Lane q holds elements 8q..8q+7.
-template <int ROLE>
-__device__ inline void quant_store_tq3(const uint16_t *blk, int q, uint8_t *codes, uint16_t *scales, uint32_t *qh,
-                                       int64_t pair, int64_t t, int b, int D, int Tc)
+// of the scaled value (binary32), as a 2-bit plane byte per element group
+// (byte j: elements j, j+8, j+16, j+24) and a third-bit word.  Lane q holds
+// elements 8q..8q+7 and returns plane bytes 2q, 2q+1.
+__device__ inline LaneCodes quant_lane_tq3(const uint16_t *blk, int q)
 {
 #pragma clang fp contract(off)
     constexpr uint32_t SIGNS = 0x9E3779B9u;
@@ -109,8 +119,9 @@ __device__ inline void quant_store_tq3(const uint16_t *blk, int q, uint8_t *code
     m = fmax(m, __shfl_xor(m, 1));
     m = fmax(m, __shfl_xor(m, 2));
     const float d32 = __fdiv_rn((float)m, LV[7]);
-    const uint16_t dbits = f2h_bits(d32);
-    const float d = h2f(dbits);
+    LaneCodes lc;
+    lc.dbits = f2h_bits(d32);
+    const float d = h2f(lc.dbits);
     const float id = (d != 0.0f) ? __fdiv_rn(1.0f, d) : 0.0f;
     uint32_t plane = 0, third = 0;  // this lane's bits of the 2-bit plane bytes 0..7 (two words), third bits
     uint32_t plane_hi = 0;
@@ -134,76 +145,28 @@ __device__ inline void quant_store_tq3(const uint16_t *blk, int q, uint8_t *code
     plane_hi |= (uint32_t)__shfl_xor((int)plane_hi, 2);
     third |= (uint32_t)__shfl_xor((int)third, 1);
     third |= (uint32_t)__shfl_xor((int)third, 2);
-
-    const int64_t R = row_code_bytes(KVQ_TURBO3, D);
-    const int NB = D / 32;
-    if (ROLE == 0) {
-        if (q == 0)
-            *reinterpret_cast<u32x2 *>(codes + (pair * Tc + t) * R + 8 * b) = u32x2{plane, plane_hi};
-        if (q == 1) {
-            qh[(pair * Tc + t) * NB + b] = third;
-            scales[(pair * Tc + t) * NB + b] = dbits;
-        }
-    } else {
-        // 8-token groups: byte u of token t at ((pair*(Tc/8) + t/8)*R + u)*8 + t%8
-        const uint32_t w = (q < 2) ? plane : plane_hi;
-#pragma unroll
-        for (int k = 0; k < 2; k++) {
-            const int u = 2 * q + k;  // bytes 2q, 2q+1 of the block's 8
-            codes[((pair * (Tc / 8) + t / 8) * R + 8 * b + u) * 8 + (t & 7)] = (uint8_t)(w >> (8 * (u & 3)));
-        }
-        if (q == 0) {
-            const int64_t si = ((pair * (Tc / 8) + t / 8) * NB + b) * 8 + (t & 7);
-            qh[si] = third;
-            scales[si] = dbits;
-        }
-    }
+    lc.bits = third;
+    lc.w[0] = (((q < 2) ? plane : plane_hi) >> (16 * (q & 1))) & 0xFFFFu;  // bytes 2q, 2q+1
+    lc.w[1] = lc.w[2] = lc.w[3] = 0;
+    return lc;
 }
 
-// qh: q5_0's high-bit words (one per row and block, indexed like the
-// scales), unused for the other types.
-template <int T, int ROLE>
-__device__ inline void quant_store(const uint16_t *blk, int q, uint8_t *codes, uint16_t *scales, uint32_t *qh,
-                                   int64_t pair, int64_t t, int b, int D, int Tc)
+template <int T>
+__device__ inline LaneCodes quant_lane(const uint16_t *blk, int q)
 {
 #pragma clang fp contract(off)
-    if constexpr (T == KVQ_TURBO3) {
-        quant_store_tq3<ROLE>(blk, q, codes, scales, qh, pair, t, b, D, Tc);
-        return;
-    }
-    const int NB = D / 32;
-    const int64_t R = row_code_bytes(T, D);
+    if constexpr (T == KVQ_TURBO3)
+        return quant_lane_tq3(blk, q);
+    LaneCodes lc;
+    lc.dbits = 0;
+    lc.bits = 0;
     uint16_t xb[8];
     load8<T>(blk, q, xb);
-
-    // Where unit u of this token lives (units: bytes, or binary16 for f16).
-    const int64_t U = (T == KVQ_F16) ? D : R;
-    auto unit_index = [&](int64_t u) -> int64_t {
-        if (ROLE == 0)
-            return (pair * Tc + t) * U + u;
-        return ((pair * (Tc / 8) + t / 8) * U + u) * 8 + (t & 7);
-    };
-    auto scale_index = [&]() -> int64_t {
-        if (ROLE == 0)
-            return (pair * Tc + t) * NB + b;
-        return ((pair * (Tc / 8) + t / 8) * NB + b) * 8 + (t & 7);
-    };
-
     if (T == KVQ_F16) {
-        uint16_t *dst = reinterpret_cast<uint16_t *>(codes);
-        if (ROLE == 0) {
-            u32x4 v;
-            v.x = xb[0] | ((uint32_t)xb[1] << 16);
-            v.y = xb[2] | ((uint32_t)xb[3] << 16);
-            v.z = xb[4] | ((uint32_t)xb[5] << 16);
-            v.w = xb[6] | ((uint32_t)xb[7] << 16);
-            *reinterpret_cast<u32x4 *>(dst + unit_index(32 * b + 8 * q)) = v;
-        } else {
 #pragma unroll
-            for (int k = 0; k < 8; k++)
-                dst[unit_index(32 * b + 8 * q + k)] = xb[k];
-        }
-        return;
+        for (int i = 0; i < 4; i++)
+            lc.w[i] = xb[2 * i] | ((uint32_t)xb[2 * i + 1] << 16);
+        return lc;
     }
 
     float x[8];
@@ -211,8 +174,6 @@ __device__ inline void quant_store(const uint16_t *blk, int q, uint8_t *codes, u
     for (int k = 0; k < 8; k++)
         x[k] = h2f(xb[k]);
 
-    float d;
-    uint16_t dbits;
     if (T == KVQ_Q8_0) {
         float amax = 0.0f;
 #pragma unroll
@@ -221,7 +182,7 @@ __device__ inline void quant_store(const uint16_t *blk, int q, uint8_t *codes, u
         amax = fmaxf(amax, __shfl_xor(amax, 1));
         amax = fmaxf(amax, __shfl_xor(amax, 2));
         float d32 = __fdiv_rn(amax, 127.0f);
-        dbits = f2h_bits(d32);
+        lc.dbits = f2h_bits(d32);
     } else {
         // key = |x| bits (monotonic for finite binary16) , lowest index, sign
         uint32_t key = 0;
@@ -238,30 +199,23 @@ __device__ inline void quant_store(const uint16_t *blk, int q, uint8_t *codes, u
         uint32_t absbits = key >> 6;
         float m = (absbits == 0) ? 0.0f : h2f((uint16_t)(absbits | ((key & 1u) << 15)));
         float d32 = __fdiv_rn(m, (T == KVQ_Q5_0) ? -16.0f : -8.0f);
-        dbits = f2h_bits(d32);
+        lc.dbits = f2h_bits(d32);
     }
-    d = h2f(dbits);
+    const float d = h2f(lc.dbits);
     const float id = (d != 0.0f) ? __fdiv_rn(1.0f, d) : 0.0f;
 
     if (T == KVQ_Q8_0) {
-        uint8_t c[8];
+        uint32_t c[8];
 #pragma unroll
         for (int k = 0; k < 8; k++) {
             const float v = x[k] * id;  // plain binary32 product (contraction is off in this file)
             float r = round_half_away(v);
             r = fminf(127.0f, fmaxf(-127.0f, r));
-            c[k] = (uint8_t)(int8_t)(int)r;
+            c[k] = (uint32_t)(uint8_t)(int8_t)(int)r;
         }
-        if (ROLE == 0) {
-            u32x2 v;
-            v.x = c[0] | (c[1] << 8) | (c[2] << 16) | ((uint32_t)c[3] << 24);
-            v.y = c[4] | (c[5] << 8) | (c[6] << 16) | ((uint32_t)c[7] << 24);
-            *reinterpret_cast<u32x2 *>(codes + unit_index(32 * b + 8 * q)) = v;
-        } else {
-#pragma unroll
-            for (int k = 0; k < 8; k++)
-                codes[unit_index(32 * b + 8 * q + k)] = c[k];
-        }
+        lc.w[0] = c[0] | (c[1] << 8) | (c[2] << 16) | (c[3] << 24);
+        lc.w[1] = c[4] | (c[5] << 8) | (c[6] << 16) | (c[7] << 24);
+        lc.w[2] = lc.w[3] = 0;
     } else {
         constexpr float HALF_RANGE = (T == KVQ_Q5_0) ? 16.5f : 8.5f;
         constexpr int TOP = (T == KVQ_Q5_0) ? 31 : 15;
@@ -273,10 +227,12 @@ __device__ inline void quant_store(const uint16_t *blk, int q, uint8_t *codes, u
             int ci = (int)__builtin_truncf(u);
             c[k] = ci < 0 ? 0 : (ci > TOP ? TOP : ci);
         }
-        uint8_t by[4];
+        uint32_t w = 0;
 #pragma unroll
-        for (int k = 0; k < 4; k++)
-            by[k] = (uint8_t)((c[k] & 15) | ((c[k + 4] & 15) << 4));  // element 4q+k low, 16+4q+k high
+        for (int k = 0; k < 4; k++)  // byte k: element 4q+k low, 16+4q+k high
+            w |= (uint32_t)((c[k] & 15) | ((c[k + 4] & 15) << 4)) << (8 * k);
+        lc.w[0] = w;
+        lc.w[1] = lc.w[2] = lc.w[3] = 0;
         if (T == KVQ_Q5_0) {
             // the block's 32 high bits: this lane's 8, then OR over the quad
             uint32_t h = 0;
@@ -285,20 +241,56 @@ __device__ inline void quant_store(const uint16_t *blk, int q, uint8_t *codes, u
                 h |= ((uint32_t)(c[k] >> 4) << (4 * q + k)) | ((uint32_t)(c[k + 4] >> 4) << (16 + 4 * q + k));
             h |= (uint32_t)__shfl_xor((int)h, 1);
             h |= (uint32_t)__shfl_xor((int)h, 2);
-            if (q == 0)
-                qh[scale_index()] = h;
-        }
-        if (ROLE == 0) {
-            *reinterpret_cast<uint32_t *>(codes + unit_index(16 * b + 4 * q)) =
-                by[0] | (by[1] << 8) | (by[2] << 16) | ((uint32_t)by[3] << 24);
-        } else {
-#pragma unroll
-            for (int k = 0; k < 4; k++)
-                codes[unit_index(16 * b + 4 * q + k)] = by[k];
+            lc.bits = h;
         }
     }
-    if (q == 0)
-        scales[scale_index()] = dbits;
+    return lc;
+}
+
+// Quantize one block (this lane's 8 elements) and store codes, scale and bit
+// word straight into a plane, for token t of pair `pair`.  ROLE 0: the
+// token-major K plane (a lane's units are contiguous: one store); ROLE 1: the
+// 8-token interleaved V plane (one store per unit, 8 tokens apart -- the
+// bulk append stages whole 8-token groups instead).  qh: the bit words (q5_0,
+// turbo3), unused for the other types.
+template <int T, int ROLE>
+__device__ inline void quant_store(const uint16_t *blk, int q, uint8_t *codes, uint16_t *scales, uint32_t *qh,
+                                   int64_t pair, int64_t t, int b, int D, int Tc)
+{
+    constexpr int NU = lane_units<T>();
+    constexpr int W = (T == KVQ_F16) ? 2 : 1;  // bytes per unit
+    const int NB = D / 32;
+    const int64_t U = row_code_bytes(T, D) / W;  // units per row
+    const int64_t UB = U / NB;                    // units per block
+    const LaneCodes lc = quant_lane<T>(blk, q);
+    const int64_t u0 = UB * b + NU * q;  // the lane's first unit in the row
+    const int64_t si = (ROLE == 0) ? (pair * Tc + t) * NB + b : ((pair * (Tc / 8) + t / 8) * NB + b) * 8 + (t & 7);
+    if (ROLE == 0) {
+        uint8_t *dst = codes + ((pair * Tc + t) * U + u0) * W;
+        if (NU * W == 16)
+            *reinterpret_cast<u32x4 *>(dst) = u32x4{lc.w[0], lc.w[1], lc.w[2], lc.w[3]};
+        else if (NU * W == 8)
+            *reinterpret_cast<u32x2 *>(dst) = u32x2{lc.w[0], lc.w[1]};
+        else if (NU * W == 4)
+            *reinterpret_cast<uint32_t *>(dst) = lc.w[0];
+        else
+            *reinterpret_cast<uint16_t *>(dst) = (uint16_t)lc.w[0];
+    } else {
+        const int64_t gbase = (pair * (Tc / 8) + t / 8) * U;
+#pragma unroll
+        for (int k = 0; k < NU; k++) {
+            const int64_t idx = ((gbase + u0 + k) * 8 + (t & 7)) * W;
+            if (W == 2)
+                *reinterpret_cast<uint16_t *>(codes + idx) = (uint16_t)(lc.w[k >> 1] >> (16 * (k & 1)));
+            else
+                codes[idx] = (uint8_t)(lc.w[k >> 2] >> (8 * (k & 3)));
+        }
+    }
+    if (q == 0 && T != KVQ_F16) {
+        scales[si] = lc.dbits;
+        if (T == KVQ_Q5_0 || T == KVQ_TURBO3)
+            qh[si] = lc.bits;
+    }
 }
 
 }  // namespace quant

@@ -73,6 +73,18 @@ def row_bytes(w, t):
             "q4_0": w.head_dim // 2 + w.head_dim // 16}[t]
 
 
+DECODE_SOURCES = ("kvq_decode.hip", "kvq_device.h", "kvq_quant.h", "kvq_internal.h")
+
+
+def decode_sources_hash() -> str:
+    """sha256 over the sources the decode and merge kernels are built from,
+    in a fixed order (the profile summary records the same hash)."""
+    h = hashlib.sha256()
+    for name in DECODE_SOURCES:
+        h.update(open(os.path.join(ROOT, "mixed_precision_quantized_quantize_amd", "csrc", name), "rb").read())
+    return h.hexdigest()
+
+
 def traffic_from_profile(src_hash, workload):
     """Measured HBM bytes per decode call (both kernels) from the committed
     counter summary (FETCH_SIZE and WRITE_SIZE scaled by a plain copy of known
@@ -87,7 +99,7 @@ def traffic_from_profile(src_hash, workload):
                 rec[k.strip()] = v.split("#")[0].strip()
     except OSError:
         return None
-    if rec.get("decode_kernel_source_sha256") != src_hash or "hbm_bytes_per_launch" not in rec:
+    if rec.get("decode_kernel_sources_sha256") != src_hash or "hbm_bytes_per_launch" not in rec:
         return None
     return int(rec["hbm_bytes_per_launch"])
 
@@ -387,8 +399,7 @@ def main():
     kv_step = kv_layer * L
     value = kv_step / (ms_step * 1e-3) / 1e9
     achieved = alg_bytes_launch / (dec_avg_ms * 1e-3) / 1e9
-    src = open(os.path.join(ROOT, "mixed_precision_quantized_quantize_amd", "csrc", "kvq_decode.hip"), "rb").read()
-    traffic = traffic_from_profile(hashlib.sha256(src).hexdigest(), w.name)
+    traffic = traffic_from_profile(decode_sources_hash(), w.name)
 
     result = {
         "metric": "decode-attn KV GB/s (% HBM peak) + tok/s, K8V4 Llama-3-8B shape, 32K ctx",

@@ -197,11 +197,12 @@ int kvq_decode_workspace_bytes(const kvq_shape *shape, size_t *bytes);
  *   out     : device float32 [n_seqs][n_q_heads][head_dim]
  *   workspace, workspace_bytes: device scratch for the partials
  *   n_splits: how many waves share the context of one (sequence, kv head)
- *             pair; 0 chooses (four waves per compute unit over the whole
- *             batch, eight where K is q4_0 or q5_0 or V is q5_0 or turbo3, neither
- *             is f16, head_dim <= 128 and each wave still gets at least 16 tiles, shared in
- *             proportion to each sequence's context, at least four tiles per
- *             wave).  Never more than the pair's 32-token tiles.
+ *             pair; 0 chooses: four waves per compute unit over the whole
+ *             batch (eight where K is q5_0, V is q5_0 or turbo3, or both are
+ *             q4_0 -- neither half f16 -- at head_dim <= 128 while each wave
+ *             still gets at least 16 tiles), shared in proportion to each
+ *             sequence's context, at least four tiles per wave.  Never more
+ *             than the pair's 32-token tiles.
  * Query head hq reads kv head hq / (n_q_heads/n_kv_heads).  Two launches on
  * `stream`.  In the first, the k waves of a pair take its tiles round robin
  * (wave r: tiles r, r+k, ...), and each writes one (max, sum, unnormalized

@@ -114,10 +114,12 @@ int waves_per_cu(const kvq_shape &sh, int32_t kt, int32_t vt, int64_t tiles, int
 {
     if (sh.head_dim > 128)
         return 4;
-    // a binary16 half makes the pair byte-heavy again: f16/q5_0, q5_0/f16 and
-    // f16/turbo3 stream 3-6% faster with four
-    const bool heavy = (kt == KVQ_Q4_0 || kt == KVQ_Q5_0 || vt == KVQ_Q5_0 || vt == KVQ_TURBO3) && kt != KVQ_F16 &&
-                       vt != KVQ_F16;
+    // Measured over all 20 pairs at the Llama-3-8B shape: q4_0 keys are heavy
+    // only beside 4- or 5-bit or turbo3 values (q4_0/q8_0: 138 us with four,
+    // 150 with eight), and a binary16 half makes any pair byte-heavy again
+    // (f16/q5_0, q5_0/f16, f16/turbo3: 3-6% faster with four).
+    const bool heavy = (kt == KVQ_Q5_0 || vt == KVQ_Q5_0 || vt == KVQ_TURBO3 || (kt == KVQ_Q4_0 && vt == KVQ_Q4_0)) &&
+                       kt != KVQ_F16 && vt != KVQ_F16;
     return heavy && tiles >= (int64_t)16 * 8 * cus ? 8 : 4;
 }
 

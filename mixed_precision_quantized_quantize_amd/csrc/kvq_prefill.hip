@@ -196,8 +196,8 @@ __global__ __launch_bounds__(64 * PW) __attribute__((amdgpu_waves_per_eu(D <= 12
 
     const int ntile = (key_end + TILE - 1) / TILE;
 
-    // ---- dequantization of tile t (raw copy in lds[t % NRAW]) into
-    // dq[t & 1].  The tile's jobs are K sets (T, b), then V blocks b; this
+    // ---- dequantization of tile t (raw copy in lds[t % NRAW]) into dqt,
+    // the operand array of its parity (dq0 or dq1).  The tile's jobs are K sets (T, b), then V blocks b; this
     // wave takes jobs wave, wave + PW, ...  As 2*NB is a multiple of PW, the
     // i-th job of every wave is of the same kind: straight-line code with
     // wave-uniform offsets.  MASK: the tile may reach past key_end.
@@ -290,8 +290,8 @@ __global__ __launch_bounds__(64 * PW) __attribute__((amdgpu_waves_per_eu(D <= 12
         }
     };
 
-    // ---- one tile's attention from its operands (dq[t & 1], and the raw
-    // tile for binary16 planes); DG: the tile may hold keys past a row's
+    // ---- one tile's attention from its operands (dqt, and the raw tile for
+    // binary16 planes); DG: the tile may hold keys past a row's
     // position (masking)
     auto compute = [&](auto diag_c, const int t, const uint8_t *const dqt) __attribute__((always_inline)) {
         constexpr bool DG = decltype(diag_c)::value;

@@ -200,8 +200,10 @@ int kvq_decode_workspace_bytes(const kvq_shape *shape, size_t *bytes);
  *             pair; 0 chooses: four waves per compute unit over the whole
  *             batch (eight where K is q5_0, V is q5_0 or turbo3, or both are
  *             q4_0 -- neither half f16 -- at head_dim <= 128 while each wave
- *             still gets at least 16 tiles), shared in proportion to each
- *             sequence's context, at least four tiles per wave.  Never more
+ *             still gets at least 16 tiles); each pair of a sequence with nt
+ *             tiles gets ceil(nt / tau) waves for the smallest tau >= 4
+ *             that keeps the total within that, so that no wave streams
+ *             more than tau tiles whatever the mix of contexts.  Never more
  *             than the pair's 32-token tiles.
  * Query head hq reads kv head hq / (n_q_heads/n_kv_heads).  Two launches on
  * `stream`.  In the first, the k waves of a pair take its tiles round robin

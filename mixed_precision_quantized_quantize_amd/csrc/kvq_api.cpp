@@ -96,9 +96,9 @@ int check_layer(const kvq_cache *c, int32_t layer)
 
 // Decode work split (the kernels describe it): k waves per (sequence, kv
 // head) pair, the same k for the pairs of one sequence.  n_splits > 0 asks
-// for k = n_splits; 0 fills the device (waves_per_cu waves per CU, k about
-// proportional to each sequence's tiles, at least four tiles per wave).
-// Never more waves for a pair than it has tiles.
+// for k = n_splits; 0 fills the device (waves_per_cu waves per CU, every
+// wave at most tau tiles for the smallest tau >= 4 that fits, see
+// decode_plan).  Never more waves for a pair than it has tiles.
 constexpr int AUTO_WAVES_MAX = 4096;
 // Waves per CU of the automatic split.  Where the tile math is heavy for its
 // bytes (K q4_0 or q5_0, or V q5_0 or turbo3: more vector instructions to
@@ -148,10 +148,36 @@ int64_t decode_plan(const kvq_shape &sh, int32_t kt, int32_t vt, const int32_t *
         T += (int64_t)sh.n_kv_heads * ((ctx_len[s] + 31) / 32);
     const int cus = device_cus();
     const int64_t target = std::min<int64_t>((int64_t)cus * waves_per_cu(sh, kt, vt, T, cus), AUTO_WAVES_MAX);
+    // Automatic split: the fewest tiles per wave, tau >= 4, for which
+    // k_s = ceil(nt_s / tau) waves per pair stay within the target -- every
+    // wave then streams at most tau tiles, whatever the mix of contexts (a
+    // share proportional to the context, rounded down, left a short
+    // sequence's single wave with up to twice the average).
+    int64_t tau = 0;
+    if (req <= 0) {
+        int64_t nt_max = 1;
+        for (int s = 0; s < sh.n_seqs; s++)
+            nt_max = std::max<int64_t>(nt_max, (ctx_len[s] + 31) / 32);
+        auto waves = [&](int64_t t) {
+            int64_t w = 0;
+            for (int s = 0; s < sh.n_seqs; s++)
+                w += ((ctx_len[s] + 31) / 32 + t - 1) / t * sh.n_kv_heads;
+            return w;
+        };
+        int64_t lo = std::max<int64_t>(4, (T + target - 1) / target), hi = std::max(lo, nt_max);
+        while (lo < hi) {  // smallest tau in [lo, hi] whose waves fit (hi when none does)
+            const int64_t mid = (lo + hi) / 2;
+            if (waves(mid) <= target)
+                hi = mid;
+            else
+                lo = mid + 1;
+        }
+        tau = lo;
+    }
     int64_t W = 0;
     for (int s = 0; s < sh.n_seqs; s++) {
         const int64_t nt = (ctx_len[s] + 31) / 32;
-        int64_t k = req > 0 ? req : std::min<int64_t>(target * nt / T, nt / 4);
+        int64_t k = req > 0 ? req : (nt + tau - 1) / tau;
         k = std::max<int64_t>(1, std::min<int64_t>(k, nt));
         if (s == 0)
             *k_uniform = (int32_t)k;

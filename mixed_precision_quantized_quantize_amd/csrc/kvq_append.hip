@@ -58,11 +58,12 @@ __device__ inline void append_v(const AppendArgs &a, const int blk_id, const int
     const int q = tid & 3, qw = tid >> 2;
     const int item_l = qw / (8 * NB), rem = qw - item_l * 8 * NB;
     const int b = rem >> 3, ti = rem & 7;
-    const int64_t item = (int64_t)blk_id * IPW + item_l;
-    const int64_t n_items = (int64_t)a.n_seqs * a.H * a.ng;
-    const int gi = (int)(item % a.ng);
-    const int64_t sh = item / a.ng;  // s * H + h
-    const int s = (int)(sh / a.H);
+    // 32-bit indices: the host keeps n_seqs * H * ng below 2^31
+    const int item = blk_id * IPW + item_l;
+    const int n_items = a.n_seqs * a.H * a.ng;
+    const int gi = item % a.ng;
+    const int sh = item / a.ng;  // s * H + h
+    const int s = sh / a.H;
     const bool live = item < n_items;
     const int p0 = live ? a.pos[s] : 0, p1 = p0 + a.n_new;
     const int g = p0 / 8 + gi;

@@ -84,10 +84,6 @@ __global__ __launch_bounds__(64 * PW) __attribute__((amdgpu_waves_per_eu(D <= 12
     constexpr int VL = (VT == KVQ_Q4_0 || VT == KVQ_Q5_0 || VT == KVQ_TURBO3) ? NB : NCT;
     constexpr bool KQ = KT != KVQ_F16, VQ = VT != KVQ_F16;
 
-    // raw tiles: tile t in lds[t % NRAW] (t+1 being dequantized and t+2 in
-    // flight while t is computed)
-    constexpr int NRAW = 3;
-    __shared__ __attribute__((aligned(16))) uint8_t lds[NRAW][g::BYTES];
     // Dequantized operands of the current tile, built once per workgroup:
     // K hi and lo per (score tile T, block b), V (times scale) per (block b,
     // half hh); each set is one MFMA operand, 16 bytes per lane, lane-major.
@@ -99,6 +95,14 @@ __global__ __launch_bounds__(64 * PW) __attribute__((amdgpu_waves_per_eu(D <= 12
     // other's, and may interleave the two
     __shared__ __attribute__((aligned(16))) uint8_t dq0[DQ_BYTES > 0 ? DQ_BYTES : 16];
     __shared__ __attribute__((aligned(16))) uint8_t dq1[DQ_BYTES > 0 ? DQ_BYTES : 16];
+    // raw tiles: tile t in lds[t % NRAW].  While t is computed, t+1 is being
+    // dequantized and the copies of the later tiles are in flight: t+2 with
+    // three buffers, t+2 and t+3 with four, which every pair gets where they
+    // fit beside the operand arrays at the workgroups per CU the kernel is
+    // built for (two at head_dim <= 128, one at 256)
+    constexpr int LDS_WG = (D <= 128 ? 80 : 160) * 1024;
+    constexpr int NRAW = 4 * g::BYTES + 2 * (DQ_BYTES > 0 ? DQ_BYTES : 16) <= LDS_WG ? 4 : 3;
+    __shared__ __attribute__((aligned(16))) uint8_t lds[NRAW][g::BYTES];
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -325,7 +329,15 @@ __global__ __launch_bounds__(64 * PW) __attribute__((amdgpu_waves_per_eu(D <= 12
                     vop[i] = u32x4{vop[i].x & vk[0], vop[i].y & vk[1], vop[i].z & vk[2], vop[i].w & vk[3]};
             }
         }
-        // ---- scores
+        // ---- scores.  The two contraction phases raise the wave's issue
+        // priority (s_setprio), so that while one wave of a SIMD streams its
+        // MFMAs the other wave's softmax fills the vector slots between them.
+        // The score phase does so only where no dequantization is
+        // interleaved with it (both parts binary16): the priority change is
+        // a scheduling boundary, and the interleave is worth more.
+        constexpr bool PRIO_QK = !KQ && !VQ;
+        if (PRIO_QK)
+            __builtin_amdgcn_s_setprio(1);
         floatx4 sacc[RB][2];
 #pragma unroll
         for (int rb = 0; rb < RB; rb++)
@@ -351,6 +363,8 @@ __global__ __launch_bounds__(64 * PW) __attribute__((amdgpu_waves_per_eu(D <= 12
                 }
             }
 
+        if (PRIO_QK)
+            __builtin_amdgcn_s_setprio(0);
         // ---- online softmax per row block; key r of lane group j is tb+8j+r
         half8 pb[RB];
         const bool diag = DG && tb + TILE - 1 > wave_first;  // some key of the tile is past some row's position
@@ -395,6 +409,7 @@ __global__ __launch_bounds__(64 * PW) __attribute__((amdgpu_waves_per_eu(D <= 12
         }
 
         // ---- O^T += V^T . P
+        __builtin_amdgcn_s_setprio(1);
 #pragma unroll
         for (int b = 0; b < NB; b++) {
             half8 va[2];
@@ -418,24 +433,47 @@ __global__ __launch_bounds__(64 * PW) __attribute__((amdgpu_waves_per_eu(D <= 12
 #pragma unroll
         for (int rb = 0; rb < RB; rb++)
             lacc[rb] = mfma(ones, pb[rb], lacc[rb]);
+        __builtin_amdgcn_s_setprio(0);
     };
 
     // ---- the tile loop: one barrier per tile.  At the barrier of tile t,
     // tile t+1's copy has landed (each wave waited for its share), tile t's
     // operands are complete, and every wave is done with tile t-1's operands
     // and with the raw buffer of tile t-1.  Then: start the copy of tile
-    // t+2 into that buffer, build tile t+1's operands, and compute tile t --
-    // the dequantization's vector instructions run beside the MFMAs.
+    // t+NRAW-1 into that buffer, build tile t+1's operands, and compute tile
+    // t -- the dequantization's vector instructions run beside the MFMAs.
     // dqw, dqr: the operand buffers of tiles t+1 and t.  In the loops they
     // are the arrays themselves (pairs of tiles per round), so that the
     // compiler may move tile t's operand reads and MFMAs in between tile
     // t+1's dequantization.
+    // Wait until this wave's copies of the tile before the last one issued
+    // have completed: instruction i of a tile's copy is issued by wave
+    // i % PW, and vector-memory loads complete in issue order, so at most
+    // this wave's share of one tile may remain outstanding.
+    constexpr int NDMA = g::NDMA;
+    static_assert(PW == 4 && (NDMA + 3) / 4 < 64, "vmcnt holds 6 bits");
+    auto wait_share = [&]() __attribute__((always_inline)) {
+        constexpr int c0 = (NDMA + 3) / 4, c1 = (NDMA + 2) / 4, c2 = (NDMA + 1) / 4, c3 = NDMA / 4;
+        switch (wave) {
+        case 0: __builtin_amdgcn_s_waitcnt((c0 & 15) | ((c0 >> 4) << 14) | 0x70 | 0xF00); break;
+        case 1: __builtin_amdgcn_s_waitcnt((c1 & 15) | ((c1 >> 4) << 14) | 0x70 | 0xF00); break;
+        case 2: __builtin_amdgcn_s_waitcnt((c2 & 15) | ((c2 >> 4) << 14) | 0x70 | 0xF00); break;
+        default: __builtin_amdgcn_s_waitcnt((c3 & 15) | ((c3 >> 4) << 14) | 0x70 | 0xF00); break;
+        }
+    };
     auto body = [&](auto diag_c, auto last2_c, const int t, uint8_t *const dqw, const uint8_t *const dqr) __attribute__((always_inline)) {
         constexpr bool LAST2 = decltype(last2_c)::value;  // t = ntile-2: no copy to start, dequant with mask
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        if (NRAW >= 4 && !LAST2)
+            wait_share();  // tile t+1 landed; this wave's copies of tile t+2 may still be in flight
+        else
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
-        if (!LAST2)
+        if (NRAW >= 4) {
+            if (!LAST2 && t + 3 < ntile)
+                issue_tile<KT, VT, D>(lds[(t + 3) % NRAW], (t + 3) * TILE, lane, doff, rs, wave, PW);
+        } else if (!LAST2) {
             issue_tile<KT, VT, D>(lds[(t + 2) % NRAW], (t + 2) * TILE, lane, doff, rs, wave, PW);
+        }
         if (KQ || VQ)
             dequant(std::integral_constant<bool, LAST2>(), t + 1, dqw);
         compute(diag_c, t, dqr);
@@ -447,6 +485,8 @@ __global__ __launch_bounds__(64 * PW) __attribute__((amdgpu_waves_per_eu(D <= 12
     __syncthreads();
     if (ntile > 1)
         issue_tile<KT, VT, D>(lds[1], TILE, lane, doff, rs, wave, PW);
+    if (NRAW >= 4 && ntile > 2)
+        issue_tile<KT, VT, D>(lds[2 % NRAW], 2 * TILE, lane, doff, rs, wave, PW);
     if (KQ || VQ) {
         if (ntile > 1)
             dequant(F(), 0, dq0);

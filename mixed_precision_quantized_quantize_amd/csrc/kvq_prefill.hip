@@ -83,6 +83,9 @@ __global__ __launch_bounds__(64 * PW) __attribute__((amdgpu_waves_per_eu(D <= 12
     constexpr int ROWS_G = 16 * RB * PW;
     constexpr int VL = (VT == KVQ_Q4_0 || VT == KVQ_Q5_0 || VT == KVQ_TURBO3) ? NB : NCT;
     constexpr bool KQ = KT != KVQ_F16, VQ = VT != KVQ_F16;
+    // raised issue priority from the dequantization through the scores (see
+    // the score phase)
+    constexpr bool PRIO_DQ = (KT == KVQ_Q8_0 || KT == KVQ_Q5_0) && VQ;
 
     // Dequantized operands of the current tile, built once per workgroup:
     // K hi and lo per (score tile T, block b), V (times scale) per (block b,
@@ -332,9 +335,12 @@ __global__ __launch_bounds__(64 * PW) __attribute__((amdgpu_waves_per_eu(D <= 12
         // ---- scores.  The two contraction phases raise the wave's issue
         // priority (s_setprio), so that while one wave of a SIMD streams its
         // MFMAs the other wave's softmax fills the vector slots between them.
-        // The score phase does so only where no dequantization is
-        // interleaved with it (both parts binary16): the priority change is
-        // a scheduling boundary, and the interleave is worth more.
+        // The priority change is a scheduling boundary, so where the next
+        // tile's dequantization is interleaved with the score MFMAs, the
+        // raised span starts before that dequantization (body below), and
+        // only for 8- and 5-bit keys with quantized values (1-3% faster); for
+        // the other pairs it measured no faster, or slower (f16/q4_0 +3%,
+        // K4V4 +1%)
         constexpr bool PRIO_QK = !KQ && !VQ;
         if (PRIO_QK)
             __builtin_amdgcn_s_setprio(1);
@@ -363,7 +369,7 @@ __global__ __launch_bounds__(64 * PW) __attribute__((amdgpu_waves_per_eu(D <= 12
                 }
             }
 
-        if (PRIO_QK)
+        if (PRIO_QK || PRIO_DQ)
             __builtin_amdgcn_s_setprio(0);
         // ---- online softmax per row block; key r of lane group j is tb+8j+r
         half8 pb[RB];
@@ -474,6 +480,8 @@ __global__ __launch_bounds__(64 * PW) __attribute__((amdgpu_waves_per_eu(D <= 12
         } else if (!LAST2) {
             issue_tile<KT, VT, D>(lds[(t + 2) % NRAW], (t + 2) * TILE, lane, doff, rs, wave, PW);
         }
+        if (PRIO_DQ)
+            __builtin_amdgcn_s_setprio(1);  // through this dequantization and tile t's scores
         if (KQ || VQ)
             dequant(std::integral_constant<bool, LAST2>(), t + 1, dqw);
         compute(diag_c, t, dqr);

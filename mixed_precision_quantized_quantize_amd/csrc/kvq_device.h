@@ -68,68 +68,61 @@ __device__ inline void deq_q4_pair(uint32_t y, uint32_t &lo, uint32_t &hi)
     hi = h2_bits(__builtin_elementwise_fma(bits_h2(bfi(0x00F000F0u, y, e)), k16, k72));
 }
 
-// q5_0: as deq_q4_pair, with each element's fifth bit supplied in hb_lo (bit
-// 4 / 20: the low-nibble elements of half 0 / 1) and hb_hi (bit 8 / 24: the
-// high-nibble elements) -> binary16 (code - 16), exact:
-// low:  binary16 1024 + c          minus 1040
-// high: binary16 1024 + 16 c       times 1/16 minus 80
-__device__ inline void deq_q5_pair(uint32_t y, uint32_t hb_lo, uint32_t hb_hi, uint32_t &lo, uint32_t &hi)
+// q5_0 codes (c = nibble + 16 * fifth bit) -> binary16 (c - 16), exact, as
+// deq_q4_pair does with nibbles: the five bits of a low-nibble element are
+// inserted under 0x6400 (binary16 1024 + c, minus 1040); those of a
+// high-nibble element one nibble up (1024 + 16 c, times 1/16, minus 80).
+
+// q5_0 K codes of one block for one lane: w as for q4_0, x = the block's
+// high-bit word shifted right by 4j (bits 0..3: elements 4j..4j+3; bits
+// 16..19: elements 16+4j..16+4j+3).  The two fifth bits of an element pair
+// are spread into place by one 24-bit multiply: bits 0, 1 times 0x80010
+// land at 4 and 20 (and at 19 and 5, which the insert masks drop), times
+// 0x800100 at 8 and 24 (and 23, 9).
+__device__ inline half8 k_operand_q5(uint32_t w, uint32_t x)
 {
     const uint32_t e = 0x64006400u;
     const half2 k1040 = {(_Float16)1040.0f, (_Float16)1040.0f};
     const half2 k16 = {(_Float16)0.0625f, (_Float16)0.0625f};
     const half2 k80 = {(_Float16)-80.0f, (_Float16)-80.0f};
-    lo = h2_bits(bits_h2(bfi(0x000F000Fu, y, e) | hb_lo) - k1040);
-    hi = h2_bits(__builtin_elementwise_fma(bits_h2(bfi(0x00F000F0u, y, e) | hb_hi), k16, k80));
-}
-
-// Fifth bits of an element pair for deq_q5_pair: x holds them in bits 0, 1
-// (the low-nibble elements of half 0, 1) and 16, 17 (the high-nibble ones).
-__device__ inline void q5_pair_bits(uint32_t x, uint32_t &hb_lo, uint32_t &hb_hi)
-{
-    hb_lo = ((x & 1u) << 4) | ((x & 2u) << 19);
-    hb_hi = ((x >> 8) & 0x100u) | ((x << 7) & 0x1000000u);
-}
-
-// Fifth bits of two tokens' element pair (a V operand): bit 0 (low-nibble
-// element) and bit 16 (high-nibble element) of sa (token of half 0) and sb.
-__device__ inline void q5_token_bits(uint32_t sa, uint32_t sb, uint32_t &hb_lo, uint32_t &hb_hi)
-{
-    hb_lo = ((sa & 1u) << 4) | ((sb & 1u) << 20);
-    hb_hi = ((sa >> 8) & 0x100u) | ((sb << 8) & 0x1000000u);
-}
-
-// q5_0 K codes of one block for one lane: w as for q4_0, x = the block's
-// high-bit word shifted right by 4j (bits 0..3: elements 4j..4j+3; bits
-// 16..19: elements 16+4j..16+4j+3).
-__device__ inline half8 k_operand_q5(uint32_t w, uint32_t x)
-{
-    uint32_t l01, h01, l23, h23, a, b;
-    q5_pair_bits(x, a, b);
-    deq_q5_pair(__builtin_amdgcn_perm(w, w, 0x0C010C00u), a, b, l01, h01);
-    q5_pair_bits(x >> 2, a, b);
-    deq_q5_pair(__builtin_amdgcn_perm(w, w, 0x0C030C02u), a, b, l23, h23);
-    return pack4(l01, l23, h01, h23);
+    uint32_t lo[2], hi[2];
+#pragma unroll
+    for (int q = 0; q < 2; q++) {
+        const uint32_t y = __builtin_amdgcn_perm(w, w, q ? 0x0C030C02u : 0x0C010C00u);
+        const uint32_t ml = ((x >> (2 * q)) & 3u) * 0x00080010u;
+        const uint32_t mh = ((x >> (16 + 2 * q)) & 3u) * 0x00800100u;
+        lo[q] = h2_bits(bits_h2(bfi(0x001F001Fu, bfi(0x00100010u, ml, y), e)) - k1040);
+        hi[q] = h2_bits(__builtin_elementwise_fma(bits_h2(bfi(0x01F001F0u, bfi(0x01000100u, mh, y), e)), k16, k80));
+    }
+    return pack4(lo[0], lo[1], hi[0], hi[1]);
 }
 
 // q5_0 V operand of one block: the lane's code byte n (element n low, n+16
 // high) for tokens 0..7 in w (bytes of tokens 0..3 in w.x, 4..7 in w.y) and
 // those tokens' high-bit words h[0..7] -> the two operands (channel tiles
-// of elements n and n+16), binary16 (code - 16).
+// of elements n and n+16), binary16 (code - 16).  Per token pair (a, b) the
+// fifth bits are moved into place with rotations (v_alignbit): a's word
+// rotated right by n-4 has element n's bit at 4 and element n+16's at 20,
+// b's rotated by n+12 has them at 20 and 4; bit-field inserts then put them
+// beside the nibbles.
 __device__ inline void v_operand_q5(u32x2 w, const uint32_t (&h)[8], int n, half8 &va0, half8 &va1)
 {
-    uint32_t s[8];
-#pragma unroll
-    for (int i = 0; i < 8; i++)
-        s[i] = h[i] >> n;
+    const uint32_t e = 0x64006400u;
+    const half2 k1040 = {(_Float16)1040.0f, (_Float16)1040.0f};
+    const half2 k16 = {(_Float16)0.0625f, (_Float16)0.0625f};
+    const half2 k80 = {(_Float16)-80.0f, (_Float16)-80.0f};
     uint32_t lo[4], hi[4];
 #pragma unroll
     for (int p = 0; p < 4; p++) {
         const uint32_t word = (p < 2) ? w.x : w.y;
         const uint32_t y = __builtin_amdgcn_perm(word, word, (p & 1) ? 0x0C030C02u : 0x0C010C00u);
-        uint32_t a, b;
-        q5_token_bits(s[2 * p], s[2 * p + 1], a, b);
-        deq_q5_pair(y, a, b, lo[p], hi[p]);
+        const uint32_t ra = __builtin_amdgcn_alignbit(h[2 * p], h[2 * p], (uint32_t)(n - 4));
+        const uint32_t rb = __builtin_amdgcn_alignbit(h[2 * p + 1], h[2 * p + 1], (uint32_t)(n + 12));
+        const uint32_t f_lo = bfi(0x00100000u, rb, ra);  // bit 4: a's element n, bit 20: b's
+        const uint32_t g = bfi(0x00000010u, rb, ra);     // bit 4: b's element n+16, bit 20: a's
+        const uint32_t f_hi = __builtin_amdgcn_alignbit(g, g, 12u);  // -> bits 24 and 8
+        lo[p] = h2_bits(bits_h2(bfi(0x001F001Fu, bfi(0x00100010u, f_lo, y), e)) - k1040);
+        hi[p] = h2_bits(__builtin_elementwise_fma(bits_h2(bfi(0x01F001F0u, bfi(0x01000100u, f_hi, y), e)), k16, k80));
     }
     va0 = pack4(lo[0], lo[1], lo[2], lo[3]);
     va1 = pack4(hi[0], hi[1], hi[2], hi[3]);

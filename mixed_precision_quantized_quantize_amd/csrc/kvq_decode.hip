@@ -277,7 +277,7 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(D <=
     };
 
     // One 32-token tile starting at token tb, from its operands in registers.
-    auto process = [&](const Ops &op, const int tb, const int t_end) {
+    auto process = [&](Ops &op, const int tb, const int t_end) {
         // ---------------- scores: S^T tile T, lane holds tokens 8j+4T+i, head n
         const uint32_t *ksc = op.ks;
         floatx4 sacc[2];
@@ -314,15 +314,28 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(D <=
 #pragma unroll
         for (int r = 0; r < 8; r++)
             x[r] = sacc[r >> 2][r & 3] * c2;
-        const bool tail = tb + TILE > t_end;
-        uint32_t keep[4] = {0xFFFFFFFFu, 0xFFFFFFFFu, 0xFFFFFFFFu, 0xFFFFFFFFu};  // per token pair
-        if (tail) {
+        // The tile past the context (at most one per wave, its last): masked
+        // tokens' scores become -inf, and since positions past the context
+        // may hold any bits, their V scales (binary16 V: their values) are
+        // forced to +0, so that P' = p * scale is +0 rather than 0 * NaN.
+        // Only this branch pays for the masks.
+        if (tb + TILE > t_end) {
+            uint32_t keep[4] = {0xFFFFFFFFu, 0xFFFFFFFFu, 0xFFFFFFFFu, 0xFFFFFFFFu};  // per token pair
 #pragma unroll
             for (int r = 0; r < 8; r++)
                 if (tb + 8 * j + r >= t_end) {
                     x[r] = -INFINITY;
                     keep[r >> 1] &= (r & 1) ? 0x0000FFFFu : 0xFFFF0000u;
                 }
+            if (VT == KVQ_F16) {
+#pragma unroll
+                for (int ct = 0; ct < VL; ct++)
+                    op.v[ct] = u32x4{op.v[ct].x & keep[0], op.v[ct].y & keep[1], op.v[ct].z & keep[2], op.v[ct].w & keep[3]};
+            } else {
+#pragma unroll
+                for (int b = 0; b < NB; b++)
+                    op.vs[b] = u32x4{op.vs[b].x & keep[0], op.vs[b].y & keep[1], op.vs[b].z & keep[2], op.vs[b].w & keep[3]};
+            }
         }
         float mt = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])), fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
         mt = fmaxf(mt, __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(bp16, __builtin_bit_cast(int, mt))));
@@ -355,13 +368,9 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(D <=
             if (VT == KVQ_F16) {
                 pb = pack4(p16[0], p16[1], p16[2], p16[3]);
             } else {
-                // positions past the context may hold any bits: a masked pair
-                // is forced to +0 instead of 0 * (scale bits)
-                const u32x4 dv = op.vs[b];
-                pb = pack4(h2_bits(bits_h2(p16[0]) * bits_h2(dv.x)) & keep[0],
-                           h2_bits(bits_h2(p16[1]) * bits_h2(dv.y)) & keep[1],
-                           h2_bits(bits_h2(p16[2]) * bits_h2(dv.z)) & keep[2],
-                           h2_bits(bits_h2(p16[3]) * bits_h2(dv.w)) & keep[3]);
+                const u32x4 dv = op.vs[b];  // masked tokens' scales are +0 (tail tile)
+                pb = pack4(h2_bits(bits_h2(p16[0]) * bits_h2(dv.x)), h2_bits(bits_h2(p16[1]) * bits_h2(dv.y)),
+                           h2_bits(bits_h2(p16[2]) * bits_h2(dv.z)), h2_bits(bits_h2(p16[3]) * bits_h2(dv.w)));
             }
             if constexpr (VT == KVQ_Q4_0) {
                 // bytes of tokens 0..3 (word 0) and 4..7 (word 1); low nibbles feed
@@ -394,8 +403,7 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(D <=
                     half8 va;
                     const u32x4 w = op.v[ct];
                     if (VT == KVQ_F16) {
-                        // a masked token's value may be any bits, even NaN
-                        va = pack4(w.x & keep[0], w.y & keep[1], w.z & keep[2], w.w & keep[3]);
+                        va = pack4(w.x, w.y, w.z, w.w);  // masked tokens' values are +0 (tail tile)
                     } else {
                         va = deq_q8(w.x, w.y);
                     }

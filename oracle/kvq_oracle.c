@@ -139,6 +139,8 @@ uint16_t kvqo_f32_to_f16(float f)
     double a = fabs((double)f);
     if (isnan(f))
         return (uint16_t)(sign | 0x7e00);
+    if (isinf(f))
+        return (uint16_t)(sign | 0x7c00); /* infinities stay infinite */
     if (a < ldexp(1.0, -14)) {
         /* subnormal range: integer multiple of 2^-24 (1024 means 2^-14) */
         double n = nearbyint(a * ldexp(1.0, 24));

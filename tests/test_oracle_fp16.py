@@ -42,3 +42,11 @@ def test_f32_to_f16_random_and_edges(orc):
     edges = np.concatenate([edges, -edges])
     with np.errstate(over="ignore"):
         assert (orc.f32_to_f16_bits(edges) == edges.astype(np.float16).view(np.uint16)).all()
+
+
+def test_f32_to_f16_infinities(orc):
+    # IEEE 754: an infinite binary32 value converts to the infinity of the
+    # same sign (found by the sanitized oracle run, where +inf had come back
+    # as 1.0 through frexp of an infinity)
+    x = np.array([np.inf, -np.inf], dtype=np.float32)
+    assert (orc.f32_to_f16_bits(x) == x.astype(np.float16).view(np.uint16)).all()

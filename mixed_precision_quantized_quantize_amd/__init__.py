@@ -25,7 +25,8 @@ KVQ_OK, KVQ_E_ARG, KVQ_E_TYPE, KVQ_E_SHAPE, KVQ_E_RANGE, KVQ_E_WORKSPACE, KVQ_E_
 KVQ_MAX_SEQS, KVQ_MAX_GROUP, KVQ_MAX_SPLITS = 256, 16, 256
 
 EXPORTS = ["kvq_strerror", "kvq_plane_bytes", "kvq_cache_check", "kvq_append", "kvq_decode_workspace_bytes",
-           "kvq_attn_decode", "kvq_attn_decode_append", "kvq_attn_prefill_chunk", "kvq_stream_read"]
+           "kvq_attn_decode", "kvq_attn_decode_append", "kvq_attn_prefill_chunk",
+           "kvq_stream_read"]
 
 
 class KvqLibraryMissing(RuntimeError):
@@ -157,6 +158,10 @@ def stream_read(buf, key: int, sink, blocks: int = 0) -> None:
     stream; `sink` is a device uint32 / int32 tensor of at least one element."""
     import torch
 
+    if not (buf.is_cuda and sink.is_cuda and buf.device == sink.device and buf.is_contiguous()):
+        raise ValueError("stream_read: buf and sink must be contiguous tensors on one GPU")
+    if sink.numel() < 1 or sink.element_size() != 4:
+        raise ValueError("stream_read: sink must hold at least one 32-bit element")
     _check(kvq_stream_read(buf.data_ptr(), buf.numel() * buf.element_size(), key, sink.data_ptr(), blocks,
                            torch.cuda.current_stream(buf.device).cuda_stream), "kvq_stream_read")
 
@@ -176,7 +181,8 @@ class KVCache:
         self.shape = kvq_shape(n_layers, n_seqs, n_q_heads, n_kv_heads, head_dim, max_ctx)
         if isinstance(types[0], (str, int)):
             types = [tuple(types)] * n_layers
-        assert len(types) == n_layers
+        if len(types) != n_layers:
+            raise ValueError(f"{len(types)} (k_type, v_type) pairs for {n_layers} layers")
         self.types = [(_type(k), _type(v)) for k, v in types]
         self.k_planes = (kvq_plane * n_layers)()
         self.v_planes = (kvq_plane * n_layers)()
@@ -197,10 +203,44 @@ class KVCache:
     def _stream(self):
         return self.torch.cuda.current_stream(self.device).cuda_stream
 
+    # The C ABI sees only pointers; the kernels index every tensor by the
+    # cache's shape.  Each tensor is therefore checked here -- dtype, shape,
+    # contiguity and device -- before anything reaches the library, so that a
+    # wrong-shaped tensor raises instead of being read or written past its end.
+    def _tensor(self, x, name, dtype, shape):
+        t = self.torch
+        if not isinstance(x, t.Tensor):
+            raise TypeError(f"{name}: expected a torch.Tensor, got {type(x).__name__}")
+        if x.dtype != dtype:
+            raise TypeError(f"{name}: dtype {x.dtype}, expected {dtype}")
+        if tuple(x.shape) != tuple(shape):
+            raise ValueError(f"{name}: shape {tuple(x.shape)}, expected {tuple(shape)}")
+        if not x.is_contiguous():
+            raise ValueError(f"{name}: must be contiguous")
+        if x.device != self.device:
+            raise ValueError(f"{name}: on {x.device}, the cache is on {self.device}")
+        return x
+
+    def _host_ints(self, vals, name):
+        vals = [int(v) for v in vals]
+        if len(vals) != self.shape.n_seqs:
+            raise ValueError(f"{name}: {len(vals)} entries, expected n_seqs = {self.shape.n_seqs}")
+        return vals
+
+    def _layer(self, layer):
+        if not 0 <= int(layer) < self.shape.n_layers:
+            raise IndexError(f"layer {layer} out of range [0, {self.shape.n_layers})")
+        return int(layer)
+
     def append(self, layer, K, V, pos):
         """K, V: binary16 device tensors [S][n_new][Hkv][D]; pos: host ints [S]."""
-        assert K.dtype == self.torch.float16 and V.dtype == self.torch.float16
-        assert K.is_contiguous() and V.is_contiguous() and K.shape == V.shape and K.dim() == 4
+        sh, layer = self.shape, self._layer(layer)
+        if not isinstance(K, self.torch.Tensor) or K.dim() != 4:
+            raise ValueError("K: expected a 4-D tensor [n_seqs][n_new][n_kv_heads][head_dim]")
+        want = (sh.n_seqs, K.shape[1], sh.n_kv_heads, sh.head_dim)
+        self._tensor(K, "K", self.torch.float16, want)
+        self._tensor(V, "V", self.torch.float16, want)
+        pos = self._host_ints(pos, "pos")
         kt, vt = self.types[layer]
         _check(kvq_append(self.desc, layer, K.data_ptr(), V.data_ptr(), K.shape[1], pos, kt, vt, self._stream()),
                "kvq_append")
@@ -211,17 +251,22 @@ class KVCache:
             self._ws = self.torch.empty(max(nb, 16) // 4, dtype=self.torch.float32, device=self.device)
         return self._ws
 
+    def _out(self, out, shape):
+        if out is None:
+            return self.torch.empty(shape, dtype=self.torch.float32, device=self.device)
+        return self._tensor(out, "out", self.torch.float32, shape)
+
     def _decode_args(self, Q, out):
         sh = self.shape
-        assert Q.dtype == self.torch.float16 and Q.is_contiguous()
-        assert tuple(Q.shape) == (sh.n_seqs, sh.n_q_heads, sh.head_dim)
-        if out is None:
-            out = self.torch.empty(tuple(Q.shape), dtype=self.torch.float32, device=self.device)
-        return out, self.workspace()
+        want = (sh.n_seqs, sh.n_q_heads, sh.head_dim)
+        self._tensor(Q, "Q", self.torch.float16, want)
+        return self._out(out, want), self.workspace()
 
     def decode(self, layer, Q, ctx_len, scale, out=None, n_splits=0):
         """Q: binary16 [S][Hq][D] -> float32 [S][Hq][D]."""
+        layer = self._layer(layer)
         out, ws = self._decode_args(Q, out)
+        ctx_len = self._host_ints(ctx_len, "ctx_len")
         _check(kvq_attn_decode(self.desc, layer, Q.data_ptr(), ctx_len, scale, out.data_ptr(), ws.data_ptr(),
                                ws.numel() * 4, n_splits, self._stream()), "kvq_attn_decode")
         return out
@@ -229,11 +274,11 @@ class KVCache:
     def decode_append(self, layer, K, V, Q, ctx_len, scale, out=None, n_splits=0):
         """Writes K, V (binary16 [S][Hkv][D]) at positions ctx_len[s]-1, then
         decodes Q: binary16 [S][Hq][D] -> float32 [S][Hq][D]."""
-        sh = self.shape
-        for x in (K, V):
-            assert x.dtype == self.torch.float16 and x.is_contiguous()
-            assert tuple(x.shape) == (sh.n_seqs, sh.n_kv_heads, sh.head_dim)
+        sh, layer = self.shape, self._layer(layer)
+        for x, name in ((K, "K"), (V, "V")):
+            self._tensor(x, name, self.torch.float16, (sh.n_seqs, sh.n_kv_heads, sh.head_dim))
         out, ws = self._decode_args(Q, out)
+        ctx_len = self._host_ints(ctx_len, "ctx_len")
         _check(kvq_attn_decode_append(self.desc, layer, K.data_ptr(), V.data_ptr(), Q.data_ptr(), ctx_len, scale,
                                       out.data_ptr(), ws.data_ptr(), ws.numel() * 4, n_splits, self._stream()),
                "kvq_attn_decode_append")
@@ -241,9 +286,13 @@ class KVCache:
 
     def prefill(self, layer, Q, q_pos0, scale, out=None):
         """Q: binary16 [S][n_tok][Hq][D] -> float32 [S][n_tok][Hq][D]."""
-        assert Q.dtype == self.torch.float16 and Q.is_contiguous() and Q.dim() == 4
-        if out is None:
-            out = self.torch.empty(tuple(Q.shape), dtype=self.torch.float32, device=self.device)
+        sh, layer = self.shape, self._layer(layer)
+        if not isinstance(Q, self.torch.Tensor) or Q.dim() != 4:
+            raise ValueError("Q: expected a 4-D tensor [n_seqs][n_tok][n_q_heads][head_dim]")
+        want = (sh.n_seqs, Q.shape[1], sh.n_q_heads, sh.head_dim)
+        self._tensor(Q, "Q", self.torch.float16, want)
+        out = self._out(out, want)
+        q_pos0 = self._host_ints(q_pos0, "q_pos0")
         _check(kvq_attn_prefill_chunk(self.desc, layer, Q.data_ptr(), Q.shape[1], q_pos0, scale, out.data_ptr(),
                                       self._stream()), "kvq_attn_prefill_chunk")
         return out

@@ -20,8 +20,9 @@
  *  - llama.cpp issue "Eval bug: Metal fails mixed quantized KV on Apple
  *    Silicon when Flash Attention is unavailable ...": the llama_kv_cache
  *    size log lines (K q8_0 / V q4_0 byte totals) and, under "Expected
- *    behavior", the request for a clear early rejection without partial
- *    initialization -- which is this library's error convention; and, in
+ *    behavior", the wish that an unusable configuration be refused up front,
+ *    before anything has been set up -- this library's error convention
+ *    (every argument is checked before any device work); and, in
  *    its comment thread, q5_0 named as the working middle ground between
  *    q8_0 and q4_0 (the format itself is not on the pages: ggml's 5-bit
  *    block, read the way q4_0 is read below).
@@ -187,8 +188,14 @@ int kvq_append(const kvq_cache *cache, int32_t layer, const void *K, const void 
  * streams) need workspaces of their own. */
 int kvq_decode_workspace_bytes(const kvq_shape *shape, size_t *bytes);
 
-/* Flash-decode one query token per sequence over layer `layer` (the
- * split-K flash decoding the llama.cpp guide runs on the quantized cache).
+/* Flash-decode one query token per sequence over layer `layer`: tiled,
+ * exact softmax attention that never materializes the score row (the
+ * llama.cpp guide, section "Flash Attention"), read straight from the
+ * quantized blocks.  With one query token per sequence there is little
+ * parallel work per (sequence, kv head), so the context of each pair is
+ * split over several waves whose partial results are combined by a
+ * log-sum-exp merge; that split is this library's design (the pages do not
+ * describe one).
  *   Q       : device binary16 [n_seqs][n_q_heads][head_dim]
  *   ctx_len : host int32 [n_seqs], 1 <= ctx_len[s] <= max_ctx; query s
  *             attends to cache positions 0 .. ctx_len[s]-1 (append the new
@@ -242,18 +249,6 @@ int kvq_attn_decode_append(const kvq_cache *cache, int32_t layer, const void *K,
  * non-finite scale). */
 int kvq_attn_prefill_chunk(const kvq_cache *cache, int32_t layer, const void *Q, int32_t n_tok,
                            const int32_t *q_pos0, float scale, float *out, void *stream);
-
-/* ---- measurement support (not part of the attention path) ----
- *
- * Streams `bytes` of device memory at `src` through non-temporal vector loads
- * and discards them: the practical read-bandwidth ceiling that decode
- * figures are compared with.  `src` device, 16-byte aligned, bytes a
- * multiple of 16; `sink` device, one uint32 that is written only if the XOR
- * of everything a lane read equals `key` (pick a key that no lane's fold
- * takes, or ignore the sink).  blocks: workgroups of 256 threads, 0 = eight
- * per compute unit.  KVQ_E_ARG on a null pointer, misalignment or a size
- * that is not a multiple of 16; KVQ_E_HIP if the launch fails. */
-int kvq_stream_read(const void *src, size_t bytes, uint32_t key, uint32_t *sink, int32_t blocks, void *stream);
 
 #ifdef __cplusplus
 }

@@ -1,10 +1,11 @@
 // kvq_api.cpp -- the C ABI of libkvq: host-side validation and dispatch.
 //
 // Every argument is checked here before anything is enqueued, so a failing
-// call returns a KVQ_E_* code with no device side effects -- the "clear early
-// rejection without partial initialization" that the llama.cpp issue asks
-// for under "Expected behavior".  The kernels themselves assume the checked
-// preconditions.
+// call returns a KVQ_E_* code with no device side effects: an unusable
+// configuration is refused up front, before anything is set up, as the
+// llama.cpp issue "Eval bug: Metal fails mixed quantized KV on Apple Silicon
+// when Flash Attention is unavailable" wishes under "Expected behavior".  The
+// kernels themselves assume the checked preconditions.
 #include <math.h>
 #include <string.h>
 

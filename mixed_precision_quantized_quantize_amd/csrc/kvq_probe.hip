@@ -13,6 +13,7 @@
 #include <hip/hip_runtime.h>
 
 #include "kvq.h"
+#include "kvq_probe.h"
 
 namespace kvq {
 namespace {

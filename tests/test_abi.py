@@ -13,7 +13,8 @@ import pytest
 import mixed_precision_quantized_quantize_amd as kvq
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADER = os.path.join(ROOT, "include", "kvq.h")
+HEADERS = [os.path.join(ROOT, "include", f) for f in sorted(os.listdir(os.path.join(ROOT, "include")))
+           if f.endswith(".h")]
 FAKE = 0x7F0000000000  # aligned, never dereferenced
 
 
@@ -27,7 +28,8 @@ def L():
 
 
 def declared_functions():
-    text = open(HEADER).read()
+    """Every kvq_* function declared in include/*.h."""
+    text = "".join(open(h).read() for h in HEADERS)
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     return sorted(set(re.findall(r"\b(kvq_[a-z_]+)\s*\(", text)))
 

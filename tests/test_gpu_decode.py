@@ -69,6 +69,22 @@ def test_decode_many_splits_short_context():
     small_case("q8_0", "q4_0", S=1, Hq=8, Hkv=1, D=128, T=2000, ctx=[1999], n_splits_list=[0, 63, 256], seed=11)
 
 
+@pytest.mark.parametrize("kt,vt,D,T,splits", [
+    # head_dim 128: 256 slots per pair, more than 16 per merge group (8 groups)
+    ("q8_0", "q4_0", 128, 9000, [256, 200]),
+    ("q8_0", "turbo3", 128, 9000, [256]),
+    # head_dim 256: 4 merge groups, 65..128 slots per pair
+    ("q8_0", "q4_0", 256, 4096, [65, 100, 128]),
+    ("q8_0", "turbo3", 256, 4096, [100]),
+])
+def test_decode_merge_chunked_path(kt, vt, D, T, splits):
+    """More partial slots per pair than the merge's one-round-trip paths take
+    (16 per group of channels): the chunked merge, with the turbo3 rotation
+    back on the same path."""
+    print(f"decode merge chunked path {kt}/{vt} D={D} splits={splits}", flush=True)
+    small_case(kt, vt, S=1, Hq=4, Hkv=1, D=D, T=T, ctx=[T - 5], n_splits_list=splits, seed=D + len(splits))
+
+
 # ---------------------------------------------------------------- named workloads
 
 def workload_layer(name, layer, seqs_check, heads_check, pair=None, chunk_tokens=2048):
@@ -119,18 +135,21 @@ def test_llama3_8b_32k_full_size_sampled():
     workload_layer("llama3_8b_32k", 0, [0, 13], [0, 7, 8, 31])
 
 
-def test_llama31_70b_32k_full_size_sampled():
-    workload_layer("llama31_70b_32k", 0, [0], [0, 9, 63])
+def test_llama31_70b_32k_full_size_all_heads():
+    """The one sequence of the 70B-shaped layer, every one of its 64 query
+    heads (its many waves per pair exercise the merge's larger paths)."""
+    workload_layer("llama31_70b_32k", 0, [0], list(range(64)))
 
 
-def test_llama31_70b_32k_turbo3_full_size_sampled():
+def test_llama31_70b_32k_turbo3_full_size_all_heads():
     """The TurboQuant page's configuration: Llama-3.1-70B shape at 32K tokens,
-    keys q8_0, values turbo3."""
-    workload_layer("llama31_70b_32k", 0, [0], [0, 9, 63], pair=("q8_0", "turbo3"))
+    keys q8_0, values turbo3; all 64 query heads."""
+    workload_layer("llama31_70b_32k", 0, [0], list(range(64)), pair=("q8_0", "turbo3"))
 
 
-def test_llama3_8b_128k_decode_full_size_sampled():
-    workload_layer("llama3_8b_128k_prefill", 0, [3], [0, 17])
+def test_llama3_8b_128k_decode_full_size_all_heads():
+    """K4V4 decode at 131072 tokens: every query head of one sequence."""
+    workload_layer("llama3_8b_128k_prefill", 0, [3], list(range(32)))
 
 
 # ---------------------------------------------------------------- merge and graph replay

@@ -178,6 +178,8 @@ class KVCache:
 
         self.torch = torch
         self.device = torch.device(device)
+        if self.device.type == "cuda" and self.device.index is None:  # compare as tensors report it
+            self.device = torch.device("cuda", torch.cuda.current_device())
         self.shape = kvq_shape(n_layers, n_seqs, n_q_heads, n_kv_heads, head_dim, max_ctx)
         if isinstance(types[0], (str, int)):
             types = [tuple(types)] * n_layers

@@ -123,7 +123,9 @@ enum {
     KVQ_E_SHAPE = -3,     /* unsupported head_dim / head grouping / counts    */
     KVQ_E_RANGE = -4,     /* layer, position or context length out of range   */
     KVQ_E_WORKSPACE = -5, /* workspace NULL or smaller than required          */
-    KVQ_E_HIP = -6        /* a HIP call or kernel launch failed               */
+    KVQ_E_HIP = -6,       /* a HIP call or kernel launch failed               */
+    KVQ_E_TOO_BIG = -7    /* kvq_attn_decode_append_noalloc: the call needs
+                             more partial slots than its static scratch holds */
 };
 
 /* Supported limits. */
@@ -249,6 +251,33 @@ int kvq_attn_decode_append(const kvq_cache *cache, int32_t layer, const void *K,
  * non-finite scale). */
 int kvq_attn_prefill_chunk(const kvq_cache *cache, int32_t layer, const void *Q, int32_t n_tok,
                            const int32_t *q_pos0, float scale, float *out, void *stream);
+
+/* ---- for callers that cannot allocate device memory ----
+ *
+ * kvq_attn_decode_append without the workspace argument, for callers that
+ * cannot call hipMalloc or allocate through a library: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation.  The
+ * partial slots live in a static device array of KVQ_NOALLOC_SCRATCH_BYTES
+ * that the library holds on every GPU it runs on until the process ends; its
+ * device address is looked up once per device, at the first call on that
+ * device (with that device current).  Nothing is allocated by any call.
+ *   - A call whose partial slots (kvq_attn_decode's need for this call's
+ *     work split: waves x (n_q_heads/n_kv_heads) x (head_dim+4) floats)
+ *     exceed KVQ_NOALLOC_SCRATCH_BYTES returns KVQ_E_TOO_BIG before any
+ *     device work.  At group 8 and head_dim 128 the array holds 3971 waves'
+ *     slots (4224 B each): more than the automatic split of a 256-CU device
+ *     uses for any batch of at most 1024 (sequence, kv head) pairs.
+ *   - Every call on one GPU shares that GPU's array, which keeps the last
+ *     call's partials.  No call needs it cleared: each wave writes its slot
+ *     before the merge reads it.  Calls that overlap in time on one GPU
+ *     (other streams, other threads) race on the array and must not be
+ *     issued; calls ordered on one stream are safe.
+ * Other arguments, results and errors as kvq_attn_decode_append; for the
+ * same arguments and n_splits the planes and `out` are bit-identical. */
+#define KVQ_NOALLOC_SCRATCH_BYTES ((size_t)16 << 20)
+int kvq_attn_decode_append_noalloc(const kvq_cache *cache, int32_t layer, const void *K, const void *V,
+                                   const void *Q, const int32_t *ctx_len, float scale, float *out,
+                                   int32_t n_splits, void *stream);
 
 #ifdef __cplusplus
 }

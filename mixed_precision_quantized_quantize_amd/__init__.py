@@ -22,10 +22,12 @@ TYPES = {"f16": F16, "q8_0": Q8_0, "q4_0": Q4_0, "q5_0": Q5_0, "turbo3": TURBO3}
 TYPE_NAMES = {v: k for k, v in TYPES.items()}
 
 KVQ_OK, KVQ_E_ARG, KVQ_E_TYPE, KVQ_E_SHAPE, KVQ_E_RANGE, KVQ_E_WORKSPACE, KVQ_E_HIP = 0, -1, -2, -3, -4, -5, -6
+KVQ_E_TOO_BIG = -7
 KVQ_MAX_SEQS, KVQ_MAX_GROUP, KVQ_MAX_SPLITS = 256, 16, 256
+KVQ_NOALLOC_SCRATCH_BYTES = 16 << 20
 
 EXPORTS = ["kvq_strerror", "kvq_plane_bytes", "kvq_cache_check", "kvq_append", "kvq_decode_workspace_bytes",
-           "kvq_attn_decode", "kvq_attn_decode_append", "kvq_attn_prefill_chunk",
+           "kvq_attn_decode", "kvq_attn_decode_append", "kvq_attn_prefill_chunk", "kvq_attn_decode_append_noalloc",
            "kvq_stream_read"]
 
 
@@ -79,6 +81,8 @@ def lib():
                                                  vp, vp, sz, i32, vp]
             L.kvq_attn_prefill_chunk.argtypes = [P(kvq_cache), i32, vp, i32, P(ctypes.c_int32), ctypes.c_float,
                                                  vp, vp]
+            L.kvq_attn_decode_append_noalloc.argtypes = [P(kvq_cache), i32, vp, vp, vp, P(ctypes.c_int32),
+                                                         ctypes.c_float, vp, i32, vp]
             L.kvq_stream_read.argtypes = [vp, sz, ctypes.c_uint32, vp, i32, vp]
             for name in EXPORTS:
                 if name != "kvq_strerror":
@@ -146,6 +150,12 @@ def kvq_attn_prefill_chunk(cache: kvq_cache, layer: int, Q_ptr: int, n_tok: int,
                            out_ptr: int, stream: int) -> int:
     return lib().kvq_attn_prefill_chunk(ctypes.byref(cache), int(layer), Q_ptr, int(n_tok), _i32_array(q_pos0),
                                         float(scale), out_ptr, stream)
+
+
+def kvq_attn_decode_append_noalloc(cache: kvq_cache, layer: int, K_ptr: int, V_ptr: int, Q_ptr: int, ctx_len,
+                                   scale: float, out_ptr: int, n_splits: int, stream: int) -> int:
+    return lib().kvq_attn_decode_append_noalloc(ctypes.byref(cache), int(layer), K_ptr, V_ptr, Q_ptr,
+                                                _i32_array(ctx_len), float(scale), out_ptr, int(n_splits), stream)
 
 
 def kvq_stream_read(src_ptr: int, nbytes: int, key: int, sink_ptr: int, blocks: int, stream: int) -> int:
@@ -284,6 +294,22 @@ class KVCache:
         _check(kvq_attn_decode_append(self.desc, layer, K.data_ptr(), V.data_ptr(), Q.data_ptr(), ctx_len, scale,
                                       out.data_ptr(), ws.data_ptr(), ws.numel() * 4, n_splits, self._stream()),
                "kvq_attn_decode_append")
+        return out
+
+    def decode_append_noalloc(self, layer, K, V, Q, ctx_len, scale, out, n_splits=0):
+        """decode_append through kvq_attn_decode_append_noalloc: the partial
+        slots live in the library's static per-GPU scratch array, and nothing
+        is allocated (``out`` is required for that reason)."""
+        sh, layer = self.shape, self._layer(layer)
+        for x, name in ((K, "K"), (V, "V")):
+            self._tensor(x, name, self.torch.float16, (sh.n_seqs, sh.n_kv_heads, sh.head_dim))
+        want = (sh.n_seqs, sh.n_q_heads, sh.head_dim)
+        self._tensor(Q, "Q", self.torch.float16, want)
+        self._tensor(out, "out", self.torch.float32, want)
+        ctx_len = self._host_ints(ctx_len, "ctx_len")
+        _check(kvq_attn_decode_append_noalloc(self.desc, layer, K.data_ptr(), V.data_ptr(), Q.data_ptr(), ctx_len,
+                                              scale, out.data_ptr(), n_splits, self._stream()),
+               "kvq_attn_decode_append_noalloc")
         return out
 
     def prefill(self, layer, Q, q_pos0, scale, out=None):

@@ -10,12 +10,43 @@
 #include <string.h>
 
 #include <algorithm>
+#include <mutex>
 
 #include "kvq_internal.h"
 
 using namespace kvq;
 
+// Partial slots of kvq_attn_decode_append_noalloc: a static array that every
+// GPU the library runs on holds until the process ends.  In host code this
+// name is only a host-side stand-in; the array's device address on the
+// current device comes from noalloc_scratch() below and is what the kernels
+// receive.
+static __device__ __align__(256) uint8_t scratch[KVQ_NOALLOC_SCRATCH_BYTES];
+
 namespace {
+
+constexpr int MAX_DEVICES = 64;
+
+// The array's address on the current device, looked up once per device (with
+// that device current) and kept: each GPU holds its own copy of the array at
+// its own address.  KVQ_E_HIP if the lookup fails.
+int noalloc_scratch(void **ptr)
+{
+    static std::mutex mu;
+    static void *addr[MAX_DEVICES] = {nullptr};
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= MAX_DEVICES)
+        return KVQ_E_HIP;
+    std::lock_guard<std::mutex> lock(mu);
+    if (!addr[dev]) {
+        void *p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p)
+            return KVQ_E_HIP;
+        addr[dev] = p;
+    }
+    *ptr = addr[dev];
+    return KVQ_OK;
+}
 
 bool valid_type(int32_t t)
 {
@@ -212,6 +243,7 @@ const char *kvq_strerror(int code)
     case KVQ_E_RANGE: return "layer, position or context length out of range";
     case KVQ_E_WORKSPACE: return "workspace missing or too small";
     case KVQ_E_HIP: return "HIP launch failed";
+    case KVQ_E_TOO_BIG: return "the call needs more partial slots than the no-allocation entry point's static scratch holds (KVQ_NOALLOC_SCRATCH_BYTES)";
     default: return "unknown kvq error code";
     }
 }
@@ -306,9 +338,11 @@ int kvq_decode_workspace_bytes(const kvq_shape *shape, size_t *bytes)
 
 namespace {
 
+// noalloc: the partial slots go into the static scratch array instead of
+// `workspace` (which is then ignored).
 int attn_decode(const kvq_cache *cache, int32_t layer, const void *K, const void *V, const void *Q,
                 const int32_t *ctx_len, float scale, float *out, void *workspace, size_t workspace_bytes,
-                int32_t n_splits, void *stream)
+                int32_t n_splits, void *stream, bool noalloc = false)
 {
     int rc = check_layer(cache, layer);
     if (rc)
@@ -331,6 +365,13 @@ int attn_decode(const kvq_cache *cache, int32_t layer, const void *K, const void
                                   &a.k_uniform);
     if (W >= ((int64_t)1 << 31) / 64)
         return KVQ_E_SHAPE;
+    if (noalloc) {
+        if (workspace_need(sh, W) > KVQ_NOALLOC_SCRATCH_BYTES)
+            return KVQ_E_TOO_BIG;
+        if ((rc = noalloc_scratch(&workspace)) != KVQ_OK)
+            return rc;
+        workspace_bytes = KVQ_NOALLOC_SCRATCH_BYTES;
+    }
     if (!workspace || !aligned16(workspace) || workspace_bytes < workspace_need(sh, W))
         return KVQ_E_WORKSPACE;
 
@@ -386,6 +427,15 @@ int kvq_attn_decode_append(const kvq_cache *cache, int32_t layer, const void *K,
     if (!K || !V || !aligned16(K) || !aligned16(V))
         return KVQ_E_ARG;
     return attn_decode(cache, layer, K, V, Q, ctx_len, scale, out, workspace, workspace_bytes, n_splits, stream);
+}
+
+int kvq_attn_decode_append_noalloc(const kvq_cache *cache, int32_t layer, const void *K, const void *V,
+                                   const void *Q, const int32_t *ctx_len, float scale, float *out,
+                                   int32_t n_splits, void *stream)
+{
+    if (!K || !V || !aligned16(K) || !aligned16(V))
+        return KVQ_E_ARG;
+    return attn_decode(cache, layer, K, V, Q, ctx_len, scale, out, nullptr, 0, n_splits, stream, true);
 }
 
 int kvq_attn_prefill_chunk(const kvq_cache *cache, int32_t layer, const void *Q, int32_t n_tok,

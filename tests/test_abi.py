@@ -45,7 +45,7 @@ def test_exports_every_declared_symbol(L):
 
 
 def test_strerror(L):
-    for c in range(-6, 1):
+    for c in range(-7, 1):
         assert kvq.kvq_strerror(c)
     assert "unknown" in kvq.kvq_strerror(-99)
 
@@ -196,6 +196,31 @@ def test_decode_append_rejections(L):
     assert call(ns=257) == kvq.KVQ_E_RANGE
     assert call(Q=None) == kvq.KVQ_E_ARG
     assert call(layer=2) == kvq.KVQ_E_RANGE
+
+
+def test_decode_append_noalloc_rejections(L):
+    """The no-allocation step validates like kvq_attn_decode_append, and a
+    call whose partial slots exceed the static scratch is refused before any
+    device work (only calls that fail validation run here)."""
+    sh = shape()
+    c = make_cache(sh)
+
+    def call(c=c, K=FAKE, V=FAKE, ctx=(100, 50), ns=0, Q=FAKE, out=FAKE, layer=1):
+        return kvq.kvq_attn_decode_append_noalloc(c, layer, K, V, Q, list(ctx), 0.125, out, ns, None)
+
+    assert call(K=None) == kvq.KVQ_E_ARG
+    assert call(V=FAKE + 2) == kvq.KVQ_E_ARG
+    assert call(ctx=(0, 5)) == kvq.KVQ_E_RANGE
+    assert call(ns=257) == kvq.KVQ_E_RANGE
+    assert call(Q=None) == kvq.KVQ_E_ARG
+    assert call(out=FAKE + 4) == kvq.KVQ_E_ARG
+    assert call(layer=2) == kvq.KVQ_E_RANGE
+    # 4 sequences x 4 kv heads x 256 splits = 4096 waves, each 16 heads x 260
+    # floats: 68 MB of partials, more than KVQ_NOALLOC_SCRATCH_BYTES
+    big = make_cache(shape(n_layers=1, n_seqs=4, n_q_heads=64, n_kv_heads=4, head_dim=256, max_ctx=8192))
+    assert 4096 * 16 * 260 * 4 > kvq.KVQ_NOALLOC_SCRATCH_BYTES
+    assert call(c=big, ctx=(8192,) * 4, ns=256, layer=0) == kvq.KVQ_E_TOO_BIG
+    assert "static scratch" in kvq.kvq_strerror(kvq.KVQ_E_TOO_BIG)
 
 
 def test_prefill_rejections(L):

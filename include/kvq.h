@@ -183,11 +183,15 @@ int kvq_append(const kvq_cache *cache, int32_t layer, const void *K, const void 
                const int32_t *pos, int32_t k_type, int32_t v_type, void *stream);
 
 /* Workspace bytes that kvq_attn_decode (and kvq_attn_decode_append) need for
- * any ctx_len <= max_ctx and any n_splits: one partial slot of
- * (n_q_heads/n_kv_heads) * (head_dim+4) floats per wave, for the most waves
- * a call can use (see kvq_attn_decode).  No initialization is needed.  A
- * workspace serves one call at a time: calls that overlap in time (other
- * streams) need workspaces of their own. */
+ * any ctx_len <= max_ctx and any n_splits: one 32-bit counter per (sequence,
+ * kv head) pair (padded to 256 bytes), then one partial slot of
+ * (n_q_heads/n_kv_heads) * (head_dim+4) floats per workgroup of four waves,
+ * for the most workgroups a call can use (see kvq_attn_decode).
+ * The workspace must be zero-filled before its first use (the counters start
+ * at zero); every call leaves them zero again, so it is cleared once, not per
+ * call.  A workspace belongs to caches of one shape, and serves one call at a
+ * time: calls that overlap in time (other streams) need workspaces of their
+ * own. */
 int kvq_decode_workspace_bytes(const kvq_shape *shape, size_t *bytes);
 
 /* Flash-decode one query token per sequence over layer `layer`: tiled,
@@ -204,23 +208,27 @@ int kvq_decode_workspace_bytes(const kvq_shape *shape, size_t *bytes);
  *             token's K/V first: ctx_len counts it)
  *   scale   : multiplies Q.K (typically 1/sqrt(head_dim)), used as passed
  *   out     : device float32 [n_seqs][n_q_heads][head_dim]
- *   workspace, workspace_bytes: device scratch for the partials
+ *   workspace, workspace_bytes: device scratch for the partials and the
+ *             merge counters (zero-filled before the first call, see
+ *             kvq_decode_workspace_bytes)
  *   n_splits: how many waves share the context of one (sequence, kv head)
  *             pair; 0 chooses: four waves per compute unit over the whole
  *             batch (eight where K is q5_0, V is q5_0 or turbo3, or both are
  *             q4_0 -- neither half f16 -- at head_dim <= 128 while each wave
  *             still gets at least 16 tiles); each pair of a sequence with nt
- *             tiles gets ceil(nt / tau) waves for the smallest tau >= 4
- *             that keeps the total within that, so that no wave streams
- *             more than tau tiles whatever the mix of contexts.  Never more
- *             than the pair's 32-token tiles.
- * Query head hq reads kv head hq / (n_q_heads/n_kv_heads).  Two launches on
- * `stream`.  In the first, the k waves of a pair take its tiles round robin
- * (wave r: tiles r, r+k, ...), and each writes one (max, sum, unnormalized
- * output) partial.  The second merges the k partials of every pair and
- * query head (log-sum-exp) into `out`.  Errors: KVQ_E_RANGE (ctx_len,
- * n_splits > KVQ_MAX_SPLITS), KVQ_E_WORKSPACE, KVQ_E_SHAPE (2^25 or more
- * waves). */
+ *             tiles gets ceil(nt / tau) waves, rounded up to a multiple of
+ *             four, for the smallest tau >= 4 that keeps the total within
+ *             that, so that no wave streams more than tau tiles whatever the
+ *             mix of contexts.  Never more than the pair's 32-token tiles,
+ *             nor more than KVQ_MAX_SPLITS.
+ * Query head hq reads kv head hq / (n_q_heads/n_kv_heads).  One launch on
+ * `stream`.  The k waves of a pair, in workgroups of four, take its tiles
+ * round robin (wave r: tiles r, r+k, ...); the four waves of a workgroup
+ * combine their (max, sum, unnormalized output) partials, and the pair's
+ * last workgroup to finish combines the workgroups' partials (log-sum-exp,
+ * in a fixed order: results are bitwise repeatable) into `out`.  Errors:
+ * KVQ_E_RANGE (ctx_len, n_splits > KVQ_MAX_SPLITS), KVQ_E_WORKSPACE,
+ * KVQ_E_SHAPE (2^23 or more workgroups). */
 int kvq_attn_decode(const kvq_cache *cache, int32_t layer, const void *Q, const int32_t *ctx_len, float scale,
                     float *out, void *workspace, size_t workspace_bytes, int32_t n_splits, void *stream);
 
@@ -261,20 +269,23 @@ int kvq_attn_prefill_chunk(const kvq_cache *cache, int32_t layer, const void *Q,
  * that the library holds on every GPU it runs on until the process ends; its
  * device address is looked up once per device, at the first call on that
  * device (with that device current).  Nothing is allocated by any call.
- *   - A call whose partial slots (kvq_attn_decode's need for this call's
- *     work split: waves x (n_q_heads/n_kv_heads) x (head_dim+4) floats)
- *     exceed KVQ_NOALLOC_SCRATCH_BYTES returns KVQ_E_TOO_BIG before any
- *     device work.  At group 8 and head_dim 128 the array holds 3971 waves'
- *     slots (4224 B each): more than the automatic split of a 256-CU device
- *     uses for any batch of at most 1024 (sequence, kv head) pairs.
- *   - Every call on one GPU shares that GPU's array, which keeps the last
- *     call's partials.  No call needs it cleared: each wave writes its slot
- *     before the merge reads it.  Calls that overlap in time on one GPU
- *     (other streams, other threads) race on the array and must not be
- *     issued; calls ordered on one stream are safe.
+ *   - The array holds the merge counters of up to KVQ_NOALLOC_MAX_PAIRS
+ *     (sequence, kv head) pairs (32 KiB), then the partial slots: one of
+ *     (n_q_heads/n_kv_heads) x (head_dim+4) floats per workgroup of the
+ *     call's work split.  A call with more pairs, or more slots than the
+ *     rest of the array holds, returns KVQ_E_TOO_BIG before any device work.
+ *     At group 8 and head_dim 128 (4224 B a slot) that is 3964 workgroups:
+ *     more than the automatic split of a 256-CU device uses for any batch.
+ *   - The first call on a device also enqueues a small kernel that zeroes
+ *     the counter region; every call leaves the counters zero.  Every call
+ *     on one GPU shares that GPU's array, which keeps the last call's
+ *     partials.  Calls that overlap in time on one GPU (other streams, other
+ *     threads) race on the array and must not be issued; calls ordered on one
+ *     stream are safe.
  * Other arguments, results and errors as kvq_attn_decode_append; for the
  * same arguments and n_splits the planes and `out` are bit-identical. */
 #define KVQ_NOALLOC_SCRATCH_BYTES ((size_t)16 << 20)
+#define KVQ_NOALLOC_MAX_PAIRS 8192 /* n_seqs * n_kv_heads of a call */
 int kvq_attn_decode_append_noalloc(const kvq_cache *cache, int32_t layer, const void *K, const void *V,
                                    const void *Q, const int32_t *ctx_len, float scale, float *out,
                                    int32_t n_splits, void *stream);

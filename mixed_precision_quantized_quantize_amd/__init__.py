@@ -260,7 +260,8 @@ class KVCache:
     def workspace(self):
         if self._ws is None:
             nb = kvq_decode_workspace_bytes(self.shape)
-            self._ws = self.torch.empty(max(nb, 16) // 4, dtype=self.torch.float32, device=self.device)
+            # zero-filled once: the merge counters at its start must be zero before the first call
+            self._ws = self.torch.zeros(max(nb, 16) // 4, dtype=self.torch.float32, device=self.device)
         return self._ws
 
     def _out(self, out, shape):

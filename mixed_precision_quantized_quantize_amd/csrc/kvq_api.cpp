@@ -27,10 +27,25 @@ namespace {
 
 constexpr int MAX_DEVICES = 64;
 
+// The scratch array starts with a fixed region of counters for up to
+// KVQ_NOALLOC_MAX_PAIRS (sequence, kv head) pairs, whatever the shape of a
+// call, so that one call's slots never land where another call's counters
+// are; the slots follow it.
+constexpr size_t NOALLOC_COUNTER_BYTES = (size_t)KVQ_NOALLOC_MAX_PAIRS * 4;
+
+__global__ void zero_words(uint32_t *p, int n)
+{
+    const int i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < n)
+        p[i] = 0u;
+}
+
 // The array's address on the current device, looked up once per device (with
 // that device current) and kept: each GPU holds its own copy of the array at
-// its own address.  KVQ_E_HIP if the lookup fails.
-int noalloc_scratch(void **ptr)
+// its own address.  The first call on a device also clears the counter
+// region (a small kernel on the caller's stream; every later call leaves the
+// counters zero).  KVQ_E_HIP if the lookup or the launch fails.
+int noalloc_scratch(void **ptr, void *stream)
 {
     static std::mutex mu;
     static void *addr[MAX_DEVICES] = {nullptr};
@@ -41,6 +56,10 @@ int noalloc_scratch(void **ptr)
     if (!addr[dev]) {
         void *p = nullptr;
         if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p)
+            return KVQ_E_HIP;
+        hipLaunchKernelGGL(zero_words, dim3((KVQ_NOALLOC_MAX_PAIRS + 255) / 256), dim3(256), 0, (hipStream_t)stream,
+                           (uint32_t *)p, KVQ_NOALLOC_MAX_PAIRS);
+        if (hipGetLastError() != hipSuccess)
             return KVQ_E_HIP;
         addr[dev] = p;
     }
@@ -170,10 +189,13 @@ int device_cus()
     return cached[dev];
 }
 
-// Fills wave_start[0..n_seqs] and returns the wave count W; *k_uniform is
-// the waves per pair when all sequences have the same number, else 0.
+// Plans a decode call: k[s] waves per pair of sequence s, in kw_s =
+// ceil(k[s]/4) workgroups; fills wg_start[0..n_seqs] and *kw_uniform (the
+// workgroups per pair when all sequences have the same count, else 0) and
+// returns the workgroup count.  Never more waves for a pair than it has
+// tiles, nor more than KVQ_MAX_SPLITS.
 int64_t decode_plan(const kvq_shape &sh, int32_t kt, int32_t vt, const int32_t *ctx_len, int32_t req,
-                    int32_t *wave_start, int32_t *k_uniform)
+                    int32_t *wg_start, int16_t *k_out, int32_t *kw_uniform)
 {
     int64_t T = 0;
     for (int s = 0; s < sh.n_seqs; s++)
@@ -206,28 +228,38 @@ int64_t decode_plan(const kvq_shape &sh, int32_t kt, int32_t vt, const int32_t *
         }
         tau = lo;
     }
-    int64_t W = 0;
+    int64_t n_wg = 0;
     for (int s = 0; s < sh.n_seqs; s++) {
         const int64_t nt = (ctx_len[s] + 31) / 32;
         int64_t k = req > 0 ? req : (nt + tau - 1) / tau;
-        k = std::max<int64_t>(1, std::min<int64_t>(k, nt));
+        if (req <= 0)
+            k = (k + 3) / 4 * 4;  // whole workgroups of four waves where the tiles allow
+        k = std::max<int64_t>(1, std::min<int64_t>({k, nt, (int64_t)KVQ_MAX_SPLITS}));
+        const int64_t kw = (k + 3) / 4;
+        k_out[s] = (int16_t)k;
         if (s == 0)
-            *k_uniform = (int32_t)k;
-        else if (*k_uniform != k)
-            *k_uniform = 0;
-        wave_start[s] = (int32_t)W;
-        W += k * sh.n_kv_heads;
+            *kw_uniform = (int32_t)kw;
+        else if (*kw_uniform != kw)
+            *kw_uniform = 0;
+        wg_start[s] = (int32_t)n_wg;
+        n_wg += kw * sh.n_kv_heads;
     }
-    wave_start[sh.n_seqs] = (int32_t)W;
-    return W;
+    wg_start[sh.n_seqs] = (int32_t)n_wg;
+    return n_wg;
 }
 
-// Workspace: one partial slot of [G][head_dim + 4] floats per wave.
-size_t workspace_need(const kvq_shape &sh, int64_t W)
+// Workspace: one counter per (sequence, kv head) pair (zero between calls),
+// padded to 256 bytes, then one slot of [G][head_dim + 4] floats per
+// workgroup.
+size_t counters_bytes(const kvq_shape &sh) { return ((size_t)sh.n_seqs * sh.n_kv_heads * 4 + 255) / 256 * 256; }
+
+size_t slot_bytes(const kvq_shape &sh, int64_t n_wg)
 {
     const int64_t G = sh.n_q_heads / sh.n_kv_heads;
-    return (size_t)(W * G * (sh.head_dim + 4) * (int64_t)sizeof(float));
+    return (size_t)(n_wg * G * (sh.head_dim + 4) * (int64_t)sizeof(float));
 }
+
+size_t workspace_need(const kvq_shape &sh, int64_t n_wg) { return counters_bytes(sh) + slot_bytes(sh, n_wg); }
 
 }  // namespace
 
@@ -324,13 +356,12 @@ int kvq_decode_workspace_bytes(const kvq_shape *shape, size_t *bytes)
         return rc;
     if (!bytes)
         return KVQ_E_ARG;
-    // the most waves any call can use: at most one per tile of a full cache,
-    // KVQ_MAX_SPLITS per pair, or the automatic choice (which may round up to
-    // one wave per pair)
+    // the most workgroups any call can use: per pair ceil(k/4) for at most
+    // min(tiles of a full cache, KVQ_MAX_SPLITS) waves
     const int64_t pairs = (int64_t)shape->n_seqs * shape->n_kv_heads;
-    const int64_t t_max = pairs * (capacity(shape->max_ctx) / 32);
-    const int64_t w_max = std::min<int64_t>(t_max, std::max<int64_t>(AUTO_WAVES_MAX + pairs, (int64_t)KVQ_MAX_SPLITS * pairs));
-    *bytes = workspace_need(*shape, w_max);
+    const int64_t nt_max = capacity(shape->max_ctx) / 32;
+    const int64_t kw_max = (std::min<int64_t>(nt_max, KVQ_MAX_SPLITS) + 3) / 4;
+    *bytes = workspace_need(*shape, pairs * kw_max);
     return KVQ_OK;
 }
 
@@ -355,24 +386,25 @@ int attn_decode(const kvq_cache *cache, int32_t layer, const void *K, const void
     if (n_splits < 0 || n_splits > KVQ_MAX_SPLITS)
         return KVQ_E_RANGE;
     DecodeArgs a;
-    MergeArgs m;
     memset(&a, 0, sizeof(a));
-    memset(&m, 0, sizeof(m));
     for (int s = 0; s < sh.n_seqs; s++)
         if (ctx_len[s] < 1 || ctx_len[s] > sh.max_ctx)
             return KVQ_E_RANGE;
-    const int64_t W = decode_plan(sh, cache->k[layer].type, cache->v[layer].type, ctx_len, n_splits, a.wave_start,
-                                  &a.k_uniform);
-    if (W >= ((int64_t)1 << 31) / 64)
+    const int64_t n_wg = decode_plan(sh, cache->k[layer].type, cache->v[layer].type, ctx_len, n_splits, a.wg_start,
+                                     a.k, &a.kw_uniform);
+    if (n_wg >= ((int64_t)1 << 31) / 256)
         return KVQ_E_SHAPE;
+    size_t counter_region = counters_bytes(sh);
     if (noalloc) {
-        if (workspace_need(sh, W) > KVQ_NOALLOC_SCRATCH_BYTES)
+        if ((int64_t)sh.n_seqs * sh.n_kv_heads > KVQ_NOALLOC_MAX_PAIRS ||
+            NOALLOC_COUNTER_BYTES + slot_bytes(sh, n_wg) > KVQ_NOALLOC_SCRATCH_BYTES)
             return KVQ_E_TOO_BIG;
-        if ((rc = noalloc_scratch(&workspace)) != KVQ_OK)
+        if ((rc = noalloc_scratch(&workspace, stream)) != KVQ_OK)
             return rc;
         workspace_bytes = KVQ_NOALLOC_SCRATCH_BYTES;
+        counter_region = NOALLOC_COUNTER_BYTES;
     }
-    if (!workspace || !aligned16(workspace) || workspace_bytes < workspace_need(sh, W))
+    if (!workspace || !aligned16(workspace) || workspace_bytes < counter_region + slot_bytes(sh, n_wg))
         return KVQ_E_WORKSPACE;
 
     const kvq_plane &kp = cache->k[layer], &vp = cache->v[layer];
@@ -385,27 +417,18 @@ int attn_decode(const kvq_cache *cache, int32_t layer, const void *K, const void
     a.q = (const uint16_t *)Q;
     a.knew = (const uint16_t *)K;
     a.vnew = (const uint16_t *)V;
-    a.ws = (float *)workspace;
+    a.out = out;
+    a.counters = (uint32_t *)workspace;
+    a.ws = (float *)((uint8_t *)workspace + counter_region);
     a.Hq = sh.n_q_heads;
     a.Hkv = sh.n_kv_heads;
     a.G = sh.n_q_heads / sh.n_kv_heads;
     a.Tc = (int32_t)capacity(sh.max_ctx);
     a.n_seqs = sh.n_seqs;
-    a.W = (int32_t)W;
+    a.n_wg = (int32_t)n_wg;
     a.c2 = (float)((double)scale * 1.4426950408889634);
     memcpy(a.ctx_len, ctx_len, sizeof(int32_t) * sh.n_seqs);
-
-    m.ws = a.ws;
-    m.out = out;
-    m.Hq = a.Hq;
-    m.Hkv = a.Hkv;
-    m.G = a.G;
-    m.D = sh.head_dim;
-    m.v_rotated = vp.type == KVQ_TURBO3;
-    m.n_seqs = sh.n_seqs;
-    m.k_uniform = a.k_uniform;
-    memcpy(m.wave_start, a.wave_start, sizeof(int32_t) * (sh.n_seqs + 1));
-    hipError_t e = launch_decode(kp.type, vp.type, sh.head_dim, a, m, sh.n_seqs * sh.n_kv_heads, (hipStream_t)stream);
+    hipError_t e = launch_decode(kp.type, vp.type, sh.head_dim, a, (hipStream_t)stream);
     return e == hipSuccess ? KVQ_OK : KVQ_E_HIP;
 }
 

@@ -1,5 +1,6 @@
-// kvq_decode.hip -- flash decode over the quantized cache: one persistent
-// streaming kernel and one log-sum-exp merge kernel.
+// kvq_decode.hip -- flash decode over the quantized cache: one launch per
+// call, a persistent streaming kernel whose workgroups also merge their
+// partial results.
 //
 // Flash attention in the sense of the llama.cpp guide's "Flash Attention"
 // section (tiled, the score matrix never materialized, exactly softmax
@@ -7,14 +8,12 @@
 // discussion expects the gain "integrated directly into FlashAttention", and
 // the llama.cpp issue shows a quantized V cache is only usable that way.
 //
-// Work split.  Every (sequence, kv head) pair gets k waves (k per sequence,
-// about proportional to its context, at least one tile per wave); wave r of
-// a pair takes the pair's 32-token tiles r, r+k, r+2k, ... so that the k
-// waves stream neighbouring tiles at any moment.  Each wave writes one
-// partial -- running max m (base 2), sum l and the unnormalized output O of
-// each query head -- into its own slot, and the merge kernel combines the k
-// partials of each pair.  A wave keeps the copies of its next two tiles in
-// flight while it computes the current one.
+// Work split.  Every (sequence, kv head) pair gets k waves (k per sequence)
+// in kw = ceil(k/4) workgroups of four waves; wave r = 4*rw + w of the pair
+// (workgroup rw, wave w) takes the pair's 32-token tiles r, r+k, r+2k, ...
+// so that the k waves stream neighbouring tiles at any moment (a wave with
+// r >= k has none).  A wave keeps the copies of its next tiles in flight
+// while it computes the current one.
 //
 // Per tile a wave serves the whole GQA group (up to 16 query heads) of its kv
 // head with two matrix-core contractions, both v_mfma_f32_16x16x32_f16:
@@ -28,6 +27,20 @@
 // tokens interleaved, so a lane's P.V operand (8 tokens of one channel) is
 // one 8- or 16-byte load.  Online softmax runs in base 2 (scores times
 // scale*log2 e).
+//
+// Merge.  The four waves of a workgroup combine their (max, sum, output)
+// partials in LDS.  A pair served by one workgroup writes its output right
+// there.  Otherwise each workgroup writes its combined partial into its slot
+// of the workspace and counts itself in on the pair's counter; the workgroup
+// that arrives last combines the pair's slots (log-sum-exp, in slot order,
+// so that results do not depend on arrival order), writes the output and
+// puts the counter back to zero.  The eight XCDs' L2 caches are not coherent
+// with each other, and a release fence would write back a whole L2 in every
+// workgroup; instead the slots are written and read with device-coherent
+// (sc1) stores and loads -- the way the compiler implements relaxed
+// agent-scope atomics, which need no L2 writeback -- and a workgroup's slot
+// stores have completed (s_waitcnt vmcnt(0)) before its counter increment is
+// issued.  No workgroup ever waits for another.
 #include <algorithm>
 #include <type_traits>
 
@@ -51,10 +64,50 @@ constexpr int decode_nbuf()
     using g = Geo<KT, VT, D>;
     constexpr int NDMA = g::NDMA;
     int n = KVQ_DECODE_NBUF;
-    while (n > 1 && (n * g::LDS_A > 160 * 1024 || (n - 1) * NDMA >= 64))
+    while (n > 1 && (n * g::LDS_A + 64 > 160 * 1024 || (n - 1) * NDMA >= 64))
         n--;
     return n;
 }
+
+// f(integral_constant<int, 0>), ..., f(integral_constant<int, N-1>), in order.
+template <int N, class F>
+__device__ inline __attribute__((always_inline)) void static_for(F &&f)
+{
+    if constexpr (N > 0) {
+        static_for<N - 1>(f);
+        f(std::integral_constant<int, N - 1>());
+    }
+}
+
+// Cache policy bit of a device-coherent (agent-scope) access: sc1.
+constexpr int CPOL_SC1 = 16;
+
+// turbo3 values: rotate a 32-channel block of the output back, x = s.(H y)/32,
+// for a quad of channels c .. c+3 (c a multiple of 4) per lane, eight lanes
+// per block: butterflies of span 1 and 2 inside the quad, 4, 8, 16 across
+// lanes; then the signs and 1/32.
+__device__ inline floatx4 rotate_back_quad(floatx4 v, const int c)
+{
+    const float a0 = v[0] + v[1], a1 = v[0] - v[1], a2 = v[2] + v[3], a3 = v[2] - v[3];
+    v = floatx4{a0 + a2, a1 + a3, a0 - a2, a1 - a3};
+#pragma unroll
+    for (int span = 4; span < 32; span <<= 1) {
+        const bool upper = (c & span) != 0;
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+            const float o = __shfl_xor(v[i], span / 4);
+            v[i] = upper ? o - v[i] : v[i] + o;
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < 4; i++)
+        v[i] *= ((TQ3_SIGNS >> ((c + i) & 31)) & 1u) ? -0.03125f : 0.03125f;
+    return v;
+}
+
+// LDS of the final merge: weights and sums of up to KVQ_MAX_WG_PER_PAIR
+// slots x 16 query heads.
+constexpr int MERGE_SLOTS = KVQ_MAX_WG_PER_PAIR * KVQ_MAX_GROUP;
 
 template <int KT, int VT, int D>
 __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(D <= 128 ? 2 : 1))) void decode_kernel(const DecodeArgs a)
@@ -62,56 +115,65 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(D <=
     using g = Geo<KT, VT, D>;
     constexpr int NB = g::NB, NCT = g::NCT;
 
-    // NBUF tile buffers per wave, as many as fit (up to KVQ_DECODE_NBUF), in
-    // separate arrays so that the compiler sees that a read of one does not
-    // wait for another
+    // NBUF tile buffers per wave, as many as fit (up to KVQ_DECODE_NBUF),
+    // indexed by compile-time constants only, so that the compiler sees that
+    // a read of one does not wait for another
     constexpr int NBUF = decode_nbuf<KT, VT, D>();
-    __shared__ __attribute__((aligned(16))) uint8_t lds_a[g::LDS_A];
-    __shared__ __attribute__((aligned(16))) uint8_t lds_b[NBUF >= 2 ? g::LDS_A : 16];
-    __shared__ __attribute__((aligned(16))) uint8_t lds_c[NBUF >= 3 ? g::LDS_A : 16];
+    __shared__ __attribute__((aligned(16))) uint8_t lds_t[NBUF][g::LDS_A];
+    uint8_t *const lds_a = lds_t[0];
+    // the arrival verdict of the counter increment
+    __shared__ int mrg_last;
+    // The workgroup's own merge reuses lds_a once every wave has left its
+    // tile loop (per wave and head m and l, then the running sum of O); the
+    // final merge's per-(slot, head) weights and sums reuse it after that.
+    static_assert(WAVES * 32 * 4 + KVQ_MAX_GROUP * D * 4 <= g::LDS_A, "workgroup merge fits in lds_a");
+    static_assert(2 * MERGE_SLOTS * 4 <= g::LDS_A, "final merge fits in lds_a");
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: scalar addressing
     const int n = lane & 15, j = lane >> 4;
-    const int gw = blockIdx.x * WAVES + wave;
-    if (gw >= a.W)
-        return;
     const int G = a.G, Hkv = a.Hkv;
     const int64_t Tc = a.Tc;
+    const int n_pairs = a.n_seqs * Hkv;
 
-    // this wave's pair (s, h) and its index r among the pair's k waves.
-    // The pairs are interleaved over the grid (wave gw serves pair
-    // gw mod pairs), so that every pair gets waves from early- and
-    // late-dispatched workgroups alike: with two workgroups per CU the first
-    // one on a CU runs well ahead of the second, and pairs served by only one
-    // of them would finish far apart.  When every sequence has k waves per
-    // pair this is a division; else the sequences' first waves are binary
-    // searched (dependent scalar loads) and the heads of one sequence are
-    // interleaved.
-    int s = 0, k = a.k_uniform, h, r;
-    if (k > 0) {
-        const int n_pairs = a.n_seqs * Hkv;
-        r = gw / n_pairs;
-        const int pg = gw - r * n_pairs;
+    // This workgroup's pair (s, h) and its index rw among the pair's kw
+    // workgroups.  The pairs are interleaved over the grid (workgroup b
+    // serves pair b mod pairs when every sequence has kw workgroups per pair),
+    // so that every pair gets workgroups from early- and late-dispatched
+    // parts of the grid alike; otherwise the sequences' first workgroups are
+    // binary searched (dependent scalar loads) and the heads of one sequence
+    // are interleaved.  slot0 / slot_step: the workspace slots of the pair's
+    // workgroups rw' = 0 .. kw-1 are slot0 + rw' * slot_step.
+    const int b = blockIdx.x;
+    int s = 0, kw = a.kw_uniform, h, rw, slot0, slot_step;
+    if (kw > 0) {
+        rw = b / n_pairs;
+        const int pg = b - rw * n_pairs;
         s = pg / Hkv;
         h = pg - s * Hkv;
+        slot0 = pg;
+        slot_step = n_pairs;
     } else {
-        int hi = a.n_seqs;  // wave_start[s] <= gw < wave_start[hi]
+        int hi = a.n_seqs;  // wg_start[s] <= b < wg_start[hi]
         while (hi - s > 1) {
             const int mid = (s + hi) >> 1;
-            if (a.wave_start[mid] <= gw)
+            if (a.wg_start[mid] <= b)
                 s = mid;
             else
                 hi = mid;
         }
-        k = (a.wave_start[s + 1] - a.wave_start[s]) / Hkv;
-        const int local = gw - a.wave_start[s];
-        r = local / Hkv;
-        h = local - r * Hkv;
+        kw = (a.wg_start[s + 1] - a.wg_start[s]) / Hkv;
+        const int local = b - a.wg_start[s];
+        rw = local / Hkv;
+        h = local - rw * Hkv;
+        slot0 = a.wg_start[s] + h;
+        slot_step = Hkv;
     }
+    const int k = a.k[s];           // waves per pair
+    const int r = 4 * rw + wave;    // this wave among them
     const int ctx = a.ctx_len[s];
     const int nt = (ctx + TILE - 1) / TILE;
-    const int n_mine = (nt - r + k - 1) / k;  // tiles r, r+k, ... below nt (>= 1)
+    const int n_mine = r < k ? (nt - r + k - 1) / k : 0;  // tiles r, r+k, ... below nt
     const int64_t pair = (int64_t)s * Hkv + h;
 
     // Fused one-row append: the wave that reads the pair's last tile first
@@ -122,14 +184,14 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(D <=
     if (a.knew != nullptr && r == (nt - 1) % k) {
         const int quad = lane >> 2, q = lane & 3;
         if (quad < 2 * NB) {
-            const int role = quad >= NB, b = quad - role * NB;
-            const uint16_t *blk = (role ? a.vnew : a.knew) + pair * D + 32 * b;
+            const int role = quad >= NB, bb = quad - role * NB;
+            const uint16_t *blk = (role ? a.vnew : a.knew) + pair * D + 32 * bb;
             if (role == 0)
                 quant::quant_store<KT, 0>(blk, q, const_cast<uint8_t *>(a.kc), const_cast<uint16_t *>(a.ks),
-                                          const_cast<uint32_t *>(a.kqh), pair, ctx - 1, b, D, a.Tc);
+                                          const_cast<uint32_t *>(a.kqh), pair, ctx - 1, bb, D, a.Tc);
             else
                 quant::quant_store<VT, 1>(blk, q, const_cast<uint8_t *>(a.vc), const_cast<uint16_t *>(a.vs),
-                                          const_cast<uint32_t *>(a.vqh), pair, ctx - 1, b, D, a.Tc);
+                                          const_cast<uint32_t *>(a.vqh), pair, ctx - 1, bb, D, a.Tc);
         }
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     }
@@ -426,22 +488,22 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(D <=
     // newer tiles' copies has completed.
     constexpr int NDMA = g::NDMA;
     static_assert((NBUF - 1) * NDMA < 64, "vmcnt holds 6 bits");
-    constexpr int WAIT_ALL = 0x70 | 0xF00;  // vmcnt(0), expcnt and lgkmcnt untouched
-    constexpr int WAIT_1 = (NDMA & 15) | ((NDMA >> 4) << 14) | 0x70 | 0xF00;                    // vmcnt(NDMA)
-    constexpr int WAIT_2 = ((2 * NDMA) & 15) | (((2 * NDMA) >> 4) << 14) | 0x70 | 0xF00;        // vmcnt(2*NDMA)
+    // s_waitcnt immediate for vmcnt(n * NDMA), expcnt and lgkmcnt untouched
+    auto wait_imm = [](int n) constexpr { return ((n * NDMA) & 15) | (((n * NDMA) >> 4) << 14) | 0x70 | 0xF00; };
+    auto wait_newer = [&](const int newer) __attribute__((always_inline)) {
+        // at most `newer` tiles' copies may still be outstanding
+        static_for<NBUF>([&](auto c) {
+            if (newer == c)
+                __builtin_amdgcn_s_waitcnt(wait_imm(c));
+        });
+    };
 
     reset();
     // Tile i (of n_mine) sits in `buf`; the copies of tiles i+1 .. i+NBUF-1
     // (those below n_mine) were issued after it; tile i+NBUF goes into `buf`
     // once tile i's operands are in registers.
-    auto step = [&](uint8_t *buf, const int i) {
-        const int newer = min(NBUF - 1, n_mine - 1 - i);
-        if (NBUF >= 3 && newer >= 2)
-            __builtin_amdgcn_s_waitcnt(WAIT_2);
-        else if (NBUF >= 2 && newer >= 1)
-            __builtin_amdgcn_s_waitcnt(WAIT_1);
-        else
-            __builtin_amdgcn_s_waitcnt(WAIT_ALL);
+    auto step = [&](uint8_t *buf, const int i) __attribute__((always_inline)) {
+        wait_newer(min(NBUF - 1, n_mine - 1 - i));
         Ops op;
         read_ops(buf, op);
         if (i + NBUF < n_mine) {
@@ -450,241 +512,183 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(D <=
         }
         process(op, (r + i * k) * TILE, ctx);
     };
-    uint8_t *const buf_a = lds_a + wave * g::BYTES;
-    uint8_t *const buf_b = lds_b + wave * g::BYTES;
-    uint8_t *const buf_c = lds_c + wave * g::BYTES;
-    issue_tile<KT, VT, D, CPOL_STREAM>(buf_a, r * TILE, lane, doff, rs);
-    if (NBUF >= 2 && n_mine > 1)
-        issue_tile<KT, VT, D, CPOL_STREAM>(buf_b, (r + k) * TILE, lane, doff, rs);
-    if (NBUF >= 3 && n_mine > 2)
-        issue_tile<KT, VT, D, CPOL_STREAM>(buf_c, (r + 2 * k) * TILE, lane, doff, rs);
+    static_for<NBUF>([&](auto u) {  // an idle wave (r >= k, n_mine = 0) streams nothing
+        if (u < n_mine)
+            issue_tile<KT, VT, D, CPOL_STREAM>(lds_t[u] + wave * g::BYTES, (r + u * k) * TILE, lane, doff, rs);
+    });
     int i = 0;
-    for (; i + NBUF <= n_mine; i += NBUF) {
-        step(buf_a, i);
-        if constexpr (NBUF >= 2)
-            step(buf_b, i + 1);
-        if constexpr (NBUF >= 3)
-            step(buf_c, i + 2);
-    }
-    if (NBUF >= 2 && i < n_mine)
-        step(buf_a, i++);
-    if (NBUF >= 3 && i < n_mine)
-        step(buf_b, i++);
+    for (; i + NBUF <= n_mine; i += NBUF)
+        static_for<NBUF>([&](auto u) { step(lds_t[u] + wave * g::BYTES, i + u); });
+    static_for<NBUF - 1>([&](auto u) {  // the last n_mine mod NBUF tiles, in buffers 0, 1, ...
+        if (i < n_mine) {
+            step(lds_t[u] + wave * g::BYTES, i);
+            i++;
+        }
+    });
 
-    // ---------------- the wave's partial: O of head n (channels 16ct + 4j + i),
-    // m, l -- buffer stores from the scalar base of the slot
+    // ---------------- merge the workgroup's four partials in LDS.  Lane
+    // (n, j) holds head n's running max m_run (base 2, equal in the four lane
+    // groups), its share l_run of the running sum, and O of channels
+    // 16ct + 4j + i.  Waves with no tiles hold m = -inf, l = 0, O = 0; wave
+    // 0 always has tiles (4 rw < k), so every head's maximum is finite.
     float l_tot = l_run + __shfl_xor(l_run, 16);
     l_tot += __shfl_xor(l_tot, 32);
-    if (n < G) {
-        const __amdgpu_buffer_rsrc_t rw = make_rsrc(a.ws + (int64_t)gw * G * (D + 4), G * (D + 4) * 4);
-        const int off = 4 * (n * (D + 4) + 4 * j);
-#pragma unroll
-        for (int ct = 0; ct < NCT; ct++)
-            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, o[ct]), rw, off + 64 * ct, 0, 0);
-        if (j == 0) {
-            __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, m_run), rw, off + 4 * D, 0, 0);
-            __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, l_tot), rw, off + 4 * D + 4, 0, 0);
-        }
+    __syncthreads();  // every wave has left its tile loop: lds_a is free
+    float *const ml = reinterpret_cast<float *>(lds_a);        // [wave][m: 16 | l: 16]
+    float *const acc = ml + WAVES * 32;                        // [G][D]: running sum of the scaled O
+    if (j == 0) {
+        ml[wave * 32 + n] = m_run;
+        ml[wave * 32 + 16 + n] = l_tot;
     }
-}
-
-// Log-sum-exp merge of the partials of one (sequence, kv head) pair for one
-// query head: workgroup = (pair, head), P groups of one thread per output
-// channel.  The slot weights 2^(m_j - M) go through LDS in chunks; group p
-// sums slots p, p+P, ... of a chunk, up to sixteen independent loads at a time, and
-// the groups' sums are added through LDS at the end.  P grows with the
-// slots per pair so that a long merge is not one thread's chain of loads.
-constexpr int MERGE_CHUNK = 512;
-constexpr int MERGE_MAX_THREADS = 1024;
-
-__device__ inline float block_reduce(float v, float *sh, bool is_max)
-{
-    // wave64 butterfly, then across the waves of the workgroup through LDS
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) {
-        const float u = __shfl_xor(v, o);
-        v = is_max ? fmaxf(v, u) : v + u;
-    }
-    const int wave = threadIdx.x >> 6, nw = (blockDim.x + 63) >> 6;
     __syncthreads();
-    if ((threadIdx.x & 63) == 0)
-        sh[wave] = v;
-    __syncthreads();
-    float r = sh[0];
-    for (int w = 1; w < nw; w++)
-        r = is_max ? fmaxf(r, sh[w]) : r + sh[w];
-    return r;
-}
-
-// turbo3 values: rotate each 32-channel block of the output back,
-// x = s.(H y)/32 -- butterflies of span 1..16 across the 32 threads (lanes)
-// of the block, thread c holding channel c
-__device__ inline float rotate_back(float r, const int c)
-{
+    float M = ml[n];
 #pragma unroll
-    for (int span = 1; span < 32; span <<= 1) {
-        const float o = __shfl_xor(r, span);
-        r = (c & span) ? o - r : r + o;
-    }
-    return ((TQ3_SIGNS >> (c & 31)) & 1u) ? -r * 0.03125f : r * 0.03125f;
-}
-
-// Channel c of one query head from its k <= KF partials (slot j at
-// base + j*stride): all 3*KF loads issued together (slots past k repeat the
-// last one and weigh nothing), then sum_j O_j[c] 2^(m_j - M) / sum_j l_j 2^(m_j - M)
-// in slot order.
-template <int KF>
-__device__ inline float merge_few(const float *base, const int64_t stride, const int k, const int c, const int D)
-{
-    float mj[KF], lj[KF], oj[KF];
+    for (int w = 1; w < WAVES; w++)
+        M = fmaxf(M, ml[w * 32 + n]);
+    float L = 0.0f;
 #pragma unroll
-    for (int j = 0; j < KF; j++) {
-        const float *pk = base + (int64_t)min(j, k - 1) * stride;
-        mj[j] = pk[D];
-        lj[j] = pk[D + 1];
-        oj[j] = pk[c];
-    }
-    float M = mj[0];
+    for (int w = 0; w < WAVES; w++)  // fixed order: results do not depend on timing
+        L += ml[w * 32 + 16 + n] * __builtin_amdgcn_exp2f(ml[w * 32 + n] - M);
+    const float f = __builtin_amdgcn_exp2f(m_run - M);
 #pragma unroll
-    for (int j = 1; j < KF; j++)
-        if (j < k)
-            M = fmaxf(M, mj[j]);
-    float L = 0.0f, acc = 0.0f;
+    for (int ct = 0; ct < NCT; ct++)
+        o[ct] *= f;
+    // O summed over the waves in wave order; the last wave keeps the sum
+    floatx4 *const accv = reinterpret_cast<floatx4 *>(acc + n * D + 4 * j);
 #pragma unroll
-    for (int j = 0; j < KF; j++)
-        if (j < k) {
-            const float w = __builtin_amdgcn_exp2f(mj[j] - M);
-            L += lj[j] * w;
-            acc += oj[j] * w;
-        }
-    return acc / L;
-}
-
-__global__ __launch_bounds__(MERGE_MAX_THREADS) void merge_kernel(const MergeArgs a)
-{
-    __shared__ float wts[MERGE_CHUNK];
-    __shared__ float red[MERGE_MAX_THREADS / 64];
-    __shared__ float part[MERGE_MAX_THREADS];
-    const int G = a.G, D = a.D, Dp = a.D + 4;
-    const int P = blockDim.x / D;  // groups; blockDim.x == P * D
-    const int pair = blockIdx.x / G, gg = blockIdx.x - pair * G;
-    const int s = pair / a.Hkv, h = pair - s * a.Hkv;
-    const int k = (a.wave_start[s + 1] - a.wave_start[s]) / a.Hkv;  // the pair's waves = its slots
-    // slot of wave r of the pair (the decode kernel's interleave): r*pairs + pair
-    // when every sequence has k waves per pair, else first(s) + r*Hkv + h
-    const int w0 = a.k_uniform > 0 ? pair : a.wave_start[s] + h;
-    const int slot_step = a.k_uniform > 0 ? a.n_seqs * a.Hkv : a.Hkv;
-    const int nslot = k;
-    const int64_t stride = (int64_t)slot_step * G * Dp;  // floats between the pair's consecutive slots
-    const float *base = a.ws + ((int64_t)w0 * G + gg) * Dp;
-    const int t = threadIdx.x, c = t % D, grp = t / D;
-    float *const dst = a.out + ((int64_t)s * a.Hq + (int64_t)h * G + gg) * D + c;
-
-    if (nslot <= 16) {
-        // few slots (the usual case): one thread per channel loads the (m, l)
-        // and O of every slot at once -- one round trip, no barriers
-        if (grp > 0)
-            return;  // whole waves: D is a multiple of 64
-        const float r = nslot <= 8 ? merge_few<8>(base, stride, nslot, c, D) : merge_few<16>(base, stride, nslot, c, D);
-        *dst = a.v_rotated ? rotate_back(r, c) : r;
-        return;
-    }
-
-    if (nslot <= 16 * P && nslot <= (int)blockDim.x) {
-        // up to 16 slots per group: thread t loads slot t's (m, l), and each
-        // thread the O values of its group's slots grp, grp+P, ... -- all
-        // loads issued together, one round trip; then the maximum, the
-        // weights (through LDS) and the sums
-        float mt = -INFINITY, lt = 0.0f;
-        if (t < nslot) {
-            mt = base[(int64_t)t * stride + D];
-            lt = base[(int64_t)t * stride + D + 1];
-        }
-        float ov[16];
+    for (int w = 0; w < WAVES; w++) {
+        if (wave == w && n < G) {
 #pragma unroll
-        for (int u = 0; u < 16; u++)
-            ov[u] = base[(int64_t)min(grp + u * P, nslot - 1) * stride + c];
-        const float M = block_reduce(mt, red, true);
-        const float w = t < nslot ? __builtin_amdgcn_exp2f(mt - M) : 0.0f;
-        if (t < nslot)
-            wts[t] = w;
-        const float L = block_reduce(lt * w, red, false);  // its barriers also publish wts
-        float acc = 0.0f;
-#pragma unroll
-        for (int u = 0; u < 16; u++)
-            if (grp + u * P < nslot)
-                acc += ov[u] * wts[grp + u * P];
-        if (P > 1) {
-            part[t] = acc;
-            __syncthreads();
-            if (grp == 0)
-                for (int g2 = 1; g2 < P; g2++)
-                    acc += part[g2 * D + c];
-        }
-        float r = acc / L;
-        if (a.v_rotated && grp == 0)  // whole waves take this branch
-            r = rotate_back(r, c);
-        if (grp == 0)
-            *dst = r;
-        return;
-    }
-
-    float mx = -INFINITY;
-    for (int j = t; j < nslot; j += blockDim.x)
-        mx = fmaxf(mx, base[j * stride + D]);
-    const float M = block_reduce(mx, red, true);
-
-    float lsum = 0.0f, acc = 0.0f;
-    for (int k0 = 0; k0 < nslot; k0 += MERGE_CHUNK) {
-        const int chunk = min(MERGE_CHUNK, nslot - k0);
-        __syncthreads();  // the previous chunk's weights are no longer read
-        for (int j = t; j < chunk; j += blockDim.x) {
-            const float *pk = base + (int64_t)(k0 + j) * stride;
-            const float w = __builtin_amdgcn_exp2f(pk[D] - M);
-            wts[j] = w;
-            lsum += pk[D + 1] * w;
-        }
-        __syncthreads();
-        const float *pc = base + (int64_t)k0 * stride + c;
-        int j = grp;
-        // batches of U independent loads in flight, U = 16, then 8, 4, 1
-        auto batch = [&](auto u_c) {
-            constexpr int U = decltype(u_c)::value;
-            for (; j + (U - 1) * P < chunk; j += U * P) {
-                float v[U];
-#pragma unroll
-                for (int u = 0; u < U; u++)
-                    v[u] = pc[(int64_t)(j + u * P) * stride];
-#pragma unroll
-                for (int u = 0; u < U; u++)
-                    acc += v[u] * wts[j + u * P];
+            for (int ct = 0; ct < NCT; ct++) {
+                if (w > 0)
+                    o[ct] += accv[4 * ct];
+                if (w < WAVES - 1)
+                    accv[4 * ct] = o[ct];
             }
-        };
-        batch(std::integral_constant<int, 16>());
-        batch(std::integral_constant<int, 8>());
-        batch(std::integral_constant<int, 4>());
-        batch(std::integral_constant<int, 1>());
+        }
+        if (w < WAVES - 1)
+            __syncthreads();
     }
-    const float L = block_reduce(lsum, red, false);
-    if (P > 1) {
-        part[t] = acc;
-        __syncthreads();
-        if (grp == 0)
-            for (int g2 = 1; g2 < P; g2++)
-                acc += part[g2 * D + c];
+
+    float *const out = a.out + ((int64_t)s * a.Hq + (int64_t)h * G) * D;
+    if (kw == 1) {
+        // the pair's only workgroup: normalize and write the output
+        if (wave == WAVES - 1) {
+            const float inv = 1.0f / L;
+#pragma unroll
+            for (int ct = 0; ct < NCT; ct++)
+                o[ct] *= inv;
+            if constexpr (VT == KVQ_TURBO3)
+                rotate_back_tiles<NCT>(o, lane);  // O was accumulated in the rotated basis
+            if (n < G) {
+#pragma unroll
+                for (int ct = 0; ct < NCT; ct++)
+                    *reinterpret_cast<floatx4 *>(out + n * D + 16 * ct + 4 * j) = o[ct];
+            }
+        }
+        return;
     }
-    float r = acc / L;
-    if (a.v_rotated && grp == 0)  // whole waves take this branch
-        r = rotate_back(r, c);
-    if (grp == 0)
-        *dst = r;
+
+    // ---------------- several workgroups: write this one's slot (O, m, l per
+    // head) with device-coherent stores, count in, and let the last one merge
+    const int SL = G * (D + 4);  // floats per slot
+    float *const slots = a.ws;
+    uint32_t *const counter = a.counters + pair;
+    if (wave == WAVES - 1) {
+        if (n < G) {
+            const __amdgpu_buffer_rsrc_t rw_ = make_rsrc(slots + (int64_t)(slot0 + rw * slot_step) * SL, SL * 4);
+            const int off = 4 * (n * (D + 4) + 4 * j);
+#pragma unroll
+            for (int ct = 0; ct < NCT; ct++)
+                __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, o[ct]), rw_, off + 64 * ct, 0,
+                                                       CPOL_SC1);
+            if (j == 0) {
+                __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, M), rw_, off + 4 * D, 0, CPOL_SC1);
+                __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, L), rw_, off + 4 * D + 4, 0,
+                                                      CPOL_SC1);
+            }
+        }
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the slot is written before the count
+        if (lane == 0)
+            mrg_last = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+                       (uint32_t)(kw - 1);
+    }
+    __syncthreads();
+    if (!mrg_last)
+        return;
+
+    // ---------------- the last workgroup of the pair: combine its kw slots
+    // (device-coherent loads; slot order).  Weights w_jg = 2^(m_jg - M_g) and
+    // sums L_g = sum_j l_jg w_jg per head g, then each thread sums O of its
+    // (head, channel) outputs with those weights.
+    const int t = threadIdx.x;
+    const int nw = kw * G;
+    float *const mrg_w = reinterpret_cast<float *>(lds_a);  // the workgroup merge's data is no longer read
+    float *const mrg_l = mrg_w + MERGE_SLOTS;
+    auto slot_ptr = [&](int jj) { return slots + (int64_t)(slot0 + jj * slot_step) * SL; };
+    for (int e = t; e < nw; e += 64 * WAVES) {
+        const int jj = e / G, gg = e - jj * G;
+        const float *p = slot_ptr(jj) + gg * (D + 4) + D;
+        mrg_w[e] = __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        mrg_l[e] = __hip_atomic_load(p + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    __syncthreads();
+    if (t < G) {
+        float Mg = mrg_w[t];
+        for (int jj = 1; jj < kw; jj++)
+            Mg = fmaxf(Mg, mrg_w[jj * G + t]);
+        float Lg = 0.0f;
+        for (int jj = 0; jj < kw; jj++) {
+            const float w = __builtin_amdgcn_exp2f(mrg_w[jj * G + t] - Mg);
+            mrg_w[jj * G + t] = w;
+            Lg += mrg_l[jj * G + t] * w;
+        }
+        mrg_l[t] = Lg;  // slot 0's sums are no longer needed
+    }
+    __syncthreads();
+    // Outputs in quads of channels: thread t sums channels 4q .. 4q+3 of one
+    // head for quads q = t, t + 256, ... (D/4 quads per head), one 16-byte
+    // load per slot, all the slots' loads of a quad issued together.  Eight
+    // consecutive threads hold one 32-channel block (turbo3's rotation back).
+    const int nq = G * D / 4;
+    // a descriptor per slot (the slot bases are wave-uniform; the slots of one
+    // pair may lie further apart than 32-bit buffer offsets reach)
+    auto slot_rsrc = [&](int jj) { return make_rsrc(slots + (int64_t)(slot0 + jj * slot_step) * SL, SL * 4); };
+    for (int qd = t; qd < (nq + 63) / 64 * 64; qd += 64 * WAVES) {  // whole waves (rotation shuffles)
+        const bool live = qd < nq;
+        const int gg = live ? qd / (D / 4) : 0, c = 4 * (qd - gg * (D / 4));
+        const int off = 4 * (gg * (D + 4) + c);
+        floatx4 sum = {0.0f, 0.0f, 0.0f, 0.0f};
+        if (live) {
+            int jj = 0;
+            for (; jj + 16 <= kw; jj += 16) {  // sixteen loads in flight, summed in slot order
+                floatx4 v[16];
+#pragma unroll
+                for (int u = 0; u < 16; u++)
+                    v[u] = __builtin_bit_cast(floatx4, __builtin_amdgcn_raw_buffer_load_b128(slot_rsrc(jj + u), off, 0,
+                                                                                             CPOL_SC1));
+#pragma unroll
+                for (int u = 0; u < 16; u++)
+                    sum += v[u] * mrg_w[(jj + u) * G + gg];
+            }
+            for (; jj < kw; jj++)
+                sum += __builtin_bit_cast(floatx4, __builtin_amdgcn_raw_buffer_load_b128(slot_rsrc(jj), off, 0, CPOL_SC1)) *
+                       mrg_w[jj * G + gg];
+            sum *= 1.0f / mrg_l[gg];
+        }
+        if constexpr (VT == KVQ_TURBO3)
+            sum = rotate_back_quad(sum, c);
+        if (live)
+            *reinterpret_cast<floatx4 *>(out + gg * D + c) = sum;
+    }
+    if (t == 0)  // the next call on this workspace starts from zero again
+        __hip_atomic_store(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 template <int KT, int VT, int D>
 hipError_t launch_dec(const DecodeArgs &a, hipStream_t st)
 {
-    dim3 grid((a.W + WAVES - 1) / WAVES);
-    hipLaunchKernelGGL((decode_kernel<KT, VT, D>), grid, dim3(64 * WAVES), 0, st, a);
+    hipLaunchKernelGGL((decode_kernel<KT, VT, D>), dim3(a.n_wg), dim3(64 * WAVES), 0, st, a);
     return hipGetLastError();
 }
 
@@ -700,26 +704,14 @@ hipError_t launch_dec_d(int kt, int vt, const DecodeArgs &a, hipStream_t st)
 
 }  // namespace
 
-hipError_t launch_decode(int kt, int vt, int D, const DecodeArgs &a, const MergeArgs &m, int n_pairs, hipStream_t st)
+hipError_t launch_decode(int kt, int vt, int D, const DecodeArgs &a, hipStream_t st)
 {
-    hipError_t e;
     switch (D) {
-    case 64: e = launch_dec_d<64>(kt, vt, a, st); break;
-    case 128: e = launch_dec_d<128>(kt, vt, a, st); break;
-    case 256: e = launch_dec_d<256>(kt, vt, a, st); break;
+    case 64: return launch_dec_d<64>(kt, vt, a, st);
+    case 128: return launch_dec_d<128>(kt, vt, a, st);
+    case 256: return launch_dec_d<256>(kt, vt, a, st);
     default: return hipErrorInvalidValue;
     }
-    if (e != hipSuccess)
-        return e;
-    // merge groups: about 16 slots per group for the longest merge
-    int k_max = 1;
-    for (int q = 0; q < n_pairs / m.Hkv; q++)
-        k_max = std::max(k_max, (m.wave_start[q + 1] - m.wave_start[q]) / m.Hkv);
-    int P = 1;
-    while (P * 2 * m.D <= MERGE_MAX_THREADS && P * 16 < k_max)
-        P *= 2;
-    hipLaunchKernelGGL(merge_kernel, dim3(n_pairs * m.G), dim3(P * m.D), 0, st, m);
-    return hipGetLastError();
 }
 
 }  // namespace kvq

@@ -364,6 +364,46 @@ __device__ inline void issue_tile(uint8_t *buf, int tb, int lane, const DmaOffse
     }
 }
 
+// turbo3 values: rotate an output accumulated in the rotated basis back,
+// x = s.(H y)/32 per 32-channel block, for a lane's rows in the matrix-core
+// output layout: o[ct][i] holds channel 16 ct + 4 j + i (j = lane / 16) of
+// the lane's row.  Channel 32 b + e sits at e = 16 (ct - 2 b) + 4 j + i:
+// butterflies of span 1, 2 over i, 4, 8 over the lane groups j (lanes 16
+// and 32 apart), 16 over the parity of ct; then the signs and 1/32.
+template <int NCT>
+__device__ inline void rotate_back_tiles(floatx4 (&o)[NCT], const int lane)
+{
+    const int j = lane >> 4;
+#pragma unroll
+    for (int ct = 0; ct < NCT; ct++) {
+        floatx4 &v = o[ct];
+        const float a0 = v[0] + v[1], a1 = v[0] - v[1], a2 = v[2] + v[3], a3 = v[2] - v[3];
+        v = floatx4{a0 + a2, a1 + a3, a0 - a2, a1 - a3};
+#pragma unroll
+        for (int lm = 16; lm <= 32; lm <<= 1) {
+            const bool upper = (lane & lm) != 0;
+#pragma unroll
+            for (int i = 0; i < 4; i++) {
+                const float other = __shfl_xor(v[i], lm);
+                v[i] = upper ? other - v[i] : v[i] + other;
+            }
+        }
+    }
+#pragma unroll
+    for (int b = 0; b < NCT / 2; b++) {
+        const floatx4 lo = o[2 * b], hi = o[2 * b + 1];
+        o[2 * b] = lo + hi;
+        o[2 * b + 1] = lo - hi;
+    }
+#pragma unroll
+    for (int ct = 0; ct < NCT; ct++)
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+            const int e = 16 * (ct & 1) + 4 * j + i;
+            o[ct][i] *= ((TQ3_SIGNS >> e) & 1u) ? -0.03125f : 0.03125f;
+        }
+}
+
 __device__ inline float half_at(const uint32_t *w, int idx)
 {
     uint32_t v = w[idx >> 1];

@@ -42,37 +42,35 @@ struct AppendArgs {
     int32_t pos[KVQ_MAX_SEQS];
 };
 
-// Decode work split: every (sequence, kv head) pair of sequence s gets k_s
-// waves; wave r of a pair streams its tiles r, r + k_s, ... and writes one
-// partial into slot (its global wave index).  The pairs are interleaved over
-// the waves: with one k for all sequences (k_uniform) wave r of pair p is
-// wave r*pairs + p; otherwise wave wave_start[s] + r*n_kv_heads + h.
-// wave_start[s] = first wave of sequence s (n_kv_heads * the k of every
-// earlier sequence); wave_start[n_seqs] = W, the number of waves.
+// Decode work split: every (sequence, kv head) pair of sequence s gets k[s]
+// waves in kw_s = ceil(k[s]/4) workgroups of four; wave r = 4*rw + w (of
+// workgroup rw) streams the pair's tiles r, r + k, ...  The pairs are
+// interleaved over the grid: with one kw for all sequences (kw_uniform)
+// workgroup rw of pair p is workgroup rw*pairs + p; otherwise workgroup
+// wg_start[s] + rw*n_kv_heads + h.  wg_start[s] = first workgroup of
+// sequence s (n_kv_heads * the kw of every earlier sequence); wg_start[n_seqs]
+// = n_wg.  A pair's workgroups merge through one slot each in `ws` (at the
+// workgroup's index) and the pair's counter in `counters`.
+constexpr int KVQ_MAX_WG_PER_PAIR = KVQ_MAX_SPLITS / 4;  // k <= KVQ_MAX_SPLITS waves per pair
+
 struct DecodeArgs {
     const uint8_t *kc;
     const uint16_t *ks;
     const uint8_t *vc;
     const uint16_t *vs;
     const uint16_t *q;    // [S][Hq][D]
-    const uint32_t *kqh, *vqh;    // q5_0 high-bit words, else NULL
+    const uint32_t *kqh, *vqh;    // q5_0 high-bit / turbo3 third-bit words, else NULL
     const uint16_t *knew, *vnew;  // NULL, or the new row of every sequence, binary16 [S][Hkv][D],
                                   // to quantize into position ctx_len[s] - 1 first
-    float *ws;            // partial slots [W][G][D+4]: O (unnormalized), m (base 2), l
-    int32_t Hq, Hkv, G, Tc, n_seqs, W;
-    int32_t k_uniform;  // waves per pair when every sequence has the same count, else 0
+    float *out;           // [S][Hq][D]
+    float *ws;            // slots [n_wg][G][D+4]: O (unnormalized), m (base 2), l
+    uint32_t *counters;   // one per (sequence, kv head) pair, zero between calls
+    int32_t Hq, Hkv, G, Tc, n_seqs, n_wg;
+    int32_t kw_uniform;  // workgroups per pair when every sequence has the same count, else 0
     float c2;  // scale * log2(e)
     int32_t ctx_len[KVQ_MAX_SEQS];
-    int32_t wave_start[KVQ_MAX_SEQS + 1];
-};
-
-struct MergeArgs {
-    const float *ws;
-    float *out;  // [S][Hq][D]
-    int32_t Hq, Hkv, G, D, n_seqs;
-    int32_t k_uniform;  // as in DecodeArgs (selects the slot interleave)
-    int32_t v_rotated;  // turbo3 values: rotate every 32-channel block of the output back
-    int32_t wave_start[KVQ_MAX_SEQS + 1];
+    int32_t wg_start[KVQ_MAX_SEQS + 1];
+    int16_t k[KVQ_MAX_SEQS];  // waves per pair of each sequence
 };
 
 struct PrefillArgs {
@@ -91,9 +89,8 @@ struct PrefillArgs {
 
 // Launchers return hipSuccess or the launch error.
 hipError_t launch_append(int k_type, int v_type, const AppendArgs &a, int n_quads, hipStream_t st);
-// The streaming kernel, then the merge kernel (one workgroup per pair).
-hipError_t launch_decode(int k_type, int v_type, int D, const DecodeArgs &a, const MergeArgs &m, int n_pairs,
-                         hipStream_t st);
+// One launch: streaming, then the in-kernel merge.
+hipError_t launch_decode(int k_type, int v_type, int D, const DecodeArgs &a, hipStream_t st);
 hipError_t launch_prefill(int k_type, int v_type, int D, const PrefillArgs &a, hipStream_t st);
 
 }  // namespace kvq

@@ -536,41 +536,11 @@ __global__ __launch_bounds__(64 * PW) __attribute__((amdgpu_waves_per_eu(D <= 12
     compute(Tr(), ntile - 1, (ntile & 1) ? dq0 : dq1);
 
     // ---- turbo3 values: O was accumulated in the rotated basis; rotate each
-    // 32-channel block back, x = s.(H y)/32.  Channel 32b + e of this lane's
-    // row sits at e = 16(ct - 2b) + 4j + i: butterflies of span 1, 2 over i,
-    // 4, 8 over the lane groups j (lanes 16 and 32 apart), 16 over ct.
+    // 32-channel block of every row back
     if constexpr (VT == KVQ_TURBO3) {
 #pragma unroll
-        for (int rb = 0; rb < RB; rb++) {
-#pragma unroll
-            for (int ct = 0; ct < NCT; ct++) {
-                floatx4 &v = o[rb][ct];
-                const float a0 = v[0] + v[1], a1 = v[0] - v[1], a2 = v[2] + v[3], a3 = v[2] - v[3];
-                v = floatx4{a0 + a2, a1 + a3, a0 - a2, a1 - a3};
-#pragma unroll
-                for (int lm = 16; lm <= 32; lm <<= 1) {
-                    const bool upper = (lane & lm) != 0;
-#pragma unroll
-                    for (int i = 0; i < 4; i++) {
-                        const float other = __shfl_xor(v[i], lm);
-                        v[i] = upper ? other - v[i] : v[i] + other;
-                    }
-                }
-            }
-#pragma unroll
-            for (int b = 0; b < NB; b++) {
-                const floatx4 lo = o[rb][2 * b], hi = o[rb][2 * b + 1];
-                o[rb][2 * b] = lo + hi;
-                o[rb][2 * b + 1] = lo - hi;
-            }
-#pragma unroll
-            for (int ct = 0; ct < NCT; ct++)
-#pragma unroll
-                for (int i = 0; i < 4; i++) {
-                    const int e = 16 * (ct & 1) + 4 * j + i;
-                    o[rb][ct][i] *= ((TQ3_SIGNS >> e) & 1u) ? -0.03125f : 0.03125f;
-                }
-        }
+        for (int rb = 0; rb < RB; rb++)
+            rotate_back_tiles<NCT>(o[rb], lane);
     }
 
     // ---- normalize and write this lane's rows: channels 16ct + 4j + i

@@ -159,9 +159,10 @@ def test_decode_rejections(L):
     sh = shape()
     c = make_cache(sh)
     need = kvq.kvq_decode_workspace_bytes(sh)
-    # 2 seqs x 2 kv heads, 128 tokens of capacity: at most 16 one-tile
-    # waves, one partial slot each of 4 heads x (64 + 4) floats
-    assert need == 16 * 4 * 68 * 4
+    # 2 seqs x 2 kv heads, 128 tokens of capacity (4 tiles): one counter per
+    # pair (padded to 256 B), and at most one workgroup per pair (4 waves of
+    # one tile), one slot each of 4 heads x (64 + 4) floats
+    assert need == 256 + 4 * 4 * 68 * 4
 
     def call(ctx=(100, 50), ws=FAKE, wsb=need, ns=0, scale=0.125, Q=FAKE, out=FAKE, layer=0):
         return kvq.kvq_attn_decode(c, layer, Q, list(ctx), scale, out, ws, wsb, ns, None)
@@ -215,10 +216,10 @@ def test_decode_append_noalloc_rejections(L):
     assert call(Q=None) == kvq.KVQ_E_ARG
     assert call(out=FAKE + 4) == kvq.KVQ_E_ARG
     assert call(layer=2) == kvq.KVQ_E_RANGE
-    # 4 sequences x 4 kv heads x 256 splits = 4096 waves, each 16 heads x 260
-    # floats: 68 MB of partials, more than KVQ_NOALLOC_SCRATCH_BYTES
+    # 4 sequences x 4 kv heads x 256 splits = 1024 workgroups of four waves,
+    # one slot of 16 heads x 260 floats each: 17 MB, more than the scratch
     big = make_cache(shape(n_layers=1, n_seqs=4, n_q_heads=64, n_kv_heads=4, head_dim=256, max_ctx=8192))
-    assert 4096 * 16 * 260 * 4 > kvq.KVQ_NOALLOC_SCRATCH_BYTES
+    assert 1024 * 16 * 260 * 4 > kvq.KVQ_NOALLOC_SCRATCH_BYTES
     assert call(c=big, ctx=(8192,) * 4, ns=256, layer=0) == kvq.KVQ_E_TOO_BIG
     assert "static scratch" in kvq.kvq_strerror(kvq.KVQ_E_TOO_BIG)
 

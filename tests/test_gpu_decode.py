@@ -70,18 +70,18 @@ def test_decode_many_splits_short_context():
 
 
 @pytest.mark.parametrize("kt,vt,D,T,splits", [
-    # head_dim 128: 256 slots per pair, more than 16 per merge group (8 groups)
-    ("q8_0", "q4_0", 128, 9000, [256, 200]),
-    ("q8_0", "turbo3", 128, 9000, [256]),
-    # head_dim 256: 4 merge groups, 65..128 slots per pair
+    # head_dim 128: up to 256 waves = 64 workgroups (slots) per pair
+    ("q8_0", "q4_0", 128, 9000, [256, 200, 5, 4]),
+    ("q8_0", "turbo3", 128, 9000, [256, 6]),
+    # head_dim 256: 17..32 workgroups per pair, and waves without tiles
     ("q8_0", "q4_0", 256, 4096, [65, 100, 128]),
     ("q8_0", "turbo3", 256, 4096, [100]),
 ])
-def test_decode_merge_chunked_path(kt, vt, D, T, splits):
-    """More partial slots per pair than the merge's one-round-trip paths take
-    (16 per group of channels): the chunked merge, with the turbo3 rotation
-    back on the same path."""
-    print(f"decode merge chunked path {kt}/{vt} D={D} splits={splits}", flush=True)
+def test_decode_merge_many_slots(kt, vt, D, T, splits):
+    """Many workgroups per pair: the last one to finish combines up to 64
+    slots (the turbo3 rotation back on the same path); split counts that
+    are not multiples of four leave waves without tiles."""
+    print(f"decode merge, many slots {kt}/{vt} D={D} splits={splits}", flush=True)
     small_case(kt, vt, S=1, Hq=4, Hkv=1, D=D, T=T, ctx=[T - 5], n_splits_list=splits, seed=D + len(splits))
 
 

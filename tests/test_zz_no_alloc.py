@@ -71,7 +71,7 @@ def test_noalloc_rejects_too_many_slots():
 
     import mixed_precision_quantized_quantize_amd as kvq
 
-    # 4 sequences x 4 kv heads x 256 splits = 4096 waves of 16 x 260 floats: 68 MB > 16 MiB
+    # 4 sequences x 4 kv heads x 256 splits = 1024 workgroups, a slot of 16 x 260 floats each: 17 MB > 16 MiB
     S, Hq, Hkv, D, T = 4, 64, 4, 256, 8192
     c = kvq.KVCache(1, S, Hq, Hkv, D, T, ("q4_0", "q4_0"))
     Kn = torch.zeros((S, Hkv, D), dtype=torch.float16, device="cuda")

@@ -704,6 +704,19 @@ def other_configs(dev, args, only=None, pair=None):
     return out
 
 
+def calib_copy(dev):
+    """Three plain 1 GiB device-to-device copies: the reference that scales
+    hardware byte counters (FETCH_SIZE, WRITE_SIZE) to bytes."""
+    import torch
+
+    x = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+    y = torch.empty_like(x)
+    for _ in range(3):
+        y.copy_(x)
+    torch.cuda.synchronize()
+    del x, y
+
+
 def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -724,7 +737,10 @@ def main():
     dev = torch.device("cuda:0")
 
     if args.only == "prefill":
-        print(json.dumps({"prefill": prefill_measure(dev, cpu=not args.no_cpu_baseline)}), flush=True)
+        res = prefill_measure(dev, cpu=not args.no_cpu_baseline)
+        if args.calib_copy:
+            calib_copy(dev)
+        print(json.dumps({"prefill": res}), flush=True)
         return
     if args.only not in (None, "llama3_8b_32k"):
         print(json.dumps({"configs": other_configs(dev, args, only=args.only, pair=args.pair)}), flush=True)
@@ -767,12 +783,7 @@ def main():
         result["stream_read_ceiling"] = stream_ceiling(dev, kv_bytes_per_layer(w, kt, vt), achieved)
         log(f"streaming-read ceiling {result['stream_read_ceiling']['value']:.1f} GB/s")
     if args.calib_copy:
-        x = torch.empty(1 << 28, dtype=torch.float32, device=dev)
-        y = torch.empty_like(x)
-        for _ in range(3):
-            y.copy_(x)
-        torch.cuda.synchronize()
-        del x, y
+        calib_copy(dev)
     torch.cuda.empty_cache()
     if not args.no_prefill and args.only is None:
         result["prefill"] = prefill_measure(dev, cpu=not args.no_cpu_baseline)

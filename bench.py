@@ -10,7 +10,7 @@ resident in HBM before any timed region starts.
 The printed JSON line is the Llama-3-8B-shaped decode (32 layers, 32 query /
 8 kv heads, head_dim 128, 32768-token context, batch 16, K q8_0 / V q4_0):
 `value` = algorithmic KV bytes per step / step time (GB/s); `roofline`
-covers one layer's call (streaming kernel + merge kernel) timed with HIP
+covers one layer's call (one decode_kernel launch) timed with HIP
 events on the stream it runs on; `cpu_baseline` times the CPU oracle on a
 bounded sample of the same workload on this host.  The same line carries:
   configs   every other workload, each with its own step time, roofline
@@ -99,26 +99,28 @@ def row_bytes(w, t):
 
 
 DECODE_SOURCES = ("kvq_decode.hip", "kvq_device.h", "kvq_quant.h", "kvq_internal.h")
+PREFILL_SOURCES = ("kvq_prefill.hip", "kvq_device.h", "kvq_internal.h")
 
 
-def decode_sources_hash() -> str:
-    """sha256 over the sources the decode and merge kernels are built from,
-    in a fixed order (the profile summaries record the same hash)."""
+def sources_hash(names) -> str:
+    """sha256 over the kernel sources `names` (in that order); the profile
+    summaries record the same hash."""
     h = hashlib.sha256()
-    for name in DECODE_SOURCES:
+    for name in names:
         h.update(open(os.path.join(ROOT, "mixed_precision_quantized_quantize_amd", "csrc", name), "rb").read())
     return h.hexdigest()
 
 
 def profile_name(workload, kt, vt, first_pair):
-    return f"decode_merge_kernels_{workload}" + ("" if first_pair else f"_{kt}_{vt}") + ".txt"
+    return f"decode_kernel_{workload}" + ("" if first_pair else f"_{kt}_{vt}") + ".txt"
 
 
-def traffic_from_profile(src_hash, name):
-    """Measured HBM bytes per decode call (both kernels) from a committed
-    counter summary (FETCH_SIZE and WRITE_SIZE scaled by a plain copy of known
-    size), or None when there is none or the decode source changed since the
-    counters were taken."""
+def traffic_from_profile(kernel, name):
+    """Measured HBM bytes per launch of `kernel` ("decode_kernel" or
+    "prefill_kernel") from a committed counter summary (FETCH_SIZE and
+    WRITE_SIZE scaled by a plain copy of known size), or None when there is
+    none or the kernel's sources changed since the counters were taken."""
+    srcs = {"decode_kernel": DECODE_SOURCES, "prefill_kernel": PREFILL_SOURCES}[kernel]
     rec = {}
     try:
         for line in open(os.path.join(ROOT, "profiles", name)):
@@ -127,7 +129,7 @@ def traffic_from_profile(src_hash, name):
                 rec[k.strip()] = v.split("#")[0].strip()
     except OSError:
         return None
-    if rec.get("decode_kernel_sources_sha256") != src_hash or "hbm_bytes_per_launch" not in rec:
+    if rec.get(f"{kernel}_sources_sha256") != sources_hash(srcs) or "hbm_bytes_per_launch" not in rec:
         return None
     return int(rec["hbm_bytes_per_launch"])
 
@@ -415,13 +417,14 @@ def decode_workload(w, kt, vt, dev, args, first_pair=True, flush_mall=False, ora
         "kv_bytes_per_step": kv_step,
         "roofline": {
             "bound": "hbm",
-            "kernel": ("kvq_attn_decode call (decode_kernel streaming the tiles + merge_kernel), one layer"
+            "kernel": ("kvq_attn_decode call (decode_kernel: streaming the tiles and the split merge), one layer"
                        if args.unfused else
-                       "kvq_attn_decode_append call (decode_kernel: row append + streaming the tiles; "
-                       "merge_kernel), one layer"),
+                       "kvq_attn_decode_append call (decode_kernel: row append, streaming the tiles and the "
+                       "split merge), one layer"),
             "achieved": round(achieved, 2), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBPS, 4),
-            "traffic": traffic_from_profile(decode_sources_hash(), profile_name(w.name, kt, vt, first_pair)),
+            "traffic": (None if args.unfused else
+                        traffic_from_profile("decode_kernel", profile_name(w.name, kt, vt, first_pair))),
             "alg_bytes_per_launch": alg_launch,
             "avg_launch_ms": round(call_main, 5),
             "avg_launch_timing": ("median flushed step / layers: each step timed alone after a 1 GiB write"
@@ -533,7 +536,7 @@ def single_layer_2k(dev, args):
                    "GB_per_s": round((src + kv) / (app_ms * 1e-3) / 1e9, 1),
                    "note": f"binary16 rows read ({src} B) + codes and scales written ({kv} B), flushed steps"},
         "roofline": {
-            "bound": "hbm", "kernel": "kvq_attn_decode call (decode_kernel + merge_kernel), one layer; latency-bound "
+            "bound": "hbm", "kernel": "kvq_attn_decode call (one decode_kernel launch), one layer; latency-bound "
                                       "at this size (one small wave of work per launch)",
             "achieved": round((kv + qo) / (dec_ms * 1e-3) / 1e9, 2), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
             "frac": round((kv + qo) / (dec_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4), "traffic": None,
@@ -584,9 +587,10 @@ def tinyllama_bytes_check(w, pairs):
 
 # ---------------------------------------------------------------- prefill
 
-def prefill_measure(dev, calls=5, cpu=False):
+def prefill_measure(dev, calls=5, cpu=False, pair=None):
     """Causal chunked prefill on one layer of the long-context workload: the
-    last 512-query chunk of each of 4 sequences over 131072 K4V4 positions.
+    last 512-query chunk of each of 4 sequences over 131072 K4V4 positions
+    (or the K/V type pair `pair`).
     Algorithmic flop = 4 * head_dim * n_q_heads * (visible keys summed over
     the chunk's queries) per sequence (Q.K and P.V, multiply-add = 2)."""
     import torch
@@ -595,7 +599,7 @@ def prefill_measure(dev, calls=5, cpu=False):
     from mixed_precision_quantized_quantize_amd import synth
 
     w = synth.WORKLOADS["llama3_8b_128k_prefill"]
-    kt, vt = w.type_pairs[0]
+    kt, vt = pair or w.type_pairs[0]
     n_tok, T, S = w.prefill, w.ctx, w.batch
     log(f"prefill {w.name} {kt}/{vt}: {S} x {n_tok} queries at the end of {T} tokens")
     cache = kvq.KVCache(1, S, w.n_q_heads, w.n_kv_heads, w.head_dim, T, (kt, vt), device=dev)
@@ -627,15 +631,19 @@ def prefill_measure(dev, calls=5, cpu=False):
         "workload": w.name, "layer": 0, "batch": S, "n_tok": n_tok, "q_pos0": T - n_tok, "ctx": T,
         "k_type": kt, "v_type": vt, "ms_per_call": round(ms, 4), "alg_flop_per_call": flop,
         "roofline": {"bound": "mfma", "kernel": "prefill_kernel, one layer", "achieved": round(tflops, 1),
-                     "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(tflops / MFMA_F16_PEAK_TFLOPS, 4)},
+                     "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(tflops / MFMA_F16_PEAK_TFLOPS, 4),
+                     "traffic": (traffic_from_profile("prefill_kernel", f"prefill_kernel_{w.name}.txt")
+                                 if (kt, vt) == w.type_pairs[0] else None),
+                     "traffic_unit": "bytes per launch (HBM, counters)",
+                     "avg_launch_ms": round(ms, 5)},
         "cpu_baseline": None,
     }
     if cpu:
-        res["cpu_baseline"] = prefill_cpu_baseline(w, Q)
+        res["cpu_baseline"] = prefill_cpu_baseline(w, Q, (kt, vt))
     return res
 
 
-def prefill_cpu_baseline(w, Q, n_q=64):
+def prefill_cpu_baseline(w, Q, pair, n_q=64):
     """The oracle's causal prefill on a bounded sample of the same call:
     sequence 0, the first and the last n_q queries of the chunk, all heads."""
     import numpy as np
@@ -643,7 +651,7 @@ def prefill_cpu_baseline(w, Q, n_q=64):
     import oracle
     from mixed_precision_quantized_quantize_amd import synth
 
-    kt, vt = w.type_pairs[0]
+    kt, vt = pair
     n_tok, T = w.prefill, w.ctx
     orc = oracle.OracleLayer(kt, vt, 1, w.n_q_heads, w.n_kv_heads, w.head_dim, T)
     for c0 in range(0, T, synth.CHUNK):
@@ -737,13 +745,17 @@ def main():
     dev = torch.device("cuda:0")
 
     if args.only == "prefill":
-        res = prefill_measure(dev, cpu=not args.no_cpu_baseline)
+        res = prefill_measure(dev, cpu=not args.no_cpu_baseline,
+                              pair=tuple(args.pair.split("/")) if args.pair else None)
         if args.calib_copy:
             calib_copy(dev)
         print(json.dumps({"prefill": res}), flush=True)
         return
     if args.only not in (None, "llama3_8b_32k"):
-        print(json.dumps({"configs": other_configs(dev, args, only=args.only, pair=args.pair)}), flush=True)
+        res = other_configs(dev, args, only=args.only, pair=args.pair)
+        if args.calib_copy:
+            calib_copy(dev)
+        print(json.dumps({"configs": res}), flush=True)
         return
 
     w = synth.WORKLOADS["llama3_8b_32k"]

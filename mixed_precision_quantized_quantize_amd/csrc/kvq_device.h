@@ -133,38 +133,55 @@ __device__ inline void v_operand_q5(u32x2 w, const uint32_t (&h)[8], int n, half
 // the even entry in the low half.
 constexpr uint32_t TQ3_L01 = 0xBD60C04Eu, TQ3_L23 = 0xB3D8BA0Cu, TQ3_L45 = 0x3A0C33D8u, TQ3_L67 = 0x404E3D60u;
 
-// Two levels as one binary16 pair: z holds 2-bit codes in its bytes, pick is
-// the perm selector that repeats the pair's two bytes as [a, a, b, b], and
-// bit 0 of t0 / t1 is the third bit of the first / second code.
-__device__ inline uint32_t tq3_pair(uint32_t z, uint32_t pick, uint32_t t0, uint32_t t1)
+// The same table split by byte: byte e of TQ3_LO03/TQ3_LO47 is the low byte
+// of entry e / e+4, and likewise TQ3_HI* for the high bytes -- so that one
+// byte permute looks up four entries at once.
+constexpr uint32_t tq3_bytes(uint32_t a, uint32_t b, int sh)
 {
-    // byte selector of entry e: bytes 2e, 2e+1 of the 8-byte table half
-    const uint32_t sel = (__builtin_amdgcn_perm(z, z, pick) << 1) + 0x01000100u;
-    const uint32_t lo = __builtin_amdgcn_perm(TQ3_L23, TQ3_L01, sel);  // entries 0..3
-    const uint32_t hi = __builtin_amdgcn_perm(TQ3_L67, TQ3_L45, sel);  // entries 4..7
-    const uint32_t mask = ((t0 & 1u) ? 0x0000FFFFu : 0u) | ((t1 & 1u) ? 0xFFFF0000u : 0u);
-    return bfi(mask, hi, lo);
+    return ((a >> sh) & 0xFFu) | ((a >> (16 + sh)) & 0xFFu) << 8 | ((b >> sh) & 0xFFu) << 16 |
+           ((b >> (16 + sh)) & 0xFFu) << 24;
+}
+constexpr uint32_t TQ3_LO03 = tq3_bytes(TQ3_L01, TQ3_L23, 0), TQ3_LO47 = tq3_bytes(TQ3_L45, TQ3_L67, 0);
+constexpr uint32_t TQ3_HI03 = tq3_bytes(TQ3_L01, TQ3_L23, 8), TQ3_HI47 = tq3_bytes(TQ3_L45, TQ3_L67, 8);
+static_assert(TQ3_LO03 == 0xD80C604Eu && TQ3_HI47 == 0x403D3A33u, "byte tables of the codebook");
+
+// Four levels at once: byte i of c is the 3-bit code of value i; the result
+// is values 0, 1 (lo01) and 2, 3 (lo23) as binary16 pairs, value 0 / 2 in the
+// low half.
+__device__ inline void tq3_quad(uint32_t c, uint32_t &p01, uint32_t &p23)
+{
+    const uint32_t lo = __builtin_amdgcn_perm(TQ3_LO47, TQ3_LO03, c);  // low bytes of the four levels
+    const uint32_t hi = __builtin_amdgcn_perm(TQ3_HI47, TQ3_HI03, c);  // their high bytes
+    p01 = __builtin_amdgcn_perm(hi, lo, 0x05010400u);
+    p23 = __builtin_amdgcn_perm(hi, lo, 0x07030602u);
 }
 
 // turbo3 V operand of one block: the lane's code byte n&7 for tokens 0..7
 // in w (2-bit codes of elements n&7, +8, +16, +24 at bits 0, 2, 4, 6; tokens
 // 0..3 in w.x, 4..7 in w.y) and the tokens' third-bit words h[0..7] -> the
 // two operands (channel tiles of elements n and n+16) as binary16 levels.
+// Per four tokens, byte permutes gather the byte of each word that holds
+// element n's third bit (byte n/8) and the one with element n+16's (byte
+// 2 + n/8) into one word each; a rotation moves bit n%8 of every byte to bit
+// 2, beside the 2-bit codes, and the resulting 3-bit codes select the
+// levels' bytes.
 __device__ inline void v_operand_tq3(u32x2 w, const uint32_t (&h)[8], int n, half8 &va0, half8 &va1)
 {
-    const int sh0 = 2 * (n >> 3), sh1 = sh0 + 4;  // bit offsets of elements n and n+16
-    const uint32_t z0[2] = {(w.x >> sh0) & 0x03030303u, (w.y >> sh0) & 0x03030303u};
-    const uint32_t z1[2] = {(w.x >> sh1) & 0x03030303u, (w.y >> sh1) & 0x03030303u};
-    uint32_t s[8];
-#pragma unroll
-    for (int i = 0; i < 8; i++)
-        s[i] = h[i] >> n;  // bit 0: element n's third bit, bit 16: element n+16's
+    const int sh0 = 2 * (n >> 3), sh1 = sh0 + 4;                  // bit offsets of elements n and n+16
+    const uint32_t gsel = (n & 8) ? 0x07030501u : 0x06020400u;      // [a.bn, b.bn, a.b(2+n), b.b(2+n)]
+    const uint32_t rot = (uint32_t)((n & 7) - 2) & 31u;             // rotate right: bit n%8 -> bit 2
     uint32_t r0[4], r1[4];
 #pragma unroll
-    for (int p = 0; p < 4; p++) {
-        const uint32_t pick = (p & 1) ? 0x03030202u : 0x01010000u;
-        r0[p] = tq3_pair(z0[p >> 1], pick, s[2 * p], s[2 * p + 1]);
-        r1[p] = tq3_pair(z1[p >> 1], pick, s[2 * p] >> 16, s[2 * p + 1] >> 16);
+    for (int q = 0; q < 2; q++) {  // tokens 4q .. 4q+3
+        const uint32_t wq = q ? w.y : w.x;
+        const uint32_t p01 = __builtin_amdgcn_perm(h[4 * q + 1], h[4 * q], gsel);
+        const uint32_t p23 = __builtin_amdgcn_perm(h[4 * q + 3], h[4 * q + 2], gsel);
+        const uint32_t t0 = __builtin_amdgcn_perm(p23, p01, 0x05040100u);  // byte i: token 4q+i, element n
+        const uint32_t t1 = __builtin_amdgcn_perm(p23, p01, 0x07060302u);  // element n+16
+        const uint32_t c0 = bfi(0x04040404u, __builtin_amdgcn_alignbit(t0, t0, rot), (wq >> sh0) & 0x03030303u);
+        const uint32_t c1 = bfi(0x04040404u, __builtin_amdgcn_alignbit(t1, t1, rot), (wq >> sh1) & 0x03030303u);
+        tq3_quad(c0, r0[2 * q], r0[2 * q + 1]);
+        tq3_quad(c1, r1[2 * q], r1[2 * q + 1]);
     }
     va0 = pack4(r0[0], r0[1], r0[2], r0[3]);
     va1 = pack4(r1[0], r1[1], r1[2], r1[3]);

@@ -358,7 +358,7 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(D <=
                     const uint32_t w = op.k[T][b].x;
                     ka = k_operand<KVQ_Q4_0>(&w);
                 } else {
-                    ka = k_operand_q5(op.k[T][b].x, op.kh[T][b] >> (4 * j));
+                    ka = k_operand_q5(op.k[T][b].x, op.kh[T][b], 4 * j);
                 }
                 if (KT == KVQ_F16) {
                     sacc[T] = mfma(ka, qb[b], sacc[T]);

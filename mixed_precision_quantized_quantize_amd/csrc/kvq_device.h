@@ -68,61 +68,64 @@ __device__ inline void deq_q4_pair(uint32_t y, uint32_t &lo, uint32_t &hi)
     hi = h2_bits(__builtin_elementwise_fma(bits_h2(bfi(0x00F000F0u, y, e)), k16, k72));
 }
 
-// q5_0 codes (c = nibble + 16 * fifth bit) -> binary16 (c - 16), exact, as
-// deq_q4_pair does with nibbles: the five bits of a low-nibble element are
-// inserted under 0x6400 (binary16 1024 + c, minus 1040); those of a
-// high-nibble element one nibble up (1024 + 16 c, times 1/16, minus 80).
-
-// q5_0 K codes of one block for one lane: w as for q4_0, x = the block's
-// high-bit word shifted right by 4j (bits 0..3: elements 4j..4j+3; bits
-// 16..19: elements 16+4j..16+4j+3).  The two fifth bits of an element pair
-// are spread into place by one 24-bit multiply: bits 0, 1 times 0x80010
-// land at 4 and 20 (and at 19 and 5, which the insert masks drop), times
-// 0x800100 at 8 and 24 (and 23, 9).
-__device__ inline half8 k_operand_q5(uint32_t w, uint32_t x)
+// q5_0 codes (c = nibble + 16 * fifth bit) -> binary16 (c - 16), exact: the
+// nibble goes to bits 4..7 and the fifth bit to bit 8 of a binary16 half
+// under the exponent pattern 0x6400 (binary16 1024 + 16 c), then times 1/16
+// minus 80.  q5_pair builds two such values from the bytes of two words: nib
+// holds the nibbles at bits 4..7 of its bytes, fifth the fifth bits at bit
+// 0 of its bytes (the other bits of both are ignored); sel picks bytes
+// (0, 1) or (2, 3) of each.
+__device__ inline uint32_t q5_pair(uint32_t fifth, uint32_t nib, uint32_t sel)
 {
-    const uint32_t e = 0x64006400u;
-    const half2 k1040 = {(_Float16)1040.0f, (_Float16)1040.0f};
     const half2 k16 = {(_Float16)0.0625f, (_Float16)0.0625f};
     const half2 k80 = {(_Float16)-80.0f, (_Float16)-80.0f};
-    uint32_t lo[2], hi[2];
-#pragma unroll
-    for (int q = 0; q < 2; q++) {
-        const uint32_t y = __builtin_amdgcn_perm(w, w, q ? 0x0C030C02u : 0x0C010C00u);
-        const uint32_t ml = ((x >> (2 * q)) & 3u) * 0x00080010u;
-        const uint32_t mh = ((x >> (16 + 2 * q)) & 3u) * 0x00800100u;
-        lo[q] = h2_bits(bits_h2(bfi(0x001F001Fu, bfi(0x00100010u, ml, y), e)) - k1040);
-        hi[q] = h2_bits(__builtin_elementwise_fma(bits_h2(bfi(0x01F001F0u, bfi(0x01000100u, mh, y), e)), k16, k80));
-    }
-    return pack4(lo[0], lo[1], hi[0], hi[1]);
+    const uint32_t y = __builtin_amdgcn_perm(fifth, nib, sel);  // half k: nib byte, fifth byte
+    return h2_bits(__builtin_elementwise_fma(bits_h2(bfi(0x01F001F0u, y, 0x64006400u)), k16, k80));
+}
+constexpr uint32_t Q5_SEL01 = 0x05010400u, Q5_SEL23 = 0x07030602u;
+
+// Bit k of a 4-bit value -> bit 0 of byte k (the partial products of the
+// 24-bit multiply occupy disjoint bit ranges, so nothing carries).
+__device__ inline uint32_t spread4(uint32_t v4) { return __umul24(v4, 0x00204081u); }
+
+// q5_0 K codes of one block for one lane: w = code bytes 4j..4j+3 of the
+// token's row (elements 4j+k low, 16+4j+k high), x = the block's high-bit
+// word, sh = 4j (bits sh..sh+3: fifth bits of elements 4j..4j+3, bits
+// 16+sh..: of elements 16+4j..).
+__device__ inline half8 k_operand_q5(uint32_t w, uint32_t x, int sh)
+{
+    const uint32_t fl = spread4(__builtin_amdgcn_ubfe(x, sh, 4));
+    const uint32_t fh = spread4(__builtin_amdgcn_ubfe(x, 16 + sh, 4));
+    const uint32_t wl = w << 4;  // low nibbles to bits 4..7
+    return pack4(q5_pair(fl, wl, Q5_SEL01), q5_pair(fl, wl, Q5_SEL23), q5_pair(fh, w, Q5_SEL01),
+                 q5_pair(fh, w, Q5_SEL23));
 }
 
 // q5_0 V operand of one block: the lane's code byte n (element n low, n+16
 // high) for tokens 0..7 in w (bytes of tokens 0..3 in w.x, 4..7 in w.y) and
 // those tokens' high-bit words h[0..7] -> the two operands (channel tiles
-// of elements n and n+16), binary16 (code - 16).  Per token pair (a, b) the
-// fifth bits are moved into place with rotations (v_alignbit): a's word
-// rotated right by n-4 has element n's bit at 4 and element n+16's at 20,
-// b's rotated by n+12 has them at 20 and 4; bit-field inserts then put them
-// beside the nibbles.
+// of elements n and n+16), binary16 (code - 16).  Per four tokens, byte
+// permutes gather the byte of each word that holds element n's fifth bit
+// (byte n/8) and the one with element n+16's (byte 2 + n/8); a rotation
+// moves bit n%8 of every byte to bit 0.
 __device__ inline void v_operand_q5(u32x2 w, const uint32_t (&h)[8], int n, half8 &va0, half8 &va1)
 {
-    const uint32_t e = 0x64006400u;
-    const half2 k1040 = {(_Float16)1040.0f, (_Float16)1040.0f};
-    const half2 k16 = {(_Float16)0.0625f, (_Float16)0.0625f};
-    const half2 k80 = {(_Float16)-80.0f, (_Float16)-80.0f};
+    const uint32_t gsel = (n & 8) ? 0x07030501u : 0x06020400u;  // [a.bn, b.bn, a.b(2+n), b.b(2+n)]
+    const uint32_t rot = (uint32_t)(n & 7);
     uint32_t lo[4], hi[4];
 #pragma unroll
-    for (int p = 0; p < 4; p++) {
-        const uint32_t word = (p < 2) ? w.x : w.y;
-        const uint32_t y = __builtin_amdgcn_perm(word, word, (p & 1) ? 0x0C030C02u : 0x0C010C00u);
-        const uint32_t ra = __builtin_amdgcn_alignbit(h[2 * p], h[2 * p], (uint32_t)(n - 4));
-        const uint32_t rb = __builtin_amdgcn_alignbit(h[2 * p + 1], h[2 * p + 1], (uint32_t)(n + 12));
-        const uint32_t f_lo = bfi(0x00100000u, rb, ra);  // bit 4: a's element n, bit 20: b's
-        const uint32_t g = bfi(0x00000010u, rb, ra);     // bit 4: b's element n+16, bit 20: a's
-        const uint32_t f_hi = __builtin_amdgcn_alignbit(g, g, 12u);  // -> bits 24 and 8
-        lo[p] = h2_bits(bits_h2(bfi(0x001F001Fu, bfi(0x00100010u, f_lo, y), e)) - k1040);
-        hi[p] = h2_bits(__builtin_elementwise_fma(bits_h2(bfi(0x01F001F0u, bfi(0x01000100u, f_hi, y), e)), k16, k80));
+    for (int q = 0; q < 2; q++) {  // tokens 4q .. 4q+3
+        const uint32_t wq = q ? w.y : w.x;
+        const uint32_t p01 = __builtin_amdgcn_perm(h[4 * q + 1], h[4 * q], gsel);
+        const uint32_t p23 = __builtin_amdgcn_perm(h[4 * q + 3], h[4 * q + 2], gsel);
+        const uint32_t t0 = __builtin_amdgcn_perm(p23, p01, 0x05040100u);  // byte i: token 4q+i, element n
+        const uint32_t t1 = __builtin_amdgcn_perm(p23, p01, 0x07060302u);  // element n+16
+        const uint32_t f0 = __builtin_amdgcn_alignbit(t0, t0, rot), f1 = __builtin_amdgcn_alignbit(t1, t1, rot);
+        const uint32_t wl = wq << 4;
+        lo[2 * q] = q5_pair(f0, wl, Q5_SEL01);
+        lo[2 * q + 1] = q5_pair(f0, wl, Q5_SEL23);
+        hi[2 * q] = q5_pair(f1, wq, Q5_SEL01);
+        hi[2 * q + 1] = q5_pair(f1, wq, Q5_SEL23);
     }
     va0 = pack4(lo[0], lo[1], lo[2], lo[3]);
     va1 = pack4(hi[0], hi[1], hi[2], hi[3]);

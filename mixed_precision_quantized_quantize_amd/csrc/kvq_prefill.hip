@@ -235,7 +235,7 @@ __global__ __launch_bounds__(64 * PW) __attribute__((amdgpu_waves_per_eu(D <= 12
                 } else {
                     const uint32_t w = *reinterpret_cast<const uint32_t *>(buf + krd);
                     const uint32_t hw = *reinterpret_cast<const uint32_t *>(buf + g::KH_OFF + (r * NB + b) * 4);
-                    ka = k_operand_q5(w, hw >> (4 * j));
+                    ka = k_operand_q5(w, hw, 4 * j);
                 }
                 const uint16_t dbits = *reinterpret_cast<const uint16_t *>(buf + g::KS_OFF + (r * NB + b) * 2);
                 const half8 dd = splat8(dbits * 0x00010001u);

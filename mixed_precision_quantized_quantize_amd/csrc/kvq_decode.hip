@@ -261,7 +261,6 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(D <=
         v_rd[i] = g::V_OFF + (j * g::CPG + (c ^ vswz<VT, g::CPG>(j))) * 16 + within;
     }
 
-    const int bp16 = (lane ^ 16) << 2, bp32 = (lane ^ 32) << 2;  // ds_bpermute byte addresses
     float m_run;    // running max (base 2) of head n, equal in the 4 lane groups
     float l_run;    // this lane's share of the running sum
     floatx4 o[NCT];
@@ -399,11 +398,9 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(D <=
                     op.vs[b] = u32x4{op.vs[b].x & keep[0], op.vs[b].y & keep[1], op.vs[b].z & keep[2], op.vs[b].w & keep[3]};
             }
         }
-        float mt = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])), fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
-        mt = fmaxf(mt, __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(bp16, __builtin_bit_cast(int, mt))));
-        mt = fmaxf(mt, __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(bp32, __builtin_bit_cast(int, mt))));
+        const float mt = max_lane_groups(max3(max3(x[0], x[1], x[2]), max3(x[3], x[4], x[5]), max3(x[6], x[7], x[7])));
         if (__any(mt > m_run)) {
-            const float m_new = fmaxf(m_run, mt);
+            const float m_new = __builtin_elementwise_maximum(m_run, mt);
             const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);  // 0 on the first tile
             l_run *= alpha;
 #pragma unroll

@@ -68,6 +68,26 @@ __device__ inline void deq_q4_pair(uint32_t y, uint32_t &lo, uint32_t &hi)
     hi = h2_bits(__builtin_elementwise_fma(bits_h2(bfi(0x00F000F0u, y, e)), k16, k72));
 }
 
+// max over the four lanes n, n+16, n+32, n+48 (the lane groups of one score
+// row) with two lane swaps, no LDS round trip.
+__device__ inline float max_lane_groups(float v)
+{
+    const uint32_t u = __builtin_bit_cast(uint32_t, v);
+    const auto a = __builtin_amdgcn_permlane32_swap(u, u, false, false);  // {lanes 0-31 twice}, {32-63 twice}
+    const float m = __builtin_elementwise_maximum(__builtin_bit_cast(float, (uint32_t)a[0]), __builtin_bit_cast(float, (uint32_t)a[1]));
+    const uint32_t w = __builtin_bit_cast(uint32_t, m);
+    const auto b = __builtin_amdgcn_permlane16_swap(w, w, false, false);  // rows {0,0,2,2}, {1,1,3,3}
+    return __builtin_elementwise_maximum(__builtin_bit_cast(float, (uint32_t)b[0]), __builtin_bit_cast(float, (uint32_t)b[1]));
+}
+
+// NaN-propagating maximum (v_maximum3_f32): fmaxf would first canonicalize
+// every MFMA result with an extra v_max_f32.  Scores are finite, or -inf
+// where masked (a masked key's garbage score is replaced before).
+__device__ inline float max3(float a, float b, float c)
+{
+    return __builtin_elementwise_maximum(__builtin_elementwise_maximum(a, b), c);
+}
+
 // q5_0 codes (c = nibble + 16 * fifth bit) -> binary16 (c - 16), exact: the
 // nibble goes to bits 4..7 and the fifth bit to bit 8 of a binary16 half
 // under the exponent pattern 0x6400 (binary16 1024 + 16 c), then times 1/16

@@ -53,25 +53,6 @@ constexpr int PW = 4;  // waves per workgroup
 // the compiler copied them between the two register files on every tile.
 template <int D> struct Rows { static constexpr int RB = 2; };
 
-// max over the four lanes n, n+16, n+32, n+48 (the lane groups of one row)
-__device__ inline float max_lane_groups(float v)
-{
-    const uint32_t u = __builtin_bit_cast(uint32_t, v);
-    const auto a = __builtin_amdgcn_permlane32_swap(u, u, false, false);  // {lanes 0-31 twice}, {32-63 twice}
-    const float m = __builtin_elementwise_maximum(__builtin_bit_cast(float, (uint32_t)a[0]), __builtin_bit_cast(float, (uint32_t)a[1]));
-    const uint32_t w = __builtin_bit_cast(uint32_t, m);
-    const auto b = __builtin_amdgcn_permlane16_swap(w, w, false, false);  // rows {0,0,2,2}, {1,1,3,3}
-    return __builtin_elementwise_maximum(__builtin_bit_cast(float, (uint32_t)b[0]), __builtin_bit_cast(float, (uint32_t)b[1]));
-}
-
-// NaN-propagating maximum (v_maximum3_f32): fmaxf would first canonicalize
-// every MFMA result with an extra v_max_f32.  Scores are finite here, or
-// -inf where masked (a masked key's garbage score is replaced before).
-__device__ inline float max3(float a, float b, float c)
-{
-    return __builtin_elementwise_maximum(__builtin_elementwise_maximum(a, b), c);
-}
-
 __device__ inline half8 splat8(uint32_t pair) { return pack4(pair, pair, pair, pair); }
 
 template <int KT, int VT, int D>

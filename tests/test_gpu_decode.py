@@ -22,7 +22,7 @@ PAIRS = list(itertools.product(["f16", "q8_0", "q4_0", "q5_0"], repeat=2))
 PAIRS += [(k, "turbo3") for k in ["f16", "q8_0", "q4_0", "q5_0"]]  # turbo3 stores values only
 
 
-def small_case(kt, vt, S, Hq, Hkv, D, T, ctx, n_splits_list, seed, kscale=3.0):
+def small_case(kt, vt, S, Hq, Hkv, D, T, ctx, n_splits_list, seed, kscale=3.0, scale=None):
     import torch
 
     import mixed_precision_quantized_quantize_amd as kvq
@@ -36,7 +36,7 @@ def small_case(kt, vt, S, Hq, Hkv, D, T, ctx, n_splits_list, seed, kscale=3.0):
     Q = torch.from_numpy(rng.standard_normal((S, Hq, D)).astype(np.float16)).cuda()
     cache.append(0, K, V, [0] * S)
     orc.append(bits(K), bits(V), np.zeros(S, np.int32))
-    scale = 1.0 / np.sqrt(D)
+    scale = 1.0 / np.sqrt(D) if scale is None else scale
     ref = orc.attn_decode(bits(Q), np.array(ctx, np.int32), scale)
     for ns in n_splits_list:
         out = cache.decode(0, Q, ctx, scale, n_splits=ns)
@@ -50,6 +50,18 @@ def test_decode_pairs(kt, vt, D):
     print(f"decode parity {kt}/{vt} D={D}", flush=True)
     small_case(kt, vt, S=3, Hq=16, Hkv=2, D=D, T=333, ctx=[333, 37, 1], n_splits_list=[0, 1, 3],
                seed=zlib.crc32(f"{kt}{vt}{D}".encode()) % 1000)
+
+
+@pytest.mark.parametrize("kt,vt", [("q8_0", "q4_0"), ("q4_0", "q4_0"), ("q8_0", "turbo3")])
+@pytest.mark.parametrize("scale", [-0.0883883, 0.0, 0.5])
+def test_decode_scale_sign(kt, vt, scale):
+    """The scale is used as passed: negative (the weights favour the
+    smallest scores), zero (uniform weights over the first ctx_len
+    positions; the tail tile's masked positions must still get none) and
+    large; ragged contexts and several split counts."""
+    print(f"decode scale {scale} {kt}/{vt}", flush=True)
+    small_case(kt, vt, S=3, Hq=16, Hkv=2, D=128, T=333, ctx=[333, 70, 5], n_splits_list=[0, 3, 8], seed=41,
+               scale=scale)
 
 
 @pytest.mark.parametrize("kt,vt", [("q8_0", "q4_0"), ("f16", "f16"), ("q4_0", "q8_0"), ("q5_0", "q5_0"), ("q8_0", "q5_0"), ("q8_0", "turbo3")])

@@ -399,6 +399,7 @@ def decode_workload(w, kt, vt, dev, args, first_pair=True, flush_mall=False, ora
     kv_step = kv_layer * L
     ms_main = median(tm["ms_flushed"]) if flush_mall else tm["ms_per_step"]
     call_main = ms_main / L if flush_mall else call_ms
+    traffic = None if args.unfused else traffic_from_profile("decode_kernel", profile_name(w.name, kt, vt, first_pair))
     value = kv_step / (ms_main * 1e-3) / 1e9
     achieved = alg_launch / (call_main * 1e-3) / 1e9
     res = {
@@ -423,8 +424,10 @@ def decode_workload(w, kt, vt, dev, args, first_pair=True, flush_mall=False, ora
                        "split merge), one layer"),
             "achieved": round(achieved, 2), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBPS, 4),
-            "traffic": (None if args.unfused else
-                        traffic_from_profile("decode_kernel", profile_name(w.name, kt, vt, first_pair))),
+            "traffic": traffic,
+            "traffic_GB_per_s": None if traffic is None else round(traffic / (call_main * 1e-3) / 1e9, 2),
+            "traffic_note": "HBM bytes per launch from the committed counter summary (FETCH_SIZE + WRITE_SIZE, "
+                            "copy-calibrated) whose kernel sources match; the rate divides them by avg_launch_ms",
             "alg_bytes_per_launch": alg_launch,
             "avg_launch_ms": round(call_main, 5),
             "avg_launch_timing": ("median flushed step / layers: each step timed alone after a 1 GiB write"
@@ -627,14 +630,16 @@ def prefill_measure(dev, calls=5, cpu=False, pair=None):
     del cache, out
     torch.cuda.empty_cache()
     log(f"  {ms:.3f} ms per call, {tflops:.1f} TFLOP/s ({100 * tflops / MFMA_F16_PEAK_TFLOPS:.1f}% of peak)")
+    traffic = (traffic_from_profile("prefill_kernel", f"prefill_kernel_{w.name}.txt")
+               if (kt, vt) == w.type_pairs[0] else None)
     res = {
         "workload": w.name, "layer": 0, "batch": S, "n_tok": n_tok, "q_pos0": T - n_tok, "ctx": T,
         "k_type": kt, "v_type": vt, "ms_per_call": round(ms, 4), "alg_flop_per_call": flop,
         "roofline": {"bound": "mfma", "kernel": "prefill_kernel, one layer", "achieved": round(tflops, 1),
                      "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(tflops / MFMA_F16_PEAK_TFLOPS, 4),
-                     "traffic": (traffic_from_profile("prefill_kernel", f"prefill_kernel_{w.name}.txt")
-                                 if (kt, vt) == w.type_pairs[0] else None),
+                     "traffic": traffic,
                      "traffic_unit": "bytes per launch (HBM, counters)",
+                     "traffic_GB_per_s": None if traffic is None else round(traffic / (ms * 1e-3) / 1e9, 2),
                      "avg_launch_ms": round(ms, 5)},
         "cpu_baseline": None,
     }

@@ -28,6 +28,9 @@ bounded sample of the same workload on this host.  The same line carries:
   prefill   the causal chunked prefill (512 queries per sequence at the end
             of a 131072-token K4V4 cache, one layer) against the dense
             binary16 matrix-core peak.
+  pairs     one layer of the headline shape for each of the 20 K/V type
+            pairs (all caches resident, rounds interleaved), per-call time
+            and the fraction of 8 TB/s for each pair's own bytes.
 
     python bench.py [--steps K] [--warmup W] [--gpus 1] [--only NAME]
 """
@@ -70,6 +73,7 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-prefill", action="store_true", help="skip the prefill measurement")
     p.add_argument("--no-configs", action="store_true", help="headline workload (and prefill) only")
+    p.add_argument("--no-pairs", action="store_true", help="skip the one-layer sweep over all 20 type pairs")
     p.add_argument("--no-stream-ceiling", action="store_true", help="skip the streaming-read ceiling measurement")
     p.add_argument("--cpu-seconds", type=float, default=10.0, help="oracle time budget of the headline workload")
     p.add_argument("--cpu-seconds-other", type=float, default=3.0, help="oracle time budget of each other workload")
@@ -717,6 +721,66 @@ def other_configs(dev, args, only=None, pair=None):
     return out
 
 
+PAIRS_ALL = [(k, v) for k in ("f16", "q8_0", "q4_0", "q5_0") for v in ("f16", "q8_0", "q4_0", "q5_0", "turbo3")]
+
+
+def pairs_sweep(dev, rounds=5, calls=10):
+    """One layer of the Llama-3-8B-shaped decode step (16 sequences x 32768
+    tokens, 32/8 heads, head_dim 128; kvq_attn_decode_append, automatic
+    split) for each of the 20 K/V type pairs.  Every pair's cache is resident
+    at once, holding the same seeded rows; the rounds are interleaved over
+    the pairs (a cache timed right after it was filled runs slower while the
+    fill's dirty lines leave the last-level cache).  Per pair: the median
+    per-call time and the GB/s of that pair's own algorithmic bytes."""
+    import torch
+
+    import mixed_precision_quantized_quantize_amd as kvq
+    from mixed_precision_quantized_quantize_amd import synth
+
+    w = synth.WORKLOADS["llama3_8b_32k"]
+    S, T = w.batch, w.ctx
+    log(f"pairs: one layer of {w.name}, {len(PAIRS_ALL)} type pairs, interleaved")
+    caches = {p: kvq.KVCache(1, S, w.n_q_heads, w.n_kv_heads, w.head_dim, T, p, device=dev) for p in PAIRS_ALL}
+    for c0 in range(0, T - 1, synth.CHUNK):
+        K, V = synth.kv_batch(w, 0, c0, min(synth.CHUNK, T - 1 - c0), device=dev)
+        for c in caches.values():
+            c.append(0, K, V, [c0] * S)
+        del K, V
+    Kn, Vn = synth.kv_batch(w, 0, T - 1, 1, device=dev, step=0)
+    Kn, Vn = Kn[:, 0].contiguous(), Vn[:, 0].contiguous()
+    Q = synth.queries(w, 0, device=dev)
+    out = torch.empty((S, w.n_q_heads, w.head_dim), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    ctx = [T] * S
+    times = {p: [] for p in PAIRS_ALL}
+    for _ in range(rounds):
+        for p in PAIRS_ALL:
+            c = caches[p]
+            for _ in range(2):
+                c.decode_append(0, Kn, Vn, Q, ctx, w.scale, out=out)
+            (e0, e1), = events(1)
+            e0.record(stream)
+            for _ in range(calls):
+                c.decode_append(0, Kn, Vn, Q, ctx, w.scale, out=out)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            times[p].append(e0.elapsed_time(e1) / calls)
+    res = []
+    q_bytes, o_bytes = S * w.n_q_heads * w.head_dim * 2, S * w.n_q_heads * w.head_dim * 4
+    for kt, vt in PAIRS_ALL:
+        alg = (kv_bytes_per_layer(w, kt, vt) + q_bytes + o_bytes + S * w.n_kv_heads * w.head_dim * 2 * 2 +
+               S * w.n_kv_heads * (row_bytes(w, kt) + row_bytes(w, vt)))
+        ms = median(times[(kt, vt)])
+        gbs = alg / (ms * 1e-3) / 1e9
+        res.append({"k_type": kt, "v_type": vt, "us_per_call": round(ms * 1e3, 2), "alg_bytes_per_call": alg,
+                    "GB_per_s": round(gbs, 1), "frac": round(gbs / HBM_PEAK_GBPS, 4)})
+        log(f"  {kt}/{vt}: {ms * 1e3:.1f} us, {gbs:.0f} GB/s ({100 * gbs / HBM_PEAK_GBPS:.0f}%)")
+    del caches, out
+    torch.cuda.empty_cache()
+    return {"workload": w.name, "layers": 1, "timing": f"median of {rounds} interleaved rounds of {calls} calls",
+            "pairs": res}
+
+
 def calib_copy(dev):
     """Three plain 1 GiB device-to-device copies: the reference that scales
     hardware byte counters (FETCH_SIZE, WRITE_SIZE) to bytes."""
@@ -806,6 +870,8 @@ def main():
         result["prefill"] = prefill_measure(dev, cpu=not args.no_cpu_baseline)
     if not args.no_configs and args.only is None:
         result["configs"] = other_configs(dev, args)
+    if not args.no_pairs and args.only is None:
+        result["pairs"] = pairs_sweep(dev)
     print(json.dumps(result), flush=True)
 
 

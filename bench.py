@@ -652,6 +652,52 @@ def prefill_measure(dev, calls=5, cpu=False, pair=None):
     return res
 
 
+def prefill_head_dims(dev, calls=3):
+    """The causal prefill at the other head dims: head_dim 64 (32 query / 4 kv
+    heads) and 256 (16 / 8), 4 sequences, the last 512-query chunk of 32768
+    positions, one layer; K8V4 and f16/f16.  Seeded Student-t keys as in the
+    long-context workload."""
+    import torch
+
+    import mixed_precision_quantized_quantize_amd as kvq
+    from mixed_precision_quantized_quantize_amd import synth
+
+    out_list = []
+    for D, hq, hkv in ((64, 32, 4), (256, 16, 8)):
+        w = synth.Workload(f"prefill_d{D}", 1, hq, hkv, D, 32768, 4, (("q8_0", "q4_0"), ("f16", "f16")),
+                           "student_t", 6000 + D, prefill=512)
+        n_tok, T, S = w.prefill, w.ctx, w.batch
+        Q = synth.queries(w, 0, n_tok=n_tok, device=dev)
+        for kt, vt in w.type_pairs:
+            cache = kvq.KVCache(1, S, hq, hkv, D, T, (kt, vt), device=dev)
+            for c0 in range(0, T, synth.CHUNK):
+                K, V = synth.kv_batch(w, 0, c0, min(synth.CHUNK, T - c0), device=dev)
+                cache.append(0, K, V, [c0] * S)
+                del K, V
+            out = torch.empty(tuple(Q.shape), dtype=torch.float32, device=dev)
+            p0 = [T - n_tok] * S
+            stream = torch.cuda.current_stream(dev)
+            cache.prefill(0, Q, p0, w.scale, out=out)
+            torch.cuda.synchronize()
+            (e0, e1), = events(1)
+            e0.record(stream)
+            for _ in range(calls):
+                cache.prefill(0, Q, p0, w.scale, out=out)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            ms = e0.elapsed_time(e1) / calls
+            flop = 4.0 * D * hq * sum(T - n_tok + i + 1 for i in range(n_tok)) * S
+            tf = flop / (ms * 1e-3) / 1e12
+            log(f"  prefill D={D} {hq}/{hkv} {kt}/{vt}: {ms:.3f} ms, {tf:.1f} TFLOP/s "
+                f"({100 * tf / MFMA_F16_PEAK_TFLOPS:.1f}% of peak)")
+            out_list.append({"head_dim": D, "q_heads": hq, "kv_heads": hkv, "k_type": kt, "v_type": vt,
+                             "batch": S, "n_tok": n_tok, "ctx": T, "ms_per_call": round(ms, 4),
+                             "TFLOP_per_s": round(tf, 1), "frac": round(tf / MFMA_F16_PEAK_TFLOPS, 4)})
+            del cache, out
+            torch.cuda.empty_cache()
+    return out_list
+
+
 def prefill_cpu_baseline(w, Q, pair, n_q=64):
     """The oracle's causal prefill on a bounded sample of the same call:
     sequence 0, the first and the last n_q queries of the chunk, all heads."""
@@ -868,6 +914,7 @@ def main():
     torch.cuda.empty_cache()
     if not args.no_prefill and args.only is None:
         result["prefill"] = prefill_measure(dev, cpu=not args.no_cpu_baseline)
+        result["prefill"]["other_head_dims"] = prefill_head_dims(dev)
     if not args.no_configs and args.only is None:
         result["configs"] = other_configs(dev, args)
     if not args.no_pairs and args.only is None:

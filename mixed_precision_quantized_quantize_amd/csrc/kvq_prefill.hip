@@ -41,26 +41,44 @@ namespace {
 
 using namespace dev;
 
-constexpr int PW = 4;  // waves per workgroup
+// f(integral_constant<int, 0>), ..., f(integral_constant<int, N-1>), in order.
+template <int N, class F>
+__device__ inline __attribute__((always_inline)) void static_for_pf(F &&f)
+{
+    if constexpr (N > 0) {
+        static_for_pf<N - 1>(f);
+        f(std::integral_constant<int, N - 1>());
+    }
+}
 
-// 16-row blocks per wave: two.  At head_dim <= 128 a wave then fits in 256
-// registers and two workgroups share each CU (one wave's softmax then runs
-// beside another's MFMAs); at 256 a wave takes up to 448 of 512 and the CU
-// holds one workgroup, whose 128 rows still halve the dequantization per row
-// (measured 35% faster than one row block).  This file is compiled with the
-// MFMA accumulators in VGPRs (-amdgpu-mfma-vgpr-form): the online-softmax
-// rescale touches them with vector instructions, and with AGPR accumulators
-// the compiler copied them between the two register files on every tile.
-template <int D> struct Rows { static constexpr int RB = 2; };
+// Rows and waves of a workgroup.  At head_dim <= 128: four waves of two
+// 16-row blocks; a wave then fits in 256 registers and two workgroups share
+// each CU (one wave's softmax runs beside another's MFMAs).  At 256 with a
+// quantized half: eight waves of one row block, two waves per SIMD in one
+// workgroup per CU (measured 36% faster for K8V4 than four waves of two
+// blocks, whose 448-register waves ran alone on their SIMDs, the
+// dequantization and the MFMAs largely one after the other).  f16/f16 at
+// 256 keeps four waves of two blocks: with one block per wave it spilled.
+// This file is compiled with the MFMA accumulators in VGPRs
+// (-amdgpu-mfma-vgpr-form): the online-softmax rescale touches them with
+// vector instructions, and with AGPR accumulators the compiler copied them
+// between the two register files on every tile.
+template <int KT, int VT, int D> struct Layout {
+    static constexpr bool ONE = D == 256 && !(KT == KVQ_F16 && VT == KVQ_F16);
+    static constexpr int RB = ONE ? 1 : 2;  // 16-row blocks per wave
+    static constexpr int PW = ONE ? 8 : 4;  // waves per workgroup
+    static constexpr int WPE = D <= 128 || ONE ? 2 : 1;  // waves per SIMD the registers allow
+};
 
 __device__ inline half8 splat8(uint32_t pair) { return pack4(pair, pair, pair, pair); }
 
 template <int KT, int VT, int D>
-__global__ __launch_bounds__(64 * PW) __attribute__((amdgpu_waves_per_eu(D <= 128 ? 2 : 1))) void prefill_kernel(const PrefillArgs a)
+__global__ __launch_bounds__((64 * Layout<KT, VT, D>::PW)) __attribute__((amdgpu_waves_per_eu((Layout<KT, VT, D>::WPE)))) void prefill_kernel(const PrefillArgs a)
 {
     using g = Geo<KT, VT, D>;
+    constexpr int PW = Layout<KT, VT, D>::PW;
     constexpr int NB = g::NB, NCT = g::NCT;
-    constexpr int RB = Rows<D>::RB;
+    constexpr int RB = Layout<KT, VT, D>::RB;
     constexpr int ROWS_G = 16 * RB * PW;
     constexpr int VL = (VT == KVQ_Q4_0 || VT == KVQ_Q5_0 || VT == KVQ_TURBO3) ? NB : NCT;
     constexpr bool KQ = KT != KVQ_F16, VQ = VT != KVQ_F16;
@@ -438,15 +456,14 @@ __global__ __launch_bounds__(64 * PW) __attribute__((amdgpu_waves_per_eu(D <= 12
     // i % PW, and vector-memory loads complete in issue order, so at most
     // this wave's share of one tile may remain outstanding.
     constexpr int NDMA = g::NDMA;
-    static_assert(PW == 4 && (NDMA + 3) / 4 < 64, "vmcnt holds 6 bits");
+    static_assert((NDMA + PW - 1) / PW < 64, "vmcnt holds 6 bits");
     auto wait_share = [&]() __attribute__((always_inline)) {
-        constexpr int c0 = (NDMA + 3) / 4, c1 = (NDMA + 2) / 4, c2 = (NDMA + 1) / 4, c3 = NDMA / 4;
-        switch (wave) {
-        case 0: __builtin_amdgcn_s_waitcnt((c0 & 15) | ((c0 >> 4) << 14) | 0x70 | 0xF00); break;
-        case 1: __builtin_amdgcn_s_waitcnt((c1 & 15) | ((c1 >> 4) << 14) | 0x70 | 0xF00); break;
-        case 2: __builtin_amdgcn_s_waitcnt((c2 & 15) | ((c2 >> 4) << 14) | 0x70 | 0xF00); break;
-        default: __builtin_amdgcn_s_waitcnt((c3 & 15) | ((c3 >> 4) << 14) | 0x70 | 0xF00); break;
-        }
+        // wave w issues (NDMA + PW - 1 - w) / PW of a tile's copy instructions
+        static_for_pf<PW>([&](auto w) {
+            constexpr int c = (NDMA + PW - 1 - decltype(w)::value) / PW;
+            if (wave == decltype(w)::value)
+                __builtin_amdgcn_s_waitcnt((c & 15) | ((c >> 4) << 14) | 0x70 | 0xF00);
+        });
     };
     auto body = [&](auto diag_c, auto last2_c, const int t, uint8_t *const dqw, const uint8_t *const dqr) __attribute__((always_inline)) {
         constexpr bool LAST2 = decltype(last2_c)::value;  // t = ntile-2: no copy to start, dequant with mask
@@ -541,7 +558,8 @@ __global__ __launch_bounds__(64 * PW) __attribute__((amdgpu_waves_per_eu(D <= 12
 template <int KT, int VT, int D>
 hipError_t launch_pf(const PrefillArgs &a, hipStream_t st)
 {
-    constexpr int ROWS_G = 16 * Rows<D>::RB * PW;
+    constexpr int PW = Layout<KT, VT, D>::PW;
+    constexpr int ROWS_G = 16 * Layout<KT, VT, D>::RB * PW;
     const int rows = a.n_tok << a.gp_log2;
     dim3 grid((rows + ROWS_G - 1) / ROWS_G, a.Hkv, a.n_seqs);
     hipLaunchKernelGGL((prefill_kernel<KT, VT, D>), grid, dim3(64 * PW), 0, st, a);

@@ -62,10 +62,15 @@ def test_prefill_pairs(kt, vt, D):
                  seed=zlib.crc32(f"p{kt}{vt}{D}".encode()) % 1000)
 
 
-@pytest.mark.parametrize("kt,vt", [("q8_0", "q4_0"), ("f16", "f16"), ("q4_0", "q8_0"), ("q5_0", "q5_0"), ("q5_0", "f16"), ("q8_0", "turbo3")])
+@pytest.mark.parametrize("kt,vt", PAIRS)
 def test_prefill_head_dim_256(kt, vt):
+    """Every pair at head_dim 256 (eight waves of one row block per
+    workgroup where a half is quantized, four of two for f16/f16): group 4
+    over 2 workgroups and group 8 over 5, ragged chunk starts."""
     print(f"prefill parity {kt}/{vt} D=256", flush=True)
     prefill_case(kt, vt, S=2, Hq=8, Hkv=2, D=256, T=200, n_tok=45, q_pos0=[155, 3], seed=8)
+    prefill_case(kt, vt, S=2, Hq=16, Hkv=2, D=256, T=300, n_tok=70, q_pos0=[230, 61],
+                 seed=zlib.crc32(f"p256{kt}{vt}".encode()) % 1000)
 
 
 @pytest.mark.parametrize("G", [1, 2, 3, 5, 16])

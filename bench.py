@@ -102,6 +102,19 @@ def row_bytes(w, t):
     return plane_bytes(w, t, n_seqs=1, ctx=32) // (32 * w.n_kv_heads)
 
 
+def launch_bytes(w, kt, vt, fused=True):
+    """Algorithmic HBM bytes of one decode launch over one layer: the layer's
+    K and V planes read once, the binary16 queries read, the float32 outputs
+    written and, when the append is fused, the new f16 K/V rows read and their
+    quantized rows written."""
+    S = w.batch
+    q_bytes = S * w.n_q_heads * w.head_dim * 2
+    o_bytes = S * w.n_q_heads * w.head_dim * 4
+    new_bytes = (S * w.n_kv_heads * w.head_dim * 2 * 2 +
+                 S * w.n_kv_heads * (row_bytes(w, kt) + row_bytes(w, vt))) if fused else 0
+    return kv_bytes_per_layer(w, kt, vt) + q_bytes + o_bytes + new_bytes
+
+
 DECODE_SOURCES = ("kvq_decode.hip", "kvq_device.h", "kvq_quant.h", "kvq_internal.h")
 PREFILL_SOURCES = ("kvq_prefill.hip", "kvq_device.h", "kvq_internal.h")
 
@@ -395,11 +408,7 @@ def decode_workload(w, kt, vt, dev, args, first_pair=True, flush_mall=False, ora
         call_ms = tm["ms_per_step"] / L
         call_timing = "HIP events around the timed region / (steps x layers); gaps between calls included"
 
-    q_bytes = S * w.n_q_heads * w.head_dim * 2
-    o_bytes = S * w.n_q_heads * w.head_dim * 4
-    new_bytes = 0 if args.unfused else (S * w.n_kv_heads * w.head_dim * 2 * 2 +
-                                        S * w.n_kv_heads * (row_bytes(w, kt) + row_bytes(w, vt)))
-    alg_launch = kv_layer + q_bytes + o_bytes + new_bytes
+    alg_launch = launch_bytes(w, kt, vt, fused=not args.unfused)
     kv_step = kv_layer * L
     ms_main = median(tm["ms_flushed"]) if flush_mall else tm["ms_per_step"]
     call_main = ms_main / L if flush_mall else call_ms
@@ -812,10 +821,8 @@ def pairs_sweep(dev, rounds=5, calls=10):
             torch.cuda.synchronize()
             times[p].append(e0.elapsed_time(e1) / calls)
     res = []
-    q_bytes, o_bytes = S * w.n_q_heads * w.head_dim * 2, S * w.n_q_heads * w.head_dim * 4
     for kt, vt in PAIRS_ALL:
-        alg = (kv_bytes_per_layer(w, kt, vt) + q_bytes + o_bytes + S * w.n_kv_heads * w.head_dim * 2 * 2 +
-               S * w.n_kv_heads * (row_bytes(w, kt) + row_bytes(w, vt)))
+        alg = launch_bytes(w, kt, vt)
         ms = median(times[(kt, vt)])
         gbs = alg / (ms * 1e-3) / 1e9
         res.append({"k_type": kt, "v_type": vt, "us_per_call": round(ms * 1e3, 2), "alg_bytes_per_call": alg,

@@ -50,6 +50,7 @@ METRIC = "decode-attn KV GB/s (% HBM peak) + tok/s, K8V4 Llama-3-8B shape, 32K c
 HBM_PEAK_GBPS = 8000.0
 MFMA_F16_PEAK_TFLOPS = 2500.0  # dense binary16 matrix peak
 MALL_FLUSH_BYTES = 1 << 30     # a write of this size between steps evicts the last-level cache
+PREWARM_S = 0.2               # untimed warm-up of the measurements other than the headline (see prewarm)
 
 ONLY = ("llama3_8b_32k", "single_layer_2k", "tinyllama_8k", "llama31_70b_32k", "llama3_8b_128k", "prefill")
 
@@ -175,14 +176,36 @@ def median(xs):
     return xs[n // 2] if n % 2 else 0.5 * (xs[n // 2 - 1] + xs[n // 2])
 
 
-def time_steps(run, steps, warmup, stream, flush=None, run_all=None):
+def prewarm(run, seconds):
+    """Untimed calls of run() until `seconds` of wall-clock time have passed
+    (checked every four calls).  Right after a cache is filled, the first few
+    tens of milliseconds of calls run slower (up to 2.7x on the first ones)
+    before they settle; the headline workload keeps exactly its W warmup
+    steps, the other measurements warm up for a fixed time instead.  Returns
+    the number of calls."""
+    import torch
+
+    t0, n = time.perf_counter(), 0
+    while seconds > 0:
+        for _ in range(4):
+            run()
+        n += 4
+        torch.cuda.synchronize()
+        if time.perf_counter() - t0 >= seconds:
+            break
+    return n
+
+
+def time_steps(run, steps, warmup, stream, flush=None, run_all=None, prewarm_s=0.0):
     """Back-to-back steps bracketed by one pair of events (the timed region
     holds the steps and nothing else; run_all, if given, runs all `steps` of
     them at once, e.g. one graph of them all), then a second pass with events
     around each step for the median and spread; with `flush`, a third pass
-    that runs flush() before each step and times the step alone."""
+    that runs flush() before each step and times the step alone.  Before the
+    `warmup` steps, `prewarm_s` seconds of untimed steps."""
     import torch
 
+    n_pre = prewarm(run, prewarm_s)
     for _ in range(warmup):
         run()
     torch.cuda.synchronize()
@@ -195,7 +218,7 @@ def time_steps(run, steps, warmup, stream, flush=None, run_all=None):
             run()
     e1.record(stream)
     torch.cuda.synchronize()
-    res = {"ms_per_step": e0.elapsed_time(e1) / steps}
+    res = {"ms_per_step": e0.elapsed_time(e1) / steps, "prewarm_steps": n_pre}
     ev = events(steps)
     for a, b in ev:
         a.record(stream)
@@ -385,7 +408,8 @@ def decode_workload(w, kt, vt, dev, args, first_pair=True, flush_mall=False, ora
     run = graph.replay if graph is not None else step
     flush_buf, flush = mall_flusher(dev) if flush_mall else (None, None)
     tm = time_steps(run, args.steps, args.warmup, stream, flush=flush,
-                    run_all=graph_all.replay if graph_all is not None else None)
+                    run_all=graph_all.replay if graph_all is not None else None,
+                    prewarm_s=0.0 if headline else PREWARM_S)
     del flush_buf, graph_all
 
     if args.unfused:
@@ -422,6 +446,7 @@ def decode_workload(w, kt, vt, dev, args, first_pair=True, flush_mall=False, ora
                    "append": "separate kvq_append" if args.unfused else "fused into the decode call"},
         "value": round(value, 2), "unit": "GB/s",
         "ms_per_step": round(ms_main, 4),
+        "untimed_prewarm_steps": tm["prewarm_steps"],
         "ms_per_step_median": round(median(tm["ms_flushed"]) if flush_mall else tm["ms_median"], 4),
         "ms_per_step_min_max": [round(min(tm["ms_flushed"]), 4), round(max(tm["ms_flushed"]), 4)] if flush_mall
         else [round(tm["ms_min"], 4), round(tm["ms_max"], 4)],
@@ -522,7 +547,8 @@ def single_layer_2k(dev, args):
     # back-to-back figure replays one graph of all the timed steps
     graph, graph_all = graph_of(step), graph_of(step, args.steps)
     flush_buf, flush = mall_flusher(dev)
-    tm = time_steps(graph.replay, args.steps, args.warmup, stream, flush=flush, run_all=graph_all.replay)
+    tm = time_steps(graph.replay, args.steps, args.warmup, stream, flush=flush, run_all=graph_all.replay,
+                    prewarm_s=PREWARM_S)
     del graph_all
     # per-call durations of flushed steps (events inside the step)
     for _ in range(args.steps):
@@ -542,6 +568,7 @@ def single_layer_2k(dev, args):
                    "step": f"kvq_append of all {T} rows, then kvq_attn_decode over them", "graph": True},
         "value": round(kv / (ms * 1e-3) / 1e9, 2), "unit": "GB/s",
         "ms_per_step": round(ms, 4),
+        "untimed_prewarm_steps": tm["prewarm_steps"],
         "ms_per_step_min_max": [round(min(tm["ms_flushed"]), 4), round(max(tm["ms_flushed"]), 4)],
         "timing": ("each step timed alone with HIP events after a 1 GiB device write that evicts the last-level "
                    "cache (median of the steps)"),
@@ -627,9 +654,7 @@ def prefill_measure(dev, calls=5, cpu=False, pair=None):
     out = torch.empty(tuple(Q.shape), dtype=torch.float32, device=dev)
     p0 = [T - n_tok] * S
     stream = torch.cuda.current_stream(dev)
-    for _ in range(2):
-        cache.prefill(0, Q, p0, w.scale, out=out)
-    torch.cuda.synchronize()
+    prewarm(lambda: cache.prefill(0, Q, p0, w.scale, out=out), PREWARM_S)
     (e0, e1), = events(1)
     e0.record(stream)
     for _ in range(calls):
@@ -661,11 +686,12 @@ def prefill_measure(dev, calls=5, cpu=False, pair=None):
     return res
 
 
-def prefill_head_dims(dev, calls=3):
+def prefill_head_dims(dev, calls=3, rounds=5):
     """The causal prefill at the other head dims: head_dim 64 (32 query / 4 kv
     heads) and 256 (16 / 8), 4 sequences, the last 512-query chunk of 32768
     positions, one layer; K8V4 and f16/f16.  Seeded Student-t keys as in the
-    long-context workload."""
+    long-context workload.  ms per call: median over `rounds` groups of
+    `calls` calls, after a timed warm-up."""
     import torch
 
     import mixed_precision_quantized_quantize_amd as kvq
@@ -686,15 +712,16 @@ def prefill_head_dims(dev, calls=3):
             out = torch.empty(tuple(Q.shape), dtype=torch.float32, device=dev)
             p0 = [T - n_tok] * S
             stream = torch.cuda.current_stream(dev)
-            cache.prefill(0, Q, p0, w.scale, out=out)
-            torch.cuda.synchronize()
-            (e0, e1), = events(1)
-            e0.record(stream)
-            for _ in range(calls):
-                cache.prefill(0, Q, p0, w.scale, out=out)
-            e1.record(stream)
-            torch.cuda.synchronize()
-            ms = e0.elapsed_time(e1) / calls
+            prewarm(lambda: cache.prefill(0, Q, p0, w.scale, out=out), PREWARM_S)
+            group_ms = []
+            for (e0, e1) in events(rounds):
+                e0.record(stream)
+                for _ in range(calls):
+                    cache.prefill(0, Q, p0, w.scale, out=out)
+                e1.record(stream)
+                torch.cuda.synchronize()
+                group_ms.append(e0.elapsed_time(e1) / calls)
+            ms = median(group_ms)
             flop = 4.0 * D * hq * sum(T - n_tok + i + 1 for i in range(n_tok)) * S
             tf = flop / (ms * 1e-3) / 1e12
             log(f"  prefill D={D} {hq}/{hkv} {kt}/{vt}: {ms:.3f} ms, {tf:.1f} TFLOP/s "

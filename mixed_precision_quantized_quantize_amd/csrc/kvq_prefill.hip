@@ -68,6 +68,11 @@ template <int KT, int VT, int D> struct Layout {
     static constexpr int RB = ONE ? 1 : 2;  // 16-row blocks per wave
     static constexpr int PW = ONE ? 8 : 4;  // waves per workgroup
     static constexpr int WPE = D <= 128 || ONE ? 2 : 1;  // waves per SIMD the registers allow
+    // 32-key tiles per step (one barrier, one softmax update): two at head_dim
+    // 64, where a tile's matrix work is half that of 128 but its barrier,
+    // waits, row maxima and rescale check cost the same; the step then holds
+    // as many bytes and operands as a tile at 128
+    static constexpr int SUB = D == 64 ? 2 : 1;
 };
 
 __device__ inline half8 splat8(uint32_t pair) { return pack4(pair, pair, pair, pair); }
@@ -79,6 +84,7 @@ __global__ __launch_bounds__((64 * Layout<KT, VT, D>::PW)) __attribute__((amdgpu
     constexpr int PW = Layout<KT, VT, D>::PW;
     constexpr int NB = g::NB, NCT = g::NCT;
     constexpr int RB = Layout<KT, VT, D>::RB;
+    constexpr int SUB = Layout<KT, VT, D>::SUB, STEP = TILE * SUB;
     constexpr int ROWS_G = 16 * RB * PW;
     constexpr int VL = (VT == KVQ_Q4_0 || VT == KVQ_Q5_0 || VT == KVQ_TURBO3) ? NB : NCT;
     constexpr bool KQ = KT != KVQ_F16, VQ = VT != KVQ_F16;
@@ -87,9 +93,10 @@ __global__ __launch_bounds__((64 * Layout<KT, VT, D>::PW)) __attribute__((amdgpu
     constexpr bool PRIO_DQ = (KT == KVQ_Q8_0 || KT == KVQ_Q5_0) && VQ;
 
     // Dequantized operands of the current tile, built once per workgroup:
-    // K hi and lo per (score tile T, block b), V (times scale) per (block b,
-    // half hh); each set is one MFMA operand, 16 bytes per lane, lane-major.
-    constexpr int NKSET = KQ ? 2 * NB : 0, NVSET = VQ ? 2 * NB : 0;
+    // K hi and lo per (tile u of the step, score tile T, block b), V (times
+    // scale) per (u, block b, half hh); each set is one MFMA operand, 16 bytes
+    // per lane, lane-major.
+    constexpr int NKSET = KQ ? 2 * NB * SUB : 0, NVSET = VQ ? 2 * NB * SUB : 0;
     constexpr int DQ_KHI = 0, DQ_KLO = DQ_KHI + NKSET * 1024, DQ_V = DQ_KLO + NKSET * 1024;
     constexpr int DQ_BYTES = DQ_V + NVSET * 1024;
     // tile t's in dq0 (t even) or dq1 (t odd): two arrays, so that the
@@ -97,14 +104,15 @@ __global__ __launch_bounds__((64 * Layout<KT, VT, D>::PW)) __attribute__((amdgpu
     // other's, and may interleave the two
     __shared__ __attribute__((aligned(16))) uint8_t dq0[DQ_BYTES > 0 ? DQ_BYTES : 16];
     __shared__ __attribute__((aligned(16))) uint8_t dq1[DQ_BYTES > 0 ? DQ_BYTES : 16];
-    // raw tiles: tile t in lds[t % NRAW].  While t is computed, t+1 is being
-    // dequantized and the copies of the later tiles are in flight: t+2 with
-    // three buffers, t+2 and t+3 with four, which every pair gets where they
-    // fit beside the operand arrays at the workgroups per CU the kernel is
-    // built for (two at head_dim <= 128, one at 256)
+    // raw steps (SUB tiles each, tile u at u * g::BYTES): step t in
+    // lds[t % NRAW].  While t is computed, t+1 is being dequantized and the
+    // copies of the later steps are in flight: t+2 with three buffers, t+2
+    // and t+3 with four, which every pair gets where they fit beside the
+    // operand arrays at the workgroups per CU the kernel is built for (two at
+    // head_dim <= 128, one at 256)
     constexpr int LDS_WG = (D <= 128 ? 80 : 160) * 1024;
-    constexpr int NRAW = 4 * g::BYTES + 2 * (DQ_BYTES > 0 ? DQ_BYTES : 16) <= LDS_WG ? 4 : 3;
-    __shared__ __attribute__((aligned(16))) uint8_t lds[NRAW][g::BYTES];
+    constexpr int NRAW = 4 * SUB * g::BYTES + 2 * (DQ_BYTES > 0 ? DQ_BYTES : 16) <= LDS_WG ? 4 : 3;
+    __shared__ __attribute__((aligned(16))) uint8_t lds[NRAW][SUB * g::BYTES];
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -202,24 +210,25 @@ __global__ __launch_bounds__((64 * Layout<KT, VT, D>::PW)) __attribute__((amdgpu
             o[rb][ct] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
     }
 
-    const int ntile = (key_end + TILE - 1) / TILE;
+    const int ntile = (key_end + STEP - 1) / STEP;  // steps
 
-    // ---- dequantization of tile t (raw copy in lds[t % NRAW]) into dqt,
-    // the operand array of its parity (dq0 or dq1).  The tile's jobs are K sets (T, b), then V blocks b; this
-    // wave takes jobs wave, wave + PW, ...  As 2*NB is a multiple of PW, the
-    // i-th job of every wave is of the same kind: straight-line code with
-    // wave-uniform offsets.  MASK: the tile may reach past key_end.
-    static_assert(!KQ || (2 * NB) % PW == 0, "K jobs are dealt evenly");
+    // ---- dequantization of step t (raw copy in lds[t % NRAW]) into dqt,
+    // the operand array of its parity (dq0 or dq1).  The step's jobs are K
+    // sets (u, T, b), then V blocks (u, b); this wave takes jobs wave,
+    // wave + PW, ...  As 2*NB*SUB is a multiple of PW, the i-th job of every
+    // wave is of the same kind: straight-line code with wave-uniform offsets.
+    // MASK: the step may reach past key_end.
+    static_assert(!KQ || (2 * NB * SUB) % PW == 0, "K jobs are dealt evenly");
     auto dequant = [&](auto mask_c, const int t, uint8_t *const dqt) __attribute__((always_inline)) {
         constexpr bool MASK = decltype(mask_c)::value;
-        const uint8_t *buf = lds[t % NRAW];
-        const int tb = t * TILE;
-        constexpr int NKJ = KQ ? 2 * NB : 0, NJOB = NKJ + (VQ ? NB : 0);
+        constexpr int NKJ = KQ ? 2 * NB * SUB : 0, NJOB = NKJ + (VQ ? NB * SUB : 0);
 #pragma unroll
         for (int i = 0; i < (NJOB + PW - 1) / PW; i++) {
             const int job = wave + PW * i;
             if (PW * i < NKJ) {
-                const int T = job / NB, b = job - T * NB;
+                const int u = SUB == 1 ? 0 : job / (2 * NB), T = SUB == 1 ? job / NB : (job / NB) & 1;
+                const int b = job - (job / NB) * NB;
+                const uint8_t *buf = lds[t % NRAW] + u * g::BYTES;
                 const int r = 8 * (n >> 2) + 4 * T + (n & 3);  // this lane's key in the tile
                 const int c = (KT == KVQ_Q8_0) ? 2 * b + (j >> 1) : b;
                 const int within = (KT == KVQ_Q8_0) ? 8 * (j & 1) : 4 * j;
@@ -243,7 +252,9 @@ __global__ __launch_bounds__((64 * Layout<KT, VT, D>::PW)) __attribute__((amdgpu
                 *reinterpret_cast<half8 *>(dqt + DQ_KHI + (job * 64 + lane) * 16) = hi;
                 *reinterpret_cast<half8 *>(dqt + DQ_KLO + (job * 64 + lane) * 16) = lo;
             } else if (VQ && (NJOB % PW == 0 || job < NJOB)) {  // waves < PW: only a ragged last round checks
-                const int b = job - NKJ;
+                const int u = SUB == 1 ? 0 : (job - NKJ) / NB, b = job - NKJ - u * NB;
+                const uint8_t *buf = lds[t % NRAW] + u * g::BYTES;
+                const int tb = t * STEP + TILE * u;
                 // LDS offset of the codes a lane reads for operand u (as v_rd)
                 auto vrd = [&](const int u_i) {
                     const int u = (VT == KVQ_TURBO3) ? 8 * u_i + (n & 7) : 16 * u_i + n;
@@ -293,42 +304,48 @@ __global__ __launch_bounds__((64 * Layout<KT, VT, D>::PW)) __attribute__((amdgpu
                 const half8 dv = pack4(vsc.x, vsc.y, vsc.z, vsc.w);  // scales of keys 0..7
 #pragma unroll
                 for (int hh = 0; hh < 2; hh++)
-                    *reinterpret_cast<half8 *>(dqt + DQ_V + ((2 * b + hh) * 64 + lane) * 16) = va[hh] * dv;
+                    *reinterpret_cast<half8 *>(dqt + DQ_V + ((2 * NB * u + 2 * b + hh) * 64 + lane) * 16) = va[hh] * dv;
             }
         }
     };
 
-    // ---- one tile's attention from its operands (dqt, and the raw tile for
-    // binary16 planes); DG: the tile may hold keys past a row's
-    // position (masking)
+    // ---- one step's attention from its operands (dqt, and the raw tiles
+    // for binary16 planes); DG: the step may hold keys past a row's
+    // position (masking).  Key r of lane group j in tile u is
+    // t * STEP + TILE * u + 8 j + r.
     auto compute = [&](auto diag_c, const int t, const uint8_t *const dqt) __attribute__((always_inline)) {
         constexpr bool DG = decltype(diag_c)::value;
         const uint8_t *buf = lds[t % NRAW];
-        const int tb = t * TILE;
-        // raw f16 operands (no dequantization) stay in the raw tile
-        u32x4 kop[2][NB];
-        u32x4 vop[VL];
+        const int tb = t * STEP;
+        // raw f16 operands (no dequantization) stay in the raw tiles
+        u32x4 kop[SUB][2][NB];
+        u32x4 vop[SUB][VL];
         if (!KQ) {
 #pragma unroll
-            for (int T = 0; T < 2; T++)
+            for (int u = 0; u < SUB; u++)
 #pragma unroll
-                for (int b = 0; b < NB; b++)
-                    kop[T][b] = *reinterpret_cast<const u32x4 *>(buf + k_rd[T][b]);
+                for (int T = 0; T < 2; T++)
+#pragma unroll
+                    for (int b = 0; b < NB; b++)
+                        kop[u][T][b] = *reinterpret_cast<const u32x4 *>(buf + u * g::BYTES + k_rd[T][b]);
         }
         if (!VQ) {
 #pragma unroll
-            for (int i = 0; i < VL; i++)
-                vop[i] = *reinterpret_cast<const u32x4 *>(buf + v_rd[i]);
-            if (DG && tb + TILE > key_end) {
-                uint32_t vk[4];
-#pragma unroll
-                for (int i = 0; i < 4; i++) {
-                    const int k0 = tb + 8 * j + 2 * i;
-                    vk[i] = (k0 < key_end ? 0x0000FFFFu : 0u) | (k0 + 1 < key_end ? 0xFFFF0000u : 0u);
-                }
+            for (int u = 0; u < SUB; u++) {
 #pragma unroll
                 for (int i = 0; i < VL; i++)
-                    vop[i] = u32x4{vop[i].x & vk[0], vop[i].y & vk[1], vop[i].z & vk[2], vop[i].w & vk[3]};
+                    vop[u][i] = *reinterpret_cast<const u32x4 *>(buf + u * g::BYTES + v_rd[i]);
+                if (DG && tb + TILE * (u + 1) > key_end) {
+                    uint32_t vk[4];
+#pragma unroll
+                    for (int i = 0; i < 4; i++) {
+                        const int k0 = tb + TILE * u + 8 * j + 2 * i;
+                        vk[i] = (k0 < key_end ? 0x0000FFFFu : 0u) | (k0 + 1 < key_end ? 0xFFFF0000u : 0u);
+                    }
+#pragma unroll
+                    for (int i = 0; i < VL; i++)
+                        vop[u][i] = u32x4{vop[u][i].x & vk[0], vop[u][i].y & vk[1], vop[u][i].z & vk[2], vop[u][i].w & vk[3]};
+                }
             }
         }
         // ---- scores.  The two contraction phases raise the wave's issue
@@ -343,49 +360,59 @@ __global__ __launch_bounds__((64 * Layout<KT, VT, D>::PW)) __attribute__((amdgpu
         constexpr bool PRIO_QK = !KQ && !VQ;
         if (PRIO_QK)
             __builtin_amdgcn_s_setprio(1);
-        floatx4 sacc[RB][2];
+        floatx4 sacc[RB][2 * SUB];  // score tile 2u + T
 #pragma unroll
         for (int rb = 0; rb < RB; rb++)
-            sacc[rb][0] = sacc[rb][1] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-        for (int T = 0; T < 2; T++)
+            for (int x = 0; x < 2 * SUB; x++)
+                sacc[rb][x] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-            for (int b = 0; b < NB; b++) {
-                if (KT == KVQ_F16) {
-                    const half8 ka = pack4(kop[T][b].x, kop[T][b].y, kop[T][b].z, kop[T][b].w);
+        for (int u = 0; u < SUB; u++)
 #pragma unroll
-                    for (int rb = 0; rb < RB; rb++)
-                        sacc[rb][T] = mfma(ka, qb[rb][b], sacc[rb][T]);
-                } else {
-                    const int set = T * NB + b;
-                    const half8 hi = *reinterpret_cast<const half8 *>(dqt + DQ_KHI + (set * 64 + lane) * 16);
-                    const half8 lo = *reinterpret_cast<const half8 *>(dqt + DQ_KLO + (set * 64 + lane) * 16);
+            for (int T = 0; T < 2; T++)
 #pragma unroll
-                    for (int rb = 0; rb < RB; rb++) {
-                        sacc[rb][T] = mfma(hi, qb[rb][b], sacc[rb][T]);
-                        sacc[rb][T] = mfma(lo, qb[rb][b], sacc[rb][T]);
+                for (int b = 0; b < NB; b++) {
+                    const int x = 2 * u + T;
+                    if (KT == KVQ_F16) {
+                        const u32x4 w = kop[u][T][b];
+                        const half8 ka = pack4(w.x, w.y, w.z, w.w);
+#pragma unroll
+                        for (int rb = 0; rb < RB; rb++)
+                            sacc[rb][x] = mfma(ka, qb[rb][b], sacc[rb][x]);
+                    } else {
+                        const int set = (2 * u + T) * NB + b;
+                        const half8 hi = *reinterpret_cast<const half8 *>(dqt + DQ_KHI + (set * 64 + lane) * 16);
+                        const half8 lo = *reinterpret_cast<const half8 *>(dqt + DQ_KLO + (set * 64 + lane) * 16);
+#pragma unroll
+                        for (int rb = 0; rb < RB; rb++) {
+                            sacc[rb][x] = mfma(hi, qb[rb][b], sacc[rb][x]);
+                            sacc[rb][x] = mfma(lo, qb[rb][b], sacc[rb][x]);
+                        }
                     }
                 }
-            }
 
         if (PRIO_QK || PRIO_DQ)
             __builtin_amdgcn_s_setprio(0);
-        // ---- online softmax per row block; key r of lane group j is tb+8j+r
-        half8 pb[RB];
-        const bool diag = DG && tb + TILE - 1 > wave_first;  // some key of the tile is past some row's position
+        // ---- online softmax per row block; score x = 8u + r of a lane is key
+        // tb + 32u + 8j + r
+        constexpr int NS = 8 * SUB;
+        half8 pb[RB][SUB];
+        const bool diag = DG && tb + STEP - 1 > wave_first;  // some key of the step is past some row's position
 #pragma unroll
         for (int rb = 0; rb < RB; rb++) {
-            float sc[8];
+            float sc[NS];
 #pragma unroll
-            for (int r = 0; r < 8; r++)
-                sc[r] = sacc[rb][r >> 2][r & 3];
+            for (int x = 0; x < NS; x++)
+                sc[x] = sacc[rb][x >> 2][x & 3];
             if (diag) {
 #pragma unroll
-                for (int r = 0; r < 8; r++)
-                    if (tb + 8 * j + r > lim[rb])
-                        sc[r] = -INFINITY;
+                for (int x = 0; x < NS; x++)
+                    if (tb + TILE * (x >> 3) + 8 * j + (x & 7) > lim[rb])
+                        sc[x] = -INFINITY;
             }
             float mt = max3(max3(sc[0], sc[1], sc[2]), max3(sc[3], sc[4], sc[5]), max3(sc[6], sc[7], sc[7]));
+            if constexpr (SUB == 2)
+                mt = max3(mt, max3(max3(sc[8], sc[9], sc[10]), max3(sc[11], sc[12], sc[13]), sc[14]), sc[15]);
             mt = max_lane_groups(mt) * c2a;  // NaN only for a fully masked row at scale 0: no update
             if (__any(mt > m_run[rb])) {
                 const float m_new = fmaxf(m_run[rb], mt);
@@ -397,70 +424,83 @@ __global__ __launch_bounds__((64 * Layout<KT, VT, D>::PW)) __attribute__((amdgpu
                 m_run[rb] = m_new;
             }
             const float nm = -m_run[rb];
-            float p[8];
+            float p[NS];
 #pragma unroll
-            for (int r = 0; r < 8; r++)
-                p[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[r], c2a, nm));
+            for (int x = 0; x < NS; x++)
+                p[x] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[x], c2a, nm));
             if (diag) {
 #pragma unroll
-                for (int r = 0; r < 8; r++)
-                    p[r] = (sc[r] == -INFINITY) ? 0.0f : p[r];
+                for (int x = 0; x < NS; x++)
+                    p[x] = (sc[x] == -INFINITY) ? 0.0f : p[x];
             }
-            uint32_t w[4];
 #pragma unroll
-            for (int i = 0; i < 4; i++)
-                w[i] = h2_bits(__builtin_convertvector((float2v){p[2 * i], p[2 * i + 1]}, half2));
-            pb[rb] = pack4(w[0], w[1], w[2], w[3]);
+            for (int u = 0; u < SUB; u++) {
+                uint32_t w[4];
+#pragma unroll
+                for (int i = 0; i < 4; i++)
+                    w[i] = h2_bits(__builtin_convertvector((float2v){p[8 * u + 2 * i], p[8 * u + 2 * i + 1]}, half2));
+                pb[rb][u] = pack4(w[0], w[1], w[2], w[3]);
+            }
         }
 
         // ---- O^T += V^T . P
         __builtin_amdgcn_s_setprio(1);
 #pragma unroll
-        for (int b = 0; b < NB; b++) {
-            half8 va[2];
-            if (VQ) {
+        for (int u = 0; u < SUB; u++)
 #pragma unroll
-                for (int hh = 0; hh < 2; hh++)
-                    va[hh] = *reinterpret_cast<const half8 *>(dqt + DQ_V + ((2 * b + hh) * 64 + lane) * 16);
-            } else {
+            for (int b = 0; b < NB; b++) {
+                half8 va[2];
+                if (VQ) {
 #pragma unroll
-                for (int hh = 0; hh < 2; hh++) {
-                    const u32x4 w = vop[2 * b + hh];
-                    va[hh] = pack4(w.x, w.y, w.z, w.w);
+                    for (int hh = 0; hh < 2; hh++)
+                        va[hh] = *reinterpret_cast<const half8 *>(dqt + DQ_V + ((2 * NB * u + 2 * b + hh) * 64 + lane) * 16);
+                } else {
+#pragma unroll
+                    for (int hh = 0; hh < 2; hh++) {
+                        const u32x4 w = vop[u][2 * b + hh];
+                        va[hh] = pack4(w.x, w.y, w.z, w.w);
+                    }
+                }
+#pragma unroll
+                for (int rb = 0; rb < RB; rb++) {
+                    o[rb][2 * b] = mfma(va[0], pb[rb][u], o[rb][2 * b]);
+                    o[rb][2 * b + 1] = mfma(va[1], pb[rb][u], o[rb][2 * b + 1]);
                 }
             }
 #pragma unroll
-            for (int rb = 0; rb < RB; rb++) {
-                o[rb][2 * b] = mfma(va[0], pb[rb], o[rb][2 * b]);
-                o[rb][2 * b + 1] = mfma(va[1], pb[rb], o[rb][2 * b + 1]);
-            }
-        }
-#pragma unroll
         for (int rb = 0; rb < RB; rb++)
-            lacc[rb] = mfma(ones, pb[rb], lacc[rb]);
+#pragma unroll
+            for (int u = 0; u < SUB; u++)
+                lacc[rb] = mfma(ones, pb[rb][u], lacc[rb]);
         __builtin_amdgcn_s_setprio(0);
     };
 
-    // ---- the tile loop: one barrier per tile.  At the barrier of tile t,
-    // tile t+1's copy has landed (each wave waited for its share), tile t's
-    // operands are complete, and every wave is done with tile t-1's operands
-    // and with the raw buffer of tile t-1.  Then: start the copy of tile
-    // t+NRAW-1 into that buffer, build tile t+1's operands, and compute tile
+    // ---- the step loop: one barrier per step.  At the barrier of step t,
+    // step t+1's copy has landed (each wave waited for its share), step t's
+    // operands are complete, and every wave is done with step t-1's operands
+    // and with the raw buffer of step t-1.  Then: start the copy of step
+    // t+NRAW-1 into that buffer, build step t+1's operands, and compute step
     // t -- the dequantization's vector instructions run beside the MFMAs.
-    // dqw, dqr: the operand buffers of tiles t+1 and t.  In the loops they
-    // are the arrays themselves (pairs of tiles per round), so that the
-    // compiler may move tile t's operand reads and MFMAs in between tile
+    // dqw, dqr: the operand buffers of steps t+1 and t.  In the loops they
+    // are the arrays themselves (pairs of steps per round), so that the
+    // compiler may move step t's operand reads and MFMAs in between step
     // t+1's dequantization.
-    // Wait until this wave's copies of the tile before the last one issued
-    // have completed: instruction i of a tile's copy is issued by wave
-    // i % PW, and vector-memory loads complete in issue order, so at most
-    // this wave's share of one tile may remain outstanding.
-    constexpr int NDMA = g::NDMA;
-    static_assert((NDMA + PW - 1) / PW < 64, "vmcnt holds 6 bits");
+    // Copy of step t: instruction i of its tile u is issued by wave
+    // (u * NDMA + i) % PW.  Vector-memory loads complete in issue order, so
+    // waiting until at most this wave's share of one step is outstanding
+    // means that the step before the last one issued has landed.
+    constexpr int NDMA = g::NDMA, NDMA_S = SUB * NDMA;
+    static_assert((NDMA_S + PW - 1) / PW < 64, "vmcnt holds 6 bits");
+    auto issue_step = [&](const int t) __attribute__((always_inline)) {
+#pragma unroll
+        for (int u = 0; u < SUB; u++)
+            issue_tile<KT, VT, D>(lds[t % NRAW] + u * g::BYTES, t * STEP + TILE * u, lane, doff, rs,
+                                  u == 0 ? wave : (wave + PW - (u * NDMA) % PW) % PW, PW);
+    };
     auto wait_share = [&]() __attribute__((always_inline)) {
-        // wave w issues (NDMA + PW - 1 - w) / PW of a tile's copy instructions
+        // wave w issues (NDMA_S + PW - 1 - w) / PW of a step's copy instructions
         static_for_pf<PW>([&](auto w) {
-            constexpr int c = (NDMA + PW - 1 - decltype(w)::value) / PW;
+            constexpr int c = (NDMA_S + PW - 1 - decltype(w)::value) / PW;
             if (wave == decltype(w)::value)
                 __builtin_amdgcn_s_waitcnt((c & 15) | ((c >> 4) << 14) | 0x70 | 0xF00);
         });
@@ -468,15 +508,15 @@ __global__ __launch_bounds__((64 * Layout<KT, VT, D>::PW)) __attribute__((amdgpu
     auto body = [&](auto diag_c, auto last2_c, const int t, uint8_t *const dqw, const uint8_t *const dqr) __attribute__((always_inline)) {
         constexpr bool LAST2 = decltype(last2_c)::value;  // t = ntile-2: no copy to start, dequant with mask
         if (NRAW >= 4 && !LAST2)
-            wait_share();  // tile t+1 landed; this wave's copies of tile t+2 may still be in flight
+            wait_share();  // step t+1 landed; this wave's copies of step t+2 may still be in flight
         else
             asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
         if (NRAW >= 4) {
             if (!LAST2 && t + 3 < ntile)
-                issue_tile<KT, VT, D>(lds[(t + 3) % NRAW], (t + 3) * TILE, lane, doff, rs, wave, PW);
+                issue_step(t + 3);
         } else if (!LAST2) {
-            issue_tile<KT, VT, D>(lds[(t + 2) % NRAW], (t + 2) * TILE, lane, doff, rs, wave, PW);
+            issue_step(t + 2);
         }
         if (PRIO_DQ)
             __builtin_amdgcn_s_setprio(1);  // through this dequantization and tile t's scores
@@ -486,23 +526,23 @@ __global__ __launch_bounds__((64 * Layout<KT, VT, D>::PW)) __attribute__((amdgpu
     };
     using F = std::integral_constant<bool, false>;
     using Tr = std::integral_constant<bool, true>;
-    issue_tile<KT, VT, D>(lds[0], 0, lane, doff, rs, wave, PW);
+    issue_step(0);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
     if (ntile > 1)
-        issue_tile<KT, VT, D>(lds[1], TILE, lane, doff, rs, wave, PW);
+        issue_step(1);
     if (NRAW >= 4 && ntile > 2)
-        issue_tile<KT, VT, D>(lds[2 % NRAW], 2 * TILE, lane, doff, rs, wave, PW);
+        issue_step(2);
     if (KQ || VQ) {
         if (ntile > 1)
             dequant(F(), 0, dq0);
         else
             dequant(Tr(), 0, dq0);
     }
-    // Tiles before t_d lie entirely at or below every row position of this
+    // Steps before t_d lie entirely at or below every row position of this
     // wave and run without mask code.  Every wave still meets the same
-    // barriers, those of ntile tiles.
-    const int t_d = min(ntile, (wave_first + 1) / TILE);
+    // barriers, those of ntile steps.
+    const int t_d = min(ntile, (wave_first + 1) / STEP);
     const int t_a = min(t_d, ntile - 2);
     int t = 0;
     for (; t + 2 <= t_a; t += 2) {
@@ -525,8 +565,8 @@ __global__ __launch_bounds__((64 * Layout<KT, VT, D>::PW)) __attribute__((amdgpu
         body(Tr(), F(), t, dq1, dq0);
         t++;
     }
-    // the last two tiles (with the mask code, which checks at run time
-    // whether a tile needs it)
+    // the last two steps (with the mask code, which checks at run time
+    // whether a step needs it)
     if (ntile >= 2)
         body(Tr(), Tr(), ntile - 2, (ntile & 1) ? dq0 : dq1, (ntile & 1) ? dq1 : dq0);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");

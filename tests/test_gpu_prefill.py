@@ -79,26 +79,36 @@ def test_prefill_group_sizes(G):
     prefill_case("q8_0", "q4_0", S=2, Hq=2 * G, Hkv=2, D=128, T=300, n_tok=61, q_pos0=[239, 100], seed=20 + G)
 
 
-@pytest.mark.parametrize("n_tok,q_pos0", [(1, [0, 37]), (1, [299, 5]), (33, [0, 0]), (200, [0, 100])])
-def test_prefill_chunk_shapes(n_tok, q_pos0):
-    print(f"prefill parity n_tok={n_tok} p0={q_pos0}", flush=True)
-    prefill_case("q8_0", "q4_0", S=2, Hq=32, Hkv=8, D=128, T=300, n_tok=n_tok, q_pos0=q_pos0, seed=n_tok)
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("n_tok,q_pos0", [(1, [0, 37]), (1, [299, 5]), (33, [0, 0]), (200, [0, 100]),
+                                          (32, [0, 32]), (64, [0, 64]), (65, [63, 1])])
+def test_prefill_chunk_shapes(n_tok, q_pos0, D):
+    """Chunks of one query up to several workgroups, starting at position 0
+    or mid-cache; at head_dim 64 (two 32-key tiles per step) the last step
+    may end exactly at a tile or step boundary, or hold one tile wholly
+    past the chunk."""
+    print(f"prefill parity n_tok={n_tok} p0={q_pos0} D={D}", flush=True)
+    prefill_case("q8_0", "q4_0", S=2, Hq=32, Hkv=8, D=D, T=300, n_tok=n_tok, q_pos0=q_pos0, seed=n_tok)
 
 
+@pytest.mark.parametrize("D", [64, 128])
 @pytest.mark.parametrize("kt,vt", [("q8_0", "q4_0"), ("f16", "f16"), ("q4_0", "q8_0"), ("f16", "q4_0"), ("q8_0", "q5_0"), ("q8_0", "turbo3")])
-def test_prefill_ignores_garbage_past_chunk(kt, vt):
+def test_prefill_ignores_garbage_past_chunk(kt, vt, D):
     """Positions after the chunk's last query were never written (all bits
-    set, NaN as binary16): the diagonal tiles must keep them out."""
-    print(f"prefill garbage past chunk {kt}/{vt}", flush=True)
-    prefill_case(kt, vt, S=2, Hq=16, Hkv=2, D=128, T=512, n_tok=50, q_pos0=[150, 131], seed=3, garbage=True)
+    set, NaN as binary16): the diagonal tiles must keep them out (at head_dim
+    64, with two 32-key tiles per step, the last workgroup of sequence 0
+    ends at key 199, so its last step's second tile lies wholly past it)."""
+    print(f"prefill garbage past chunk {kt}/{vt} D={D}", flush=True)
+    prefill_case(kt, vt, S=2, Hq=16, Hkv=2, D=D, T=512, n_tok=50, q_pos0=[150, 131], seed=3, garbage=True)
 
 
+@pytest.mark.parametrize("D", [64, 128])
 @pytest.mark.parametrize("scale", [-0.0883883, 0.0])
-def test_prefill_scale_sign(scale):
+def test_prefill_scale_sign(scale, D):
     """A negative scale (moved onto Q by the kernel) and scale 0 (uniform
     weights over the visible keys; masked keys must still get none)."""
-    print(f"prefill scale {scale}", flush=True)
-    prefill_case("q8_0", "q4_0", S=2, Hq=16, Hkv=2, D=128, T=300, n_tok=40, q_pos0=[200, 9], seed=31, scale=scale)
+    print(f"prefill scale {scale} D={D}", flush=True)
+    prefill_case("q8_0", "q4_0", S=2, Hq=16, Hkv=2, D=D, T=300, n_tok=40, q_pos0=[200, 9], seed=31, scale=scale)
 
 
 def test_prefill_matches_decode_for_one_query():
@@ -162,3 +172,38 @@ def test_llama3_8b_128k_prefill_full_size_sampled():
         ref = orc.attn_prefill(Qb, np.array([p0], np.int32), w.scale, want=want)
         print(assert_attn_close(got[s][np.ix_(toks, heads)], ref[0][np.ix_(toks, heads)], f"{w.name} {name}"),
               flush=True)
+
+
+def test_prefill_head_dim_64_full_size_sampled():
+    """The benchmark's head_dim-64 prefill: 4 sequences x 32768 positions, 32
+    query / 4 kv heads, K8V4, the last 512-query chunk, in the launch
+    configuration it times; sampled (query, head) outputs of one sequence
+    against the oracle."""
+    import torch
+
+    import mixed_precision_quantized_quantize_amd as kvq
+    from mixed_precision_quantized_quantize_amd import synth
+
+    D, hq, hkv, T, S, n_tok = 64, 32, 4, 32768, 4, 512
+    w = synth.Workload(f"prefill_d{D}", 1, hq, hkv, D, T, S, (("q8_0", "q4_0"),), "student_t", 6000 + D,
+                       prefill=n_tok)
+    kt, vt = w.type_pairs[0]
+    print(f"prefill parity D={D} {kt}/{vt} {S} x {n_tok} at the end of {T}", flush=True)
+    cache = kvq.KVCache(1, S, hq, hkv, D, T, (kt, vt))
+    for t0 in range(0, T, 4096):
+        K, V = synth.kv_batch(w, 0, t0, 4096, device="cuda")
+        cache.append(0, K, V, [t0] * S)
+        del K, V
+    Q = synth.queries(w, 0, n_tok=n_tok, device="cuda")
+    got = cache.prefill(0, Q, [T - n_tok] * S, w.scale).cpu().numpy()
+    torch.cuda.synchronize()
+    s = 1
+    orc = oracle.OracleLayer(kt, vt, 1, hq, hkv, D, T)
+    K, V = synth.kv_batch(w, 0, 0, T, device="cuda", seqs=[s])
+    orc.append(bits(K), bits(V), np.zeros(1, np.int32))
+    del K, V
+    toks, heads = [0, 1, 63, 64, 255, 256, 511], [0, 7, 8, 21, 31]
+    want = np.zeros((1, n_tok, hq), np.uint8)
+    want[np.ix_([0], toks, heads)] = 1
+    ref = orc.attn_prefill(bits(Q)[s:s + 1], np.array([T - n_tok], np.int32), w.scale, want=want)
+    print(assert_attn_close(got[s][np.ix_(toks, heads)], ref[0][np.ix_(toks, heads)], f"prefill D={D}"), flush=True)

@@ -7,16 +7,16 @@
 // guide's "Flash Attention" section: tiled, online softmax, exact.
 //
 // Rows are (query token, head of the GQA group) pairs, so all heads that share
-// a kv head share every K/V tile.  A workgroup owns 4 waves x 16*RB rows of
-// one (sequence, kv head) and walks the keys in 32-token tiles; each tile is
-// copied once into LDS (the four waves deal out the copy instructions), its
-// quantized blocks are turned into MFMA operands once for the workgroup (the
-// four waves deal out those jobs too and write the operands back to LDS), and
-// all four waves read them.  The operands of tile t+1 are built while tile t
-// is computed, one barrier per tile, so that each wave's dequantization runs
-// between its MFMAs.  Per wave and tile both contractions run on
-// v_mfma_f32_16x16x32_f16, and every operand is shared by the wave's RB row
-// blocks:
+// a kv head share every K/V tile.  A workgroup owns PW waves x 16*RB rows of
+// one (sequence, kv head) and walks the keys in steps of SUB 32-token tiles
+// (the layout per head_dim and pair is below); each tile is copied once into
+// LDS (the waves deal out the copy instructions), its quantized blocks are
+// turned into MFMA operands once for the workgroup (the waves deal out those
+// jobs too and write the operands back to LDS), and all waves read them.  The
+// operands of step t+1 are built while step t is computed, one barrier per
+// step, so that each wave's dequantization runs between its MFMAs.  Per wave
+// and tile both contractions run on v_mfma_f32_16x16x32_f16, and every
+// operand is shared by the wave's RB row blocks:
 //   S^T[key][row]  = K[key][c] . Q^T[c][row]
 //       A quantized K block enters as two binary16 operands hi + lo with
 //       hi = fl16(code * d), lo = fl16(code * d - hi) (one fused multiply-add),
@@ -51,28 +51,37 @@ __device__ inline __attribute__((always_inline)) void static_for_pf(F &&f)
     }
 }
 
-// Rows and waves of a workgroup.  At head_dim <= 128: four waves of two
-// 16-row blocks; a wave then fits in 256 registers and two workgroups share
-// each CU (one wave's softmax runs beside another's MFMAs).  At 256 with a
-// quantized half: eight waves of one row block, two waves per SIMD in one
-// workgroup per CU (measured 36% faster for K8V4 than four waves of two
-// blocks, whose 448-register waves ran alone on their SIMDs, the
-// dequantization and the MFMAs largely one after the other).  f16/f16 at
-// 256 keeps four waves of two blocks: with one block per wave it spilled.
+// Rows, waves and step length of a workgroup.  Waves of two 16-row blocks
+// fit in 256 registers, two waves per SIMD: at head_dim 128 eight of them
+// in one workgroup per CU; at 64 eight (quantized values) or four in each of
+// two workgroups per CU (binary16 values).  At 256 with a quantized half:
+// eight waves of one row block, two waves per SIMD in one workgroup per CU
+// (measured 36% faster for K8V4 than four waves of two blocks, whose
+// 448-register waves ran alone on their SIMDs, the dequantization and the
+// MFMAs largely one after the other).  f16/f16 at 256 keeps four waves of two
+// blocks: with one block per wave it spilled.
 // This file is compiled with the MFMA accumulators in VGPRs
 // (-amdgpu-mfma-vgpr-form): the online-softmax rescale touches them with
 // vector instructions, and with AGPR accumulators the compiler copied them
 // between the two register files on every tile.
 template <int KT, int VT, int D> struct Layout {
     static constexpr bool ONE = D == 256 && !(KT == KVQ_F16 && VT == KVQ_F16);
+    // head_dim 64 with quantized values: eight waves, four tiles per step
+    static constexpr bool W8_64 = D == 64 && VT != KVQ_F16;
     static constexpr int RB = ONE ? 1 : 2;  // 16-row blocks per wave
-    static constexpr int PW = ONE ? 8 : 4;  // waves per workgroup
+    static constexpr int PW = ONE || D == 128 || W8_64 ? 8 : 4;  // waves per workgroup
     static constexpr int WPE = D <= 128 || ONE ? 2 : 1;  // waves per SIMD the registers allow
-    // 32-key tiles per step (one barrier, one softmax update): two at head_dim
-    // 64, where a tile's matrix work is half that of 128 but its barrier,
-    // waits, row maxima and rescale check cost the same; the step then holds
-    // as many bytes and operands as a tile at 128
-    static constexpr int SUB = D == 64 ? 2 : 1;
+    // 32-key tiles per step (one barrier, one softmax update).  A step's
+    // barrier, copy waits, row maxima and rescale check cost the same
+    // whatever its length, so longer steps spread them over more matrix work;
+    // the step's raw tiles and operands must fit the LDS.  Head_dim 128: two
+    // tiles, whose operands need the whole LDS (one workgroup of eight waves
+    // per CU).  Head_dim 64: four tiles and eight waves where the values are
+    // quantized, the same LDS; two tiles and two workgroups of four waves per
+    // CU for binary16 values (with four tiles their raw operands spilled
+    // registers).
+    static constexpr int SUB = D == 64 ? (W8_64 ? 4 : 2) : D == 128 ? 2 : 1;
+    static constexpr int LDS_KB = D == 64 && !W8_64 ? 80 : 160;  // LDS budget of a workgroup
 };
 
 __device__ inline half8 splat8(uint32_t pair) { return pack4(pair, pair, pair, pair); }
@@ -110,7 +119,7 @@ __global__ __launch_bounds__((64 * Layout<KT, VT, D>::PW)) __attribute__((amdgpu
     // and t+3 with four, which every pair gets where they fit beside the
     // operand arrays at the workgroups per CU the kernel is built for (two at
     // head_dim <= 128, one at 256)
-    constexpr int LDS_WG = (D <= 128 ? 80 : 160) * 1024;
+    constexpr int LDS_WG = Layout<KT, VT, D>::LDS_KB * 1024;
     constexpr int NRAW = 4 * SUB * g::BYTES + 2 * (DQ_BYTES > 0 ? DQ_BYTES : 16) <= LDS_WG ? 4 : 3;
     __shared__ __attribute__((aligned(16))) uint8_t lds[NRAW][SUB * g::BYTES];
 
@@ -317,10 +326,13 @@ __global__ __launch_bounds__((64 * Layout<KT, VT, D>::PW)) __attribute__((amdgpu
         constexpr bool DG = decltype(diag_c)::value;
         const uint8_t *buf = lds[t % NRAW];
         const int tb = t * STEP;
-        // raw f16 operands (no dequantization) stay in the raw tiles
+        // raw f16 operands (no dequantization) stay in the raw tiles.  With
+        // two tiles per step they are read where they are used (read up
+        // front, both tiles' operands would not fit the registers).
+        constexpr bool LATE = SUB == 2;
         u32x4 kop[SUB][2][NB];
         u32x4 vop[SUB][VL];
-        if (!KQ) {
+        if (!KQ && !LATE) {
 #pragma unroll
             for (int u = 0; u < SUB; u++)
 #pragma unroll
@@ -329,7 +341,18 @@ __global__ __launch_bounds__((64 * Layout<KT, VT, D>::PW)) __attribute__((amdgpu
                     for (int b = 0; b < NB; b++)
                         kop[u][T][b] = *reinterpret_cast<const u32x4 *>(buf + u * g::BYTES + k_rd[T][b]);
         }
-        if (!VQ) {
+        // keys at or past key_end in binary16 V tiles: values forced to +0
+        uint32_t vkm[SUB][4];
+        if (!VQ && LATE && DG) {
+#pragma unroll
+            for (int u = 0; u < SUB; u++)
+#pragma unroll
+                for (int i = 0; i < 4; i++) {
+                    const int k0 = tb + TILE * u + 8 * j + 2 * i;
+                    vkm[u][i] = (k0 < key_end ? 0x0000FFFFu : 0u) | (k0 + 1 < key_end ? 0xFFFF0000u : 0u);
+                }
+        }
+        if (!VQ && !LATE) {
 #pragma unroll
             for (int u = 0; u < SUB; u++) {
 #pragma unroll
@@ -374,7 +397,7 @@ __global__ __launch_bounds__((64 * Layout<KT, VT, D>::PW)) __attribute__((amdgpu
                 for (int b = 0; b < NB; b++) {
                     const int x = 2 * u + T;
                     if (KT == KVQ_F16) {
-                        const u32x4 w = kop[u][T][b];
+                        const u32x4 w = LATE ? *reinterpret_cast<const u32x4 *>(buf + u * g::BYTES + k_rd[T][b]) : kop[u][T][b];
                         const half8 ka = pack4(w.x, w.y, w.z, w.w);
 #pragma unroll
                         for (int rb = 0; rb < RB; rb++)
@@ -411,8 +434,11 @@ __global__ __launch_bounds__((64 * Layout<KT, VT, D>::PW)) __attribute__((amdgpu
                         sc[x] = -INFINITY;
             }
             float mt = max3(max3(sc[0], sc[1], sc[2]), max3(sc[3], sc[4], sc[5]), max3(sc[6], sc[7], sc[7]));
-            if constexpr (SUB == 2)
-                mt = max3(mt, max3(max3(sc[8], sc[9], sc[10]), max3(sc[11], sc[12], sc[13]), sc[14]), sc[15]);
+#pragma unroll
+            for (int u = 1; u < SUB; u++) {
+                const float *q = sc + 8 * u;
+                mt = max3(mt, max3(max3(q[0], q[1], q[2]), max3(q[3], q[4], q[5]), q[6]), q[7]);
+            }
             mt = max_lane_groups(mt) * c2a;  // NaN only for a fully masked row at scale 0: no update
             if (__any(mt > m_run[rb])) {
                 const float m_new = fmaxf(m_run[rb], mt);
@@ -457,7 +483,14 @@ __global__ __launch_bounds__((64 * Layout<KT, VT, D>::PW)) __attribute__((amdgpu
                 } else {
 #pragma unroll
                     for (int hh = 0; hh < 2; hh++) {
-                        const u32x4 w = vop[u][2 * b + hh];
+                        u32x4 w;
+                        if (LATE) {
+                            w = *reinterpret_cast<const u32x4 *>(buf + u * g::BYTES + v_rd[2 * b + hh]);
+                            if (DG)
+                                w = u32x4{w.x & vkm[u][0], w.y & vkm[u][1], w.z & vkm[u][2], w.w & vkm[u][3]};
+                        } else {
+                            w = vop[u][2 * b + hh];
+                        }
                         va[hh] = pack4(w.x, w.y, w.z, w.w);
                     }
                 }

@@ -22,6 +22,10 @@
 //       block's K scale multiplies the MFMA result per token;
 //   O^T[chan][head] += V^T[chan][token] . P'[token][head]  -- one MFMA per 16
 //       channels and 32 tokens; P' = binary16(p) * V scale of (token, block).
+// q8_0 and q4_0 codes enter both products as binary16 subnormals (a mask or
+// byte permute of the stored bits, no per-element arithmetic); their offset
+// comes off per block, through the score MFMA's accumulator input for keys
+// and one more MFMA against a constant operand for values.
 // The score layout of the first product is exactly the operand layout of the
 // second, so probabilities never leave registers.  The V plane stores 8
 // tokens interleaved, so a lane's P.V operand (8 tokens of one channel) is
@@ -211,7 +215,16 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(D <=
     // Q^T operand: lane (n = head, j) holds 8 channels of each block (the
     // channels qk_chan picks: 8j.. for f16/q8_0, 4j.. and 16+4j.. for q4_0);
     // buffer loads from the scalar base of the pair's Q rows
+    //
+    // q8_0 and q4_0 keys are subnormal operands (kvq_device.h): the score
+    // MFMA of block b then starts from kofs[b] = -offset * 2^-24 * (sum of
+    // head n's query over the block's 32 channels), which removes the codes'
+    // offset exactly where the raw sum of the MFMA has it, and the scores
+    // come out in units of 2^-24 (folded into c2).  q4_0 slots 4..7 hold the
+    // high nibbles as 16 c: their query channels are q / 16.
+    constexpr bool KSUB = KT == KVQ_Q8_0 || KT == KVQ_Q4_0;
     half8 qb[NB];
+    floatx4 kofs[KSUB ? NB : 1];
     {
         const __amdgpu_buffer_rsrc_t rq =
             make_rsrc(reinterpret_cast<const _Float16 *>(a.q) + ((int64_t)s * a.Hq + (int64_t)h * G) * D, G * D * 2);
@@ -231,7 +244,7 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(D <=
             }
         }
     }
-    const float c2 = a.c2;
+    const float c2 = KSUB ? a.c2 * TWO_P24 : a.c2;
 
     DmaOffsets<KT, VT, D> doff;
     doff.init(lane);
@@ -352,17 +365,16 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(D <=
                     const u32x4 w = op.k[T][b];
                     ka = pack4(w.x, w.y, w.z, w.w);
                 } else if constexpr (KT == KVQ_Q8_0) {
-                    ka = deq_q8(op.k[T][b].x, op.k[T][b].y);
+                    ka = deq_q8_sub(op.k[T][b].x, op.k[T][b].y);
                 } else if constexpr (KT == KVQ_Q4_0) {
-                    const uint32_t w = op.k[T][b].x;
-                    ka = k_operand<KVQ_Q4_0>(&w);
+                    ka = k_operand_q4_sub(op.k[T][b].x);
                 } else {
                     ka = k_operand_q5(op.k[T][b].x, op.kh[T][b], 4 * j);
                 }
                 if (KT == KVQ_F16) {
                     sacc[T] = mfma(ka, qb[b], sacc[T]);
                 } else {
-                    const floatx4 c = mfma(ka, qb[b], floatx4{0.0f, 0.0f, 0.0f, 0.0f});
+                    const floatx4 c = mfma(ka, qb[b], KSUB ? kofs[KSUB ? b : 0] : floatx4{0.0f, 0.0f, 0.0f, 0.0f});
 #pragma unroll
                     for (int i = 0; i < 4; i++)
                         sacc[T][i] = __builtin_fmaf(half_at(ksc, (4 * T + i) * NB + b), c[i], sacc[T][i]);
@@ -433,15 +445,14 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(D <=
             }
             if constexpr (VT == KVQ_Q4_0) {
                 // bytes of tokens 0..3 (word 0) and 4..7 (word 1); low nibbles feed
-                // channel tile 2b, high nibbles tile 2b+1
-                const u32x4 w = op.v[b];
-                uint32_t l01, h01, l23, h23, l45, h45, l67, h67;
-                deq_q4_pair(__builtin_amdgcn_perm(w.x, w.x, 0x0C010C00u), l01, h01);
-                deq_q4_pair(__builtin_amdgcn_perm(w.x, w.x, 0x0C030C02u), l23, h23);
-                deq_q4_pair(__builtin_amdgcn_perm(w.y, w.y, 0x0C010C00u), l45, h45);
-                deq_q4_pair(__builtin_amdgcn_perm(w.y, w.y, 0x0C030C02u), l67, h67);
-                o[2 * b] = mfma(pack4(l01, l23, l45, l67), pb, o[2 * b]);
-                o[2 * b + 1] = mfma(pack4(h01, h23, h45, h67), pb, o[2 * b + 1]);
+                // channel tile 2b (c * 2^-24), high nibbles tile 2b+1 (16 c *
+                // 2^-24); the offset 8 (16 * 8) comes off by one more MFMA each
+                half8 va0, va1;
+                v_operand_q4_sub(u32x2{op.v[b].x, op.v[b].y}, va0, va1);
+                o[2 * b] = mfma(va0, pb, o[2 * b]);
+                o[2 * b + 1] = mfma(va1, pb, o[2 * b + 1]);
+                o[2 * b] = mfma(pack4(SUB_NEG8, SUB_NEG8, SUB_NEG8, SUB_NEG8), pb, o[2 * b]);
+                o[2 * b + 1] = mfma(pack4(SUB_NEG128, SUB_NEG128, SUB_NEG128, SUB_NEG128), pb, o[2 * b + 1]);
             } else if constexpr (VT == KVQ_Q5_0) {
                 // as q4_0, each code's fifth bit from its token's high-bit word
                 half8 va0, va1;
@@ -464,9 +475,14 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(D <=
                     if (VT == KVQ_F16) {
                         va = pack4(w.x, w.y, w.z, w.w);  // masked tokens' values are +0 (tail tile)
                     } else {
-                        va = deq_q8(w.x, w.y);
+                        va = deq_q8_sub(w.x, w.y);  // (c + 128) * 2^-24
                     }
                     o[ct] = mfma(va, pb, o[ct]);
+                }
+                if (VT == KVQ_Q8_0) {
+#pragma unroll
+                    for (int hh = 0; hh < 2; hh++)
+                        o[2 * b + hh] = mfma(pack4(SUB_NEG128, SUB_NEG128, SUB_NEG128, SUB_NEG128), pb, o[2 * b + hh]);
                 }
             }
         }
@@ -513,6 +529,30 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(D <=
         if (u < n_mine)
             issue_tile<KT, VT, D, CPOL_STREAM>(lds_t[u] + wave * g::BYTES, (r + u * k) * TILE, lane, doff, rs);
     });
+    // the query operands' block sums and slot order (see where qb is loaded),
+    // once the first copies are on their way
+    if constexpr (KSUB) {
+#pragma unroll
+        for (int b = 0; b < NB; b++) {
+            float qs = 0.0f;  // the lane's 8 channels, then the four lane groups
+#pragma unroll
+            for (int r = 0; r < 8; r++)
+                qs += (float)qb[b][r];
+            qs += __shfl_xor(qs, 16);
+            qs += __shfl_xor(qs, 32);
+            const float o = (KT == KVQ_Q8_0 ? -128.0f : -8.0f) * TWO_M24 * qs;
+            kofs[b] = floatx4{o, o, o, o};
+            if constexpr (KT == KVQ_Q4_0) {
+                // slots: elements 4j, 4j+2, 4j+1, 4j+3, then the high
+                // nibbles' 16+4j, ... scaled by 1/16
+                const u32x4 w = __builtin_bit_cast(u32x4, qb[b]);
+                const half2 k16 = {(_Float16)0.0625f, (_Float16)0.0625f};
+                qb[b] = pack4(__builtin_amdgcn_perm(w.y, w.x, 0x05040100u), __builtin_amdgcn_perm(w.y, w.x, 0x07060302u),
+                              h2_bits(bits_h2(__builtin_amdgcn_perm(w.w, w.z, 0x05040100u)) * k16),
+                              h2_bits(bits_h2(__builtin_amdgcn_perm(w.w, w.z, 0x07060302u)) * k16));
+            }
+        }
+    }
     int i = 0;
     for (; i + NBUF <= n_mine; i += NBUF)
         static_for<NBUF>([&](auto u) { step(lds_t[u] + wave * g::BYTES, i + u); });
@@ -522,6 +562,15 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(D <=
             i++;
         }
     });
+
+    // Subnormal value operands: O back to its units (q8_0: 2^24; q4_0: 2^24
+    // for the low nibbles' channel tiles 2b, 2^20 for the high nibbles' tiles
+    // 2b+1, which summed 16 c).
+    if constexpr (VT == KVQ_Q8_0 || VT == KVQ_Q4_0) {
+#pragma unroll
+        for (int ct = 0; ct < NCT; ct++)
+            o[ct] *= (VT == KVQ_Q4_0 && (ct & 1)) ? 1048576.0f : TWO_P24;
+    }
 
     // ---------------- merge the workgroup's four partials in LDS.  Lane
     // (n, j) holds head n's running max m_run (base 2, equal in the four lane

@@ -672,24 +672,45 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(D <=
     float *const mrg_w = reinterpret_cast<float *>(lds_a);  // the workgroup merge's data is no longer read
     float *const mrg_l = mrg_w + MERGE_SLOTS;
     auto slot_ptr = [&](int jj) { return slots + (int64_t)(slot0 + jj * slot_step) * SL; };
-    for (int e = t; e < nw; e += 64 * WAVES) {
-        const int jj = e / G, gg = e - jj * G;
-        const float *p = slot_ptr(jj) + gg * (D + 4) + D;
-        mrg_w[e] = __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        mrg_l[e] = __hip_atomic_load(p + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    // One thread per (slot, head) entry e = jj * G + gg (at most EPT per
+    // thread): its weight 2^(m_e - M_gg) and its scaled sum l_e * weight, all
+    // entries at once -- no thread walks the slots one dependent LDS read
+    // after another.
+    constexpr int EPT = (MERGE_SLOTS + 64 * WAVES - 1) / (64 * WAVES);
+    float me[EPT], le[EPT];
+#pragma unroll
+    for (int u = 0; u < EPT; u++) {
+        const int e = t + u * 64 * WAVES;
+        if (e < nw) {
+            const int jj = e / G, gg = e - jj * G;
+            const float *p = slot_ptr(jj) + gg * (D + 4) + D;
+            me[u] = __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            le[u] = __hip_atomic_load(p + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            mrg_w[e] = me[u];
+        }
     }
     __syncthreads();
-    if (t < G) {
-        float Mg = mrg_w[t];
-        for (int jj = 1; jj < kw; jj++)
-            Mg = fmaxf(Mg, mrg_w[jj * G + t]);
-        float Lg = 0.0f;
-        for (int jj = 0; jj < kw; jj++) {
-            const float w = __builtin_amdgcn_exp2f(mrg_w[jj * G + t] - Mg);
-            mrg_w[jj * G + t] = w;
-            Lg += mrg_l[jj * G + t] * w;
+#pragma unroll
+    for (int u = 0; u < EPT; u++) {
+        const int e = t + u * 64 * WAVES;
+        if (e < nw) {
+            const int gg = e % G;
+            float M = mrg_w[gg];
+#pragma unroll 8
+            for (int jj = 1; jj < kw; jj++)
+                M = fmaxf(M, mrg_w[jj * G + gg]);
+            me[u] = __builtin_amdgcn_exp2f(me[u] - M);
+            le[u] *= me[u];
         }
-        mrg_l[t] = Lg;  // slot 0's sums are no longer needed
+    }
+    __syncthreads();  // every maximum is read before the weights replace the maxima
+#pragma unroll
+    for (int u = 0; u < EPT; u++) {
+        const int e = t + u * 64 * WAVES;
+        if (e < nw) {
+            mrg_w[e] = me[u];
+            mrg_l[e] = le[u];
+        }
     }
     __syncthreads();
     // Outputs in quads of channels: thread t sums channels 4q .. 4q+3 of one
@@ -706,6 +727,10 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(D <=
         const int off = 4 * (gg * (D + 4) + c);
         floatx4 sum = {0.0f, 0.0f, 0.0f, 0.0f};
         if (live) {
+            float L = 0.0f;  // the head's sum over the slots, in slot order
+#pragma unroll 8
+            for (int j2 = 0; j2 < kw; j2++)
+                L += mrg_l[j2 * G + gg];
             int jj = 0;
             for (; jj + 16 <= kw; jj += 16) {  // sixteen loads in flight, summed in slot order
                 floatx4 v[16];
@@ -720,7 +745,7 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(D <=
             for (; jj < kw; jj++)
                 sum += __builtin_bit_cast(floatx4, __builtin_amdgcn_raw_buffer_load_b128(slot_rsrc(jj), off, 0, CPOL_SC1)) *
                        mrg_w[jj * G + gg];
-            sum *= 1.0f / mrg_l[gg];
+            sum *= 1.0f / L;
         }
         if constexpr (VT == KVQ_TURBO3)
             sum = rotate_back_quad(sum, c);

@@ -22,7 +22,7 @@ PAIRS = list(itertools.product(["f16", "q8_0", "q4_0", "q5_0"], repeat=2))
 PAIRS += [(k, "turbo3") for k in ["f16", "q8_0", "q4_0", "q5_0"]]  # turbo3 stores values only
 
 
-def small_case(kt, vt, S, Hq, Hkv, D, T, ctx, n_splits_list, seed, kscale=3.0, scale=None):
+def small_case(kt, vt, S, Hq, Hkv, D, T, ctx, n_splits_list, seed, kscale=3.0, scale=None, q=None):
     import torch
 
     import mixed_precision_quantized_quantize_amd as kvq
@@ -33,7 +33,7 @@ def small_case(kt, vt, S, Hq, Hkv, D, T, ctx, n_splits_list, seed, kscale=3.0, s
     orc = oracle.OracleLayer(kt, vt, S, Hq, Hkv, D, T)
     K = torch.from_numpy((rng.standard_t(4, (S, T, Hkv, D)) * kscale).astype(np.float16)).cuda()
     V = torch.from_numpy(rng.standard_normal((S, T, Hkv, D)).astype(np.float16)).cuda()
-    Q = torch.from_numpy(rng.standard_normal((S, Hq, D)).astype(np.float16)).cuda()
+    Q = torch.from_numpy(rng.standard_normal((S, Hq, D)).astype(np.float16) if q is None else q).cuda()
     cache.append(0, K, V, [0] * S)
     orc.append(bits(K), bits(V), np.zeros(S, np.int32))
     scale = 1.0 / np.sqrt(D) if scale is None else scale
@@ -62,6 +62,28 @@ def test_decode_scale_sign(kt, vt, scale):
     print(f"decode scale {scale} {kt}/{vt}", flush=True)
     small_case(kt, vt, S=3, Hq=16, Hkv=2, D=128, T=333, ctx=[333, 70, 5], n_splits_list=[0, 3, 8], seed=41,
                scale=scale)
+
+
+@pytest.mark.parametrize("kt,vt", [("q8_0", "q4_0"), ("q4_0", "q4_0"), ("q4_0", "q8_0"), ("q8_0", "q8_0")])
+def test_decode_query_dynamic_range(kt, vt):
+    """q8_0 and q4_0 keys enter the score product as binary16 subnormals with
+    the codes' offset removed through the block sum of the query, and the
+    high nibbles' query channels are divided by 16.  Queries whose channel
+    magnitudes spread log-uniformly over 2^-24 .. 2^2 (many of them binary16
+    subnormals, or subnormal once divided by 16), with a head of zeros, one
+    of all-tiny and one of one-signed values (a block sum as large as it
+    gets), must still match the oracle."""
+    print(f"decode query range {kt}/{vt}", flush=True)
+    rng = np.random.default_rng(5)
+    S, Hq, Hkv, D = 2, 16, 2, 128
+    mag = np.exp2(rng.uniform(-24, 2, (S, Hq, D)))
+    q = mag * rng.choice([-1.0, 1.0], (S, Hq, D))
+    q[0, 0] = 0.0
+    q[0, 1] = np.exp2(rng.uniform(-24, -14, D))
+    q[1, 2] = np.abs(q[1, 2]) + 0.5
+    for D_ in (64, 128):
+        qq = q[:, :, :D_].astype(np.float16)
+        small_case(kt, vt, S=S, Hq=Hq, Hkv=Hkv, D=D_, T=300, ctx=[300, 45], n_splits_list=[0, 3], seed=11, q=qq)
 
 
 @pytest.mark.parametrize("kt,vt", [("q8_0", "q4_0"), ("f16", "f16"), ("q4_0", "q8_0"), ("q5_0", "q5_0"), ("q8_0", "q5_0"), ("q8_0", "turbo3")])
@@ -175,7 +197,7 @@ def _decode_setup(S=4, Hq=32, Hkv=8, D=128, T=4096, seed=5):
     cache = kvq.KVCache(1, S, Hq, Hkv, D, T, ("q8_0", "q4_0"))
     K = torch.from_numpy((rng.standard_t(4, (S, T, Hkv, D)) * 3).astype(np.float16)).cuda()
     V = torch.from_numpy(rng.standard_normal((S, T, Hkv, D)).astype(np.float16)).cuda()
-    Q = torch.from_numpy(rng.standard_normal((S, Hq, D)).astype(np.float16)).cuda()
+    Q = torch.from_numpy(rng.standard_normal((S, Hq, D)).astype(np.float16) if q is None else q).cuda()
     cache.append(0, K, V, [0] * S)
     return cache, K, V, Q
 

@@ -68,52 +68,6 @@ __device__ inline void deq_q4_pair(uint32_t y, uint32_t &lo, uint32_t &hi)
     hi = h2_bits(__builtin_elementwise_fma(bits_h2(bfi(0x00F000F0u, y, e)), k16, k72));
 }
 
-// ---- Subnormal operands (decode).  The matrix core multiplies binary16
-// subnormals exactly (checked on gfx950: every product and sum of a
-// 16x16x32 MFMA with subnormal inputs on either side within 2^-23 of the
-// exact sum), so a code u < 1024 whose bits sit in a half as the bare integer
-// is the binary16 value u * 2^-24: no exponent pattern to insert and no
-// offset to subtract per element.  The code's offset (+128 for q8_0 once its
-// sign bit is flipped, +8 for q4_0) is taken out per block instead -- for
-// keys through the score MFMA's accumulator input, for values by one more
-// MFMA of the same probabilities against a constant operand -- and the 2^-24
-// is folded into the softmax scale (keys) or into the output (values).
-constexpr float TWO_M24 = 5.9604644775390625e-08f;  // 2^-24
-constexpr float TWO_P24 = 16777216.0f;              // 2^24
-constexpr uint32_t SUB_NEG8 = 0x80088008u;           // binary16 pair (-8 * 2^-24, -8 * 2^-24)
-constexpr uint32_t SUB_NEG128 = 0x80808080u;         // binary16 pair (-128 * 2^-24, -128 * 2^-24)
-
-// 8 int8 codes c -> binary16 (c + 128) * 2^-24, exact: the sign bit flipped,
-// each byte alone in a half.
-__device__ inline half8 deq_q8_sub(uint32_t w0, uint32_t w1)
-{
-    const uint32_t x0 = w0 ^ 0x80808080u, x1 = w1 ^ 0x80808080u;
-    return pack4(__builtin_amdgcn_perm(0u, x0, 0x0C010C00u), __builtin_amdgcn_perm(0u, x0, 0x0C030C02u),
-                 __builtin_amdgcn_perm(0u, x1, 0x0C010C00u), __builtin_amdgcn_perm(0u, x1, 0x0C030C02u));
-}
-
-// q4_0 K codes of one block for one lane: w = code bytes 4j..4j+3 of the
-// token's row (byte k: element 4j+k in the low nibble, 16+4j+k in the high)
-// -> k-slots 0..3 = elements 4j, 4j+2, 4j+1, 4j+3 as c * 2^-24 and k-slots
-// 4..7 = elements 16+4j, 16+4j+2, 16+4j+1, 16+4j+3 as 16 c * 2^-24 (the high
-// nibble left in place; the query channels of those slots carry q / 16).
-__device__ inline half8 k_operand_q4_sub(uint32_t w)
-{
-    const uint32_t w8 = w >> 8;
-    return pack4(w & 0x000F000Fu, w8 & 0x000F000Fu, w & 0x00F000F0u, w8 & 0x00F000F0u);
-}
-
-// q4_0 V codes of one block for one lane: code byte n of tokens 0..3 (w.x)
-// and 4..7 (w.y) -> the operand of element n (low nibbles, c * 2^-24) and of
-// element n+16 (high nibbles, 16 c * 2^-24), tokens in order.
-__device__ inline void v_operand_q4_sub(u32x2 w, half8 &va0, half8 &va1)
-{
-    const uint32_t y01 = __builtin_amdgcn_perm(w.x, w.x, 0x0C010C00u), y23 = __builtin_amdgcn_perm(w.x, w.x, 0x0C030C02u);
-    const uint32_t y45 = __builtin_amdgcn_perm(w.y, w.y, 0x0C010C00u), y67 = __builtin_amdgcn_perm(w.y, w.y, 0x0C030C02u);
-    va0 = pack4(y01 & 0x000F000Fu, y23 & 0x000F000Fu, y45 & 0x000F000Fu, y67 & 0x000F000Fu);
-    va1 = pack4(y01 & 0x00F000F0u, y23 & 0x00F000F0u, y45 & 0x00F000F0u, y67 & 0x00F000F0u);
-}
-
 // max over the four lanes n, n+16, n+32, n+48 (the lane groups of one score
 // row) with two lane swaps, no LDS round trip.
 __device__ inline float max_lane_groups(float v)

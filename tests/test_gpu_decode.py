@@ -197,7 +197,7 @@ def _decode_setup(S=4, Hq=32, Hkv=8, D=128, T=4096, seed=5):
     cache = kvq.KVCache(1, S, Hq, Hkv, D, T, ("q8_0", "q4_0"))
     K = torch.from_numpy((rng.standard_t(4, (S, T, Hkv, D)) * 3).astype(np.float16)).cuda()
     V = torch.from_numpy(rng.standard_normal((S, T, Hkv, D)).astype(np.float16)).cuda()
-    Q = torch.from_numpy(rng.standard_normal((S, Hq, D)).astype(np.float16) if q is None else q).cuda()
+    Q = torch.from_numpy(rng.standard_normal((S, Hq, D)).astype(np.float16)).cuda()
     cache.append(0, K, V, [0] * S)
     return cache, K, V, Q
 

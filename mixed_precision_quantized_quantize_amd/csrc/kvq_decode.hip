@@ -258,11 +258,12 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(D <=
     if (has_bit_words(VT))
         rs.vh = make_rsrc(a.vqh + pair * Tc * NB, Tc * NB * 4);
 
-    // Q^T operand: lane (n = head, j) holds 8 channels of each block (the
-    // channels qk_chan picks: 8j.. for f16/q8_0, 4j.. and 16+4j.. for q4_0);
-    // buffer loads from the scalar base of the pair's Q rows
+    // Q^T operand: lane (n = head, j) holds 8 channels of each block (8j..
+    // for f16/q8_0; 4j.. and 16+4j.. for q4_0 and q5_0, the q4_0 slots
+    // reordered below to match k_operand_q4_sub); buffer loads from the
+    // scalar base of the pair's Q rows
     //
-    // q8_0 and q4_0 keys are subnormal operands (kvq_device.h): the score
+    // q8_0 and q4_0 keys are subnormal operands (the helpers above): the score
     // MFMA of block b then starts from kofs[b] = -offset * 2^-24 * (sum of
     // head n's query over the block's 32 channels), which removes the codes'
     // offset exactly where the raw sum of the MFMA has it, and the scores

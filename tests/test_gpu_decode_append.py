@@ -74,7 +74,7 @@ def test_decode_append_pairs(kt, vt):
 
 
 @pytest.mark.parametrize("D", [64, 256])
-@pytest.mark.parametrize("kt,vt", [("q8_0", "q4_0"), ("f16", "q8_0"), ("q4_0", "f16"), ("q5_0", "q5_0"), ("q8_0", "turbo3")])
+@pytest.mark.parametrize("kt,vt", [("q8_0", "q4_0"), ("f16", "q8_0"), ("q4_0", "f16"), ("q5_0", "q5_0"), ("q8_0", "turbo3"), ("q4_0", "q4_0"), ("q8_0", "q8_0")])
 def test_decode_append_head_dims(kt, vt, D):
     fused_case(kt, vt, S=2, Hq=8, Hkv=2, D=D, T=200, ctx=[64, 200], splits=[0, 2, 7], seed=D)
 

@@ -129,6 +129,18 @@ __device__ inline void v_operand_q4_sub(u32x2 w, half8 &va0, half8 &va1)
     va1 = pack4(y01 & 0x00F000F0u, y23 & 0x00F000F0u, y45 & 0x00F000F0u, y67 & 0x00F000F0u);
 }
 
+// q5_0 K fifth bits of one block for one lane as a second subnormal operand:
+// x = the (token, block) high-bit word (bit e: element e), j = lane group.
+// Rotated right by 4j - 4, bits 4j+k and 16+4j+k land at bits 4+k and 20+k,
+// so word k keeps them: k-slots 2k, 2k+1 = elements 4j+k, 16+4j+k with value
+// 2^(4+k) * 2^-24 where the bit is set.  Their query channels carry
+// q * 2^-k, which makes each set bit count 16 (the fifth bit's weight).
+__device__ inline half8 k_operand_q5_fifth(uint32_t x, int j)
+{
+    const uint32_t y = __builtin_amdgcn_alignbit(x, x, (uint32_t)(4 * j - 4) & 31u);
+    return pack4(y & 0x00100010u, y & 0x00200020u, y & 0x00400040u, y & 0x00800080u);
+}
+
 // Cache policy bit of a device-coherent (agent-scope) access: sc1.
 constexpr int CPOL_SC1 = 16;
 
@@ -263,15 +275,18 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(D <=
     // reordered below to match k_operand_q4_sub); buffer loads from the
     // scalar base of the pair's Q rows
     //
-    // q8_0 and q4_0 keys are subnormal operands (the helpers above): the score
-    // MFMA of block b then starts from kofs[b] = -offset * 2^-24 * (sum of
-    // head n's query over the block's 32 channels), which removes the codes'
-    // offset exactly where the raw sum of the MFMA has it, and the scores
-    // come out in units of 2^-24 (folded into c2).  q4_0 slots 4..7 hold the
-    // high nibbles as 16 c: their query channels are q / 16.
-    constexpr bool KSUB = KT == KVQ_Q8_0 || KT == KVQ_Q4_0;
+    // q8_0, q4_0 and q5_0 keys are subnormal operands (the helpers above):
+    // the score MFMA of block b then starts from kofs[b] = -offset * 2^-24 *
+    // (sum of head n's query over the block's 32 channels), which removes the
+    // codes' offset exactly where the raw sum of the MFMA has it, and the
+    // scores come out in units of 2^-24 (folded into c2).  q4_0 and q5_0
+    // slots 4..7 hold the high nibbles as 16 c: their query channels are
+    // q / 16.  q5_0's fifth bits enter through a second MFMA against qb5.
+    constexpr bool KSUB = KT == KVQ_Q8_0 || KT == KVQ_Q4_0 || KT == KVQ_Q5_0;
+    constexpr bool K5 = KT == KVQ_Q5_0;
     half8 qb[NB];
     floatx4 kofs[KSUB ? NB : 1];
+    half8 qb5[K5 ? NB : 1];
     {
         const __amdgpu_buffer_rsrc_t rq =
             make_rsrc(reinterpret_cast<const _Float16 *>(a.q) + ((int64_t)s * a.Hq + (int64_t)h * G) * D, G * D * 2);
@@ -416,12 +431,14 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(D <=
                 } else if constexpr (KT == KVQ_Q4_0) {
                     ka = k_operand_q4_sub(op.k[T][b].x);
                 } else {
-                    ka = k_operand_q5(op.k[T][b].x, op.kh[T][b], 4 * j);
+                    ka = k_operand_q4_sub(op.k[T][b].x);  // the nibbles; the fifth bits below
                 }
                 if (KT == KVQ_F16) {
                     sacc[T] = mfma(ka, qb[b], sacc[T]);
                 } else {
-                    const floatx4 c = mfma(ka, qb[b], KSUB ? kofs[KSUB ? b : 0] : floatx4{0.0f, 0.0f, 0.0f, 0.0f});
+                    floatx4 c = mfma(ka, qb[b], KSUB ? kofs[KSUB ? b : 0] : floatx4{0.0f, 0.0f, 0.0f, 0.0f});
+                    if constexpr (K5)
+                        c = mfma(k_operand_q5_fifth(op.kh[T][b], j), qb5[K5 ? b : 0], c);
 #pragma unroll
                     for (int i = 0; i < 4; i++)
                         sacc[T][i] = __builtin_fmaf(half_at(ksc, (4 * T + i) * NB + b), c[i], sacc[T][i]);
@@ -587,9 +604,19 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(D <=
                 qs += (float)qb[b][r];
             qs += __shfl_xor(qs, 16);
             qs += __shfl_xor(qs, 32);
-            const float o = (KT == KVQ_Q8_0 ? -128.0f : -8.0f) * TWO_M24 * qs;
+            const float o = (KT == KVQ_Q8_0 ? -128.0f : KT == KVQ_Q5_0 ? -16.0f : -8.0f) * TWO_M24 * qs;
             kofs[b] = floatx4{o, o, o, o};
-            if constexpr (KT == KVQ_Q4_0) {
+            if constexpr (K5) {
+                // fifth-bit slots 2k, 2k+1: elements 4j+k and 16+4j+k, times 2^-k
+                const u32x4 w = __builtin_bit_cast(u32x4, qb[b]);
+                const half2 s1 = {(_Float16)1.0f, (_Float16)1.0f}, s2 = {(_Float16)0.5f, (_Float16)0.5f};
+                const half2 s4 = {(_Float16)0.25f, (_Float16)0.25f}, s8 = {(_Float16)0.125f, (_Float16)0.125f};
+                qb5[K5 ? b : 0] = pack4(h2_bits(bits_h2(__builtin_amdgcn_perm(w.z, w.x, 0x05040100u)) * s1),
+                                        h2_bits(bits_h2(__builtin_amdgcn_perm(w.z, w.x, 0x07060302u)) * s2),
+                                        h2_bits(bits_h2(__builtin_amdgcn_perm(w.w, w.y, 0x05040100u)) * s4),
+                                        h2_bits(bits_h2(__builtin_amdgcn_perm(w.w, w.y, 0x07060302u)) * s8));
+            }
+            if constexpr (KT == KVQ_Q4_0 || KT == KVQ_Q5_0) {
                 // slots: elements 4j, 4j+2, 4j+1, 4j+3, then the high
                 // nibbles' 16+4j, ... scaled by 1/16
                 const u32x4 w = __builtin_bit_cast(u32x4, qb[b]);

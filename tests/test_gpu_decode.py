@@ -64,11 +64,12 @@ def test_decode_scale_sign(kt, vt, scale):
                scale=scale)
 
 
-@pytest.mark.parametrize("kt,vt", [("q8_0", "q4_0"), ("q4_0", "q4_0"), ("q4_0", "q8_0"), ("q8_0", "q8_0")])
+@pytest.mark.parametrize("kt,vt", [("q8_0", "q4_0"), ("q4_0", "q4_0"), ("q4_0", "q8_0"), ("q8_0", "q8_0"), ("q5_0", "q5_0"), ("q5_0", "q4_0")])
 def test_decode_query_dynamic_range(kt, vt):
-    """q8_0 and q4_0 keys enter the score product as binary16 subnormals with
-    the codes' offset removed through the block sum of the query, and the
-    high nibbles' query channels are divided by 16.  Queries whose channel
+    """q8_0, q4_0 and q5_0 keys enter the score product as binary16
+    subnormals with the codes' offset removed through the block sum of the
+    query, the high nibbles' query channels are divided by 16, and q5_0's
+    fifth bits meet query channels scaled by 2^-k.  Queries whose channel
     magnitudes spread log-uniformly over 2^-24 .. 2^2 (many of them binary16
     subnormals, or subnormal once divided by 16), with a head of zeros, one
     of all-tiny and one of one-signed values (a block sum as large as it

@@ -22,8 +22,9 @@
 //       block's K scale multiplies the MFMA result per token;
 //   O^T[chan][head] += V^T[chan][token] . P'[token][head]  -- one MFMA per 16
 //       channels and 32 tokens; P' = binary16(p) * V scale of (token, block).
-// q8_0 and q4_0 codes enter both products as binary16 subnormals (a mask or
-// byte permute of the stored bits, no per-element arithmetic); their offset
+// q8_0 and q4_0 codes (both products) and q5_0 keys enter as binary16
+// subnormals (a mask or byte permute of the stored bits, no per-element
+// arithmetic; q5_0's fifth bits through a second score MFMA); their offset
 // comes off per block, through the score MFMA's accumulator input for keys
 // and one more MFMA against a constant operand for values.
 // The score layout of the first product is exactly the operand layout of the

@@ -99,7 +99,7 @@ __global__ __launch_bounds__((64 * Layout<KT, VT, D>::PW)) __attribute__((amdgpu
     constexpr bool KQ = KT != KVQ_F16, VQ = VT != KVQ_F16;
     // raised issue priority from the dequantization through the scores (see
     // the score phase)
-    constexpr bool PRIO_DQ = (KT == KVQ_Q8_0 || KT == KVQ_Q5_0) && VQ;
+    constexpr bool PRIO_DQ = KQ || VQ;
 
     // Dequantized operands of the current tile, built once per workgroup:
     // K hi and lo per (tile u of the step, score tile T, block b), V (times
@@ -376,10 +376,10 @@ __global__ __launch_bounds__((64 * Layout<KT, VT, D>::PW)) __attribute__((amdgpu
         // MFMAs the other wave's softmax fills the vector slots between them.
         // The priority change is a scheduling boundary, so where the next
         // tile's dequantization is interleaved with the score MFMAs, the
-        // raised span starts before that dequantization (body below), and
-        // only for 8- and 5-bit keys with quantized values (1-3% faster); for
-        // the other pairs it measured no faster, or slower (f16/q4_0 +3%,
-        // K4V4 +1%)
+        // raised span starts before that dequantization (body below): for
+        // every pair that dequantizes a half (with two-tile steps, K4V4 and
+        // q4_0/q5_0 4-6% faster, quantized keys with binary16 values 5-7%,
+        // binary16 keys 0-3%)
         constexpr bool PRIO_QK = !KQ && !VQ;
         if (PRIO_QK)
             __builtin_amdgcn_s_setprio(1);

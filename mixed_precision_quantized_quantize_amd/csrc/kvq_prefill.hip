@@ -469,8 +469,11 @@ __global__ __launch_bounds__((64 * Layout<KT, VT, D>::PW)) __attribute__((amdgpu
             }
         }
 
-        // ---- O^T += V^T . P
-        __builtin_amdgcn_s_setprio(1);
+        // ---- O^T += V^T . P (at priority 2 above the score phase where two
+        // workgroups share a CU: their waves are not in lockstep, and this
+        // orders the three phases -- head_dim 64 with binary16 values,
+        // f16/f16 10% faster; with one workgroup per CU it made no difference)
+        __builtin_amdgcn_s_setprio(Layout<KT, VT, D>::LDS_KB < 160 ? 2 : 1);
 #pragma unroll
         for (int u = 0; u < SUB; u++)
 #pragma unroll

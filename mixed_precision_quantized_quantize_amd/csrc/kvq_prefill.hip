@@ -110,9 +110,15 @@ __global__ __launch_bounds__((64 * Layout<KT, VT, D>::PW)) __attribute__((amdgpu
     constexpr int DQ_BYTES = DQ_V + NVSET * 1024;
     // tile t's in dq0 (t even) or dq1 (t odd): two arrays, so that the
     // compiler sees that building one tile's operands does not touch the
-    // other's, and may interleave the two
-    __shared__ __attribute__((aligned(16))) uint8_t dq0[DQ_BYTES > 0 ? DQ_BYTES : 16];
-    __shared__ __attribute__((aligned(16))) uint8_t dq1[DQ_BYTES > 0 ? DQ_BYTES : 16];
+    // other's, and may interleave the two.  The compiler lays the kernel's
+    // LDS arrays out by decreasing alignment, then decreasing size; the
+    // larger alignment puts the operand arrays below the raw steps whatever
+    // their sizes, so that more of the operand reads (every wave, every
+    // tile) sit within the 64 KiB a DS instruction's offset field reaches
+    // from the lane's base address and need no address instruction of their
+    // own.
+    __shared__ __attribute__((aligned(DQ_BYTES > 0 ? 32 : 16))) uint8_t dq0[DQ_BYTES > 0 ? DQ_BYTES : 16];
+    __shared__ __attribute__((aligned(DQ_BYTES > 0 ? 32 : 16))) uint8_t dq1[DQ_BYTES > 0 ? DQ_BYTES : 16];
     // raw steps (SUB tiles each, tile u at u * g::BYTES): step t in
     // lds[t % NRAW].  While t is computed, t+1 is being dequantized and the
     // copies of the later steps are in flight: t+2 with three buffers, t+2

@@ -74,7 +74,7 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-prefill", action="store_true", help="skip the prefill measurement")
     p.add_argument("--no-configs", action="store_true", help="headline workload (and prefill) only")
-    p.add_argument("--no-pairs", action="store_true", help="skip the one-layer sweep over all 20 type pairs")
+    p.add_argument("--no-pairs", action="store_true", help="skip the one-layer sweeps (decode and prefill) over all 20 type pairs")
     p.add_argument("--no-stream-ceiling", action="store_true", help="skip the streaming-read ceiling measurement")
     p.add_argument("--cpu-seconds", type=float, default=10.0, help="oracle time budget of the headline workload")
     p.add_argument("--cpu-seconds-other", type=float, default=3.0, help="oracle time budget of each other workload")
@@ -686,6 +686,18 @@ def prefill_measure(dev, calls=5, cpu=False, pair=None):
     return res
 
 
+def prefill_pairs(dev):
+    """The causal prefill of `prefill_measure` (one layer, 4 x 512 queries at
+    the end of 131072 positions) for every K/V type pair, one after another
+    on fresh caches: ms per call and TFLOP/s of the same algorithmic flop."""
+    rows = []
+    for kt, vt in PAIRS_ALL:
+        r = prefill_measure(dev, pair=(kt, vt))
+        rows.append({"k_type": kt, "v_type": vt, "ms_per_call": r["ms_per_call"],
+                     "TFLOP_per_s": r["roofline"]["achieved"], "frac": r["roofline"]["frac"]})
+    return rows
+
+
 def prefill_head_dims(dev, calls=3, rounds=5):
     """The causal prefill at the other head dims: head_dim 64 (32 query / 4 kv
     heads) and 256 (16 / 8), 4 sequences, the last 512-query chunk of 32768
@@ -953,6 +965,8 @@ def main():
         result["configs"] = other_configs(dev, args)
     if not args.no_pairs and args.only is None:
         result["pairs"] = pairs_sweep(dev)
+        if result["prefill"] is not None:
+            result["prefill"]["pairs"] = prefill_pairs(dev)
     print(json.dumps(result), flush=True)
 
 

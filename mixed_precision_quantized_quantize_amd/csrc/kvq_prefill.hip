@@ -131,6 +131,12 @@ __global__ __launch_bounds__((64 * Layout<KT, VT, D>::PW)) __attribute__((amdgpu
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    // Binary16 keys at head_dim 128: only the first half of the waves raises
+    // its issue priority in the phases below, so the two waves that share a
+    // SIMD (w and w + 4) do not move through their matrix and vector phases
+    // in step (1.5-2.7% faster for these five pairs; with quantized keys,
+    // whose dequantization already spreads the phases, it was slower).
+    const bool prio_w = !(KT == KVQ_F16 && D == 128) || wave < PW / 2;
     const int n = lane & 15, j = lane >> 4;
 
     // Workgroups of one (sequence, kv head) are kept on one XCD (dispatch is
@@ -388,7 +394,7 @@ __global__ __launch_bounds__((64 * Layout<KT, VT, D>::PW)) __attribute__((amdgpu
         // binary16 keys 0-3%)
         constexpr bool PRIO_QK = !KQ && !VQ;
         if (PRIO_QK)
-            __builtin_amdgcn_s_setprio(1);
+            if (prio_w) __builtin_amdgcn_s_setprio(1);
         floatx4 sacc[RB][2 * SUB];  // score tile 2u + T
 #pragma unroll
         for (int rb = 0; rb < RB; rb++)
@@ -421,7 +427,7 @@ __global__ __launch_bounds__((64 * Layout<KT, VT, D>::PW)) __attribute__((amdgpu
                 }
 
         if (PRIO_QK || PRIO_DQ)
-            __builtin_amdgcn_s_setprio(0);
+            if (prio_w) __builtin_amdgcn_s_setprio(0);
         // ---- online softmax per row block; score x = 8u + r of a lane is key
         // tb + 32u + 8j + r
         constexpr int NS = 8 * SUB;
@@ -479,7 +485,7 @@ __global__ __launch_bounds__((64 * Layout<KT, VT, D>::PW)) __attribute__((amdgpu
         // workgroups share a CU: their waves are not in lockstep, and this
         // orders the three phases -- head_dim 64 with binary16 values,
         // f16/f16 10% faster; with one workgroup per CU it made no difference)
-        __builtin_amdgcn_s_setprio(Layout<KT, VT, D>::LDS_KB < 160 ? 2 : 1);
+        if (prio_w) __builtin_amdgcn_s_setprio(Layout<KT, VT, D>::LDS_KB < 160 ? 2 : 1);
 #pragma unroll
         for (int u = 0; u < SUB; u++)
 #pragma unroll
@@ -514,7 +520,7 @@ __global__ __launch_bounds__((64 * Layout<KT, VT, D>::PW)) __attribute__((amdgpu
 #pragma unroll
             for (int u = 0; u < SUB; u++)
                 lacc[rb] = mfma(ones, pb[rb][u], lacc[rb]);
-        __builtin_amdgcn_s_setprio(0);
+        if (prio_w) __builtin_amdgcn_s_setprio(0);
     };
 
     // ---- the step loop: one barrier per step.  At the barrier of step t,
@@ -561,7 +567,7 @@ __global__ __launch_bounds__((64 * Layout<KT, VT, D>::PW)) __attribute__((amdgpu
             issue_step(t + 2);
         }
         if (PRIO_DQ)
-            __builtin_amdgcn_s_setprio(1);  // through this dequantization and tile t's scores
+            if (prio_w) __builtin_amdgcn_s_setprio(1);  // through this dequantization and tile t's scores
         if (KQ || VQ)
             dequant(std::integral_constant<bool, LAST2>(), t + 1, dqw);
         compute(diag_c, t, dqr);

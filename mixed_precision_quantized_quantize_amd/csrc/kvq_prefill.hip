@@ -131,12 +131,14 @@ __global__ __launch_bounds__((64 * Layout<KT, VT, D>::PW)) __attribute__((amdgpu
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    // Binary16 keys at head_dim 128: only the first half of the waves raises
-    // its issue priority in the phases below, so the two waves that share a
-    // SIMD (w and w + 4) do not move through their matrix and vector phases
-    // in step (1.5-2.7% faster for these five pairs; with quantized keys,
-    // whose dequantization already spreads the phases, it was slower).
-    const bool prio_w = !(KT == KVQ_F16 && D == 128) || wave < PW / 2;
+    // Binary16 keys in the eight-wave layouts (head_dim 128; head_dim 64 with
+    // quantized values): only the first half of the waves raises its issue
+    // priority in the phases below, so the two waves that share a SIMD (w and
+    // w + 4) do not move through their matrix and vector phases in step
+    // (1.5-2.7% faster for those pairs at head_dim 128, 3-4% at 64; with
+    // quantized keys, whose dequantization already spreads the phases, it was
+    // slower).
+    const bool prio_w = !(KT == KVQ_F16 && (D == 128 || Layout<KT, VT, D>::W8_64)) || wave < PW / 2;
     const int n = lane & 15, j = lane >> 4;
 
     // Workgroups of one (sequence, kv head) are kept on one XCD (dispatch is
